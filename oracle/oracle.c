@@ -1,0 +1,314 @@
+/*
+ * oracle.c - TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU statement of what the ternary bit-plane GEMV
+ * computes. Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library. The GPU library shares no code, header, table or helper
+ * with it, and this file includes nothing from the GPU library.
+ *
+ * Sources (cited by page title and section):
+ *   [TP] "Tritium: One Weight Format for Ternary Inference on Commodity CPUs and
+ *        Multiplier-Free Hardware" - sections "Background / The model", "The .trit v1
+ *        layout" (Equations 2-3 in the introduction), "Invariants", "On popcount",
+ *        "The hardware core", "Verification".
+ *   [TF] "The .trit format, version 1" - section 1 "Why bit planes", 2.3 "Ternary
+ *        payload", 2.4 "Dense payload", 3 "A complete file", 4 "Validation".
+ *
+ * Readings where the pages leave a step open (each is also listed in the design notes):
+ *   - Activation dequantisation: an int8 code q stands for x_scale * q (absmax), and the
+ *     weight for w_scale * trit ([TF] 2.3). The fp32 output multiplies the exact integer
+ *     sum by each scale in turn, ((float)acc * x_scale) * w_scale, the order [TP]
+ *     "Why exactness, concretely" says the reference uses. A float64 value of the same
+ *     product is returned beside it.
+ *   - When several beats break an invariant, the first in row-major order is reported,
+ *     at its lowest offending bit; within one beat P1 is checked before P2.
+ *   - The dense head is y = W x over bfloat16 inputs; the oracle accumulates in float64
+ *     and also returns sum |w * x| for the tolerance.
+ *
+ * Parity pins live in the test suite (worked example bytes of [TF] section 3, brute force
+ * against a dense integer product, closed-form invariants, the -128 extremes case).
+ */
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum {
+    OR_OK = 0,
+    OR_E_INVAL = 1, /* bad argument or a weight value outside {-1, 0, +1} */
+    OR_E_SIZE = 2,  /* byte length does not match rows * beats_per_row * 16 */
+    OR_E_P1 = 3,    /* pos & neg != 0 in some beat */
+    OR_E_P2 = 4,    /* a padding bit is set in some row's last beat */
+    OR_E_RANGE = 5  /* an accumulator left the int32 range (cannot happen for valid input) */
+};
+
+typedef struct {
+    int32_t code;
+    int64_t row, beat, col;
+} or_err;
+
+static int set_err(or_err *e, int code, int64_t row, int64_t beat, int64_t col) {
+    if (e) {
+        e->code = code;
+        e->row = row;
+        e->beat = beat;
+        e->col = col;
+    }
+    return code;
+}
+
+/* [TF] 2.3: beats_per_row = ceil(cols / 64). */
+int64_t oracle_beats_per_row(int64_t cols) { return (cols + 63) / 64; }
+
+/* [TF] 2.3: byte_len = rows * beats_per_row * 16. */
+int64_t oracle_byte_len(int64_t rows, int64_t cols) { return rows * oracle_beats_per_row(cols) * 16; }
+
+/* [TF] 2.3 / [TP] "Invariants" (P2): the valid-column mask of a row's last beat, built in 64 bits. */
+uint64_t oracle_tail_mask(int64_t cols) {
+    int64_t r = cols % 64;
+    if (r == 0) return UINT64_MAX;
+    return (UINT64_C(1) << r) - UINT64_C(1);
+}
+
+/* All integers are little-endian ([TF] section 2): assemble byte by byte, host order independent. */
+static uint64_t load_le64(const uint8_t *p) {
+    uint64_t v = 0;
+    for (int j = 0; j < 8; ++j) v |= (uint64_t)p[j] << (8 * j);
+    return v;
+}
+
+static void store_le64(uint8_t *p, uint64_t v) {
+    for (int j = 0; j < 8; ++j) p[j] = (uint8_t)(v >> (8 * j));
+}
+
+static int lowest_bit(uint64_t v) {
+    int k = 0;
+    while (!((v >> k) & 1)) ++k;
+    return k;
+}
+
+/*
+ * [TF] 2.3 "Ternary payload": beat b of row r is 16 bytes at (r * bpr + b) * 16;
+ * bytes 0..8 hold pos (bit k set => W[r][64b + k] = +1), bytes 8..16 hold neg
+ * (bit k set => W[r][64b + k] = -1). Neither bit => 0. Bits past cols stay clear.
+ */
+int oracle_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, int64_t len, or_err *e) {
+    if (rows < 0 || cols < 0) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    int64_t bpr = oracle_beats_per_row(cols);
+    if (len != rows * bpr * 16) return set_err(e, OR_E_SIZE, -1, -1, -1);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < bpr; ++b) {
+            uint64_t pos = 0, neg = 0;
+            for (int k = 0; k < 64; ++k) {
+                int64_t c = 64 * b + k;
+                if (c >= cols) break;
+                int8_t v = w[r * cols + c];
+                if (v == 1)
+                    pos |= UINT64_C(1) << k;
+                else if (v == -1)
+                    neg |= UINT64_C(1) << k;
+                else if (v != 0)
+                    return set_err(e, OR_E_INVAL, r, b, c);
+            }
+            uint8_t *beat = planes + (r * bpr + b) * 16;
+            store_le64(beat, pos);
+            store_le64(beat + 8, neg);
+        }
+    }
+    return set_err(e, OR_OK, -1, -1, -1);
+}
+
+/*
+ * [TF] section 4, checks 15, 17 and 18; [TP] "Invariants":
+ *   length: len == rows * bpr * 16;
+ *   P1: pos & neg == 0 in every beat (reported with row, beat and column);
+ *   P2: (pos | neg) & ~tail == 0 in every row's last beat (reported with the row).
+ */
+int oracle_validate(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, or_err *e) {
+    if (rows < 0 || cols < 0) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    int64_t bpr = oracle_beats_per_row(cols);
+    if (len != rows * bpr * 16) return set_err(e, OR_E_SIZE, -1, -1, -1);
+    uint64_t tail = oracle_tail_mask(cols);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < bpr; ++b) {
+            const uint8_t *beat = planes + (r * bpr + b) * 16;
+            uint64_t pos = load_le64(beat), neg = load_le64(beat + 8);
+            if (pos & neg) return set_err(e, OR_E_P1, r, b, 64 * b + lowest_bit(pos & neg));
+            if (b == bpr - 1 && ((pos | neg) & ~tail))
+                return set_err(e, OR_E_P2, r, b, 64 * b + lowest_bit((pos | neg) & ~tail));
+        }
+    }
+    return set_err(e, OR_OK, -1, -1, -1);
+}
+
+/* The trit of one weight, read from its beat's two planes ([TF] 2.3). */
+static int oracle_trit(const uint8_t *planes, int64_t bpr, int64_t r, int64_t c) {
+    const uint8_t *beat = planes + (r * bpr + c / 64) * 16;
+    int k = (int)(c % 64);
+    int p = (int)((load_le64(beat) >> k) & 1);
+    int n = (int)((load_le64(beat + 8) >> k) & 1);
+    return p - n;
+}
+
+/* Expand validated planes to one int8 per weight (the inverse of oracle_pack). */
+int oracle_unpack(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, int8_t *w, or_err *e) {
+    int rc = oracle_validate(planes, len, rows, cols, e);
+    if (rc) return rc;
+    int64_t bpr = oracle_beats_per_row(cols);
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) w[r * cols + c] = (int8_t)oracle_trit(planes, bpr, r, c);
+    return OR_OK;
+}
+
+/*
+ * The exact sum of one row: acc = sum_c W[r][c] * x[c] with W decoded one weight at a
+ * time and x sign-extended before it takes part ([TP] introduction, Equations 2-3;
+ * "The hardware core": -128 is widened, never negated in eight bits).
+ * Returns 0 and stores acc, or OR_E_RANGE if the sum leaves int32 (impossible:
+ * |acc| <= 128 * cols).
+ */
+static int oracle_row_sum(const uint8_t *planes, int64_t bpr, int64_t r, int64_t cols, const int8_t *x,
+                          int32_t *acc_out) {
+    int64_t acc = 0;
+    for (int64_t c = 0; c < cols; ++c) {
+        int64_t w = oracle_trit(planes, bpr, r, c);
+        int64_t xv = (int64_t)x[c];
+        acc += w * xv;
+    }
+    if (acc < INT32_MIN || acc > INT32_MAX) return OR_E_RANGE;
+    *acc_out = (int32_t)acc;
+    return OR_OK;
+}
+
+/* Dequantised output of one row: each scale applied in turn in fp32, plus the float64 product. */
+static void oracle_dequant(int32_t acc, float x_scale, float w_scale, float *y32, double *y64) {
+    float a = (float)acc; /* exact: |acc| < 2^24 */
+    float t = a * x_scale;
+    *y32 = t * w_scale;
+    *y64 = (double)acc * (double)x_scale * (double)w_scale;
+}
+
+/*
+ * Batch-1 ternary GEMV: out_i32[r] = sum_c W[r][c] x[c]; out_f32 / out_f64 the dequantised
+ * values (either may be NULL). The planes are validated first; invalid planes are refused.
+ * x must hold at least cols codes; only the first cols are read.
+ */
+int oracle_gemv(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, const int8_t *x, int64_t x_len,
+                float x_scale, float w_scale, int32_t *out_i32, float *out_f32, double *out_f64, int nthreads,
+                or_err *e) {
+    int rc = oracle_validate(planes, len, rows, cols, e);
+    if (rc) return rc;
+    if (x_len < cols) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    int64_t bpr = oracle_beats_per_row(cols);
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        int32_t acc = 0;
+        if (oracle_row_sum(planes, bpr, r, cols, x, &acc)) {
+            bad |= 1;
+            continue;
+        }
+        out_i32[r] = acc;
+        float y32;
+        double y64;
+        oracle_dequant(acc, x_scale, w_scale, &y32, &y64);
+        if (out_f32) out_f32[r] = y32;
+        if (out_f64) out_f64[r] = y64;
+    }
+    if (bad) return set_err(e, OR_E_RANGE, -1, -1, -1);
+    return set_err(e, OR_OK, -1, -1, -1);
+}
+
+/*
+ * The second, independent formulation ([TP] "On popcount", "Verification"): split x into
+ * its eight two's-complement bit planes X_j (bit k of X_j = bit j of x[64b + k]); then
+ *   acc = sum_b sum_j c_j * (popcount(pos & X_j) - popcount(neg & X_j)),
+ * c_j = 2^j for j < 7 and c_7 = -128. It never forms a per-weight trit.
+ */
+static int popcount64(uint64_t v) {
+    int n = 0;
+    while (v) {
+        n += (int)(v & 1);
+        v >>= 1;
+    }
+    return n;
+}
+
+int oracle_gemv_bitserial(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, const int8_t *x,
+                          int64_t x_len, int32_t *out_i32, int nthreads, or_err *e) {
+    int rc = oracle_validate(planes, len, rows, cols, e);
+    if (rc) return rc;
+    if (x_len < cols) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    int64_t bpr = oracle_beats_per_row(cols);
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t acc = 0;
+        for (int64_t b = 0; b < bpr; ++b) {
+            const uint8_t *beat = planes + (r * bpr + b) * 16;
+            uint64_t pos = load_le64(beat), neg = load_le64(beat + 8);
+            for (int j = 0; j < 8; ++j) {
+                uint64_t xj = 0;
+                for (int k = 0; k < 64; ++k) {
+                    int64_t c = 64 * b + k;
+                    if (c < cols && ((((uint8_t)x[c]) >> j) & 1)) xj |= UINT64_C(1) << k;
+                }
+                int64_t cj = (j == 7) ? -128 : ((int64_t)1 << j);
+                acc += cj * (int64_t)(popcount64(pos & xj) - popcount64(neg & xj));
+            }
+        }
+        if (acc < INT32_MIN || acc > INT32_MAX)
+            bad |= 1;
+        else
+            out_i32[r] = (int32_t)acc;
+    }
+    if (bad) return set_err(e, OR_E_RANGE, -1, -1, -1);
+    return set_err(e, OR_OK, -1, -1, -1);
+}
+
+/*
+ * Small batch: the batch-1 GEMV applied to each of `batch` activations. X is token-major,
+ * row t at X + t * ldx (ldx >= cols); out_*[t * rows + r]; x_scales[t] per token, one
+ * w_scale for the matrix.
+ */
+int oracle_gemm_small_batch(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, const int8_t *X,
+                            int64_t batch, int64_t ldx, const float *x_scales, float w_scale, int32_t *out_i32,
+                            float *out_f32, double *out_f64, int nthreads, or_err *e) {
+    if (batch < 0 || ldx < cols) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    for (int64_t t = 0; t < batch; ++t) {
+        int rc = oracle_gemv(planes, len, rows, cols, X + t * ldx, ldx, x_scales[t], w_scale, out_i32 + t * rows,
+                             out_f32 ? out_f32 + t * rows : NULL, out_f64 ? out_f64 + t * rows : NULL, nthreads, e);
+        if (rc) return rc;
+    }
+    return set_err(e, OR_OK, -1, -1, -1);
+}
+
+/* bfloat16 is the upper half of an IEEE binary32 ([TF] 2.4 stores BF16 little-endian); widening is exact. */
+static double bf16_to_double(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return (double)f;
+}
+
+/*
+ * Dense head ([TP] "Where the bytes are", [TF] 2.4): y[v] = sum_h W[v][h] x[h] over bf16
+ * W [rows x cols] row-major and bf16 x [cols], accumulated in float64 in column order;
+ * s[v] = sum_h |W[v][h] x[h]| (the scale of the admissible rounding error).
+ */
+int oracle_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, double *y, double *s,
+                      int nthreads) {
+    if (rows < 0 || cols < 0) return OR_E_INVAL;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1)
+    for (int64_t v = 0; v < rows; ++v) {
+        double acc = 0.0, mag = 0.0;
+        for (int64_t h = 0; h < cols; ++h) {
+            double p = bf16_to_double(w[v * cols + h]) * bf16_to_double(x[h]);
+            acc += p;
+            mag += p < 0 ? -p : p;
+        }
+        y[v] = acc;
+        if (s) s[v] = mag;
+    }
+    return OR_OK;
+}

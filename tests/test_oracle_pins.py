@@ -1,0 +1,337 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test fixes the oracle against something the pages or plain mathematics decide:
+the worked-example bytes of "The .trit format, version 1" (section 3), numpy's own bit
+packing and integer matrix product (library routines), exhaustive brute force on tiny
+shapes, closed-form invariants of Equations 2-3 of the Tritium paper's introduction,
+the -128 extremes case of its "The hardware core" section, exact rational arithmetic
+for the dequantisation, and the byte counts both pages print for BitNet b1.58 2B4T.
+"""
+import itertools
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from conftest import read_worked_example
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def np_pack(w: np.ndarray) -> np.ndarray:
+    """Independent packer built on numpy.packbits(bitorder='little'): bit k of byte i is element 8i+k."""
+    rows, cols = w.shape
+    bpr = (cols + 63) // 64
+    pad = np.zeros((rows, bpr * 64), dtype=np.int8)
+    pad[:, :cols] = w
+    pos = np.packbits(pad == 1, axis=1, bitorder="little").reshape(rows, bpr, 8)
+    neg = np.packbits(pad == -1, axis=1, bitorder="little").reshape(rows, bpr, 8)
+    return np.concatenate([pos, neg], axis=2).reshape(-1)
+
+
+def dense_acc(w: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """The plain definition through numpy's integer matrix product (int64)."""
+    return w.astype(np.int64) @ x[: w.shape[1]].astype(np.int64)
+
+
+def swap_planes(planes: np.ndarray) -> np.ndarray:
+    b = planes.reshape(-1, 2, 8)
+    return b[:, ::-1, :].reshape(-1).copy()
+
+
+def all_rows(cols: int) -> np.ndarray:
+    return np.array(list(itertools.product((-1, 0, 1), repeat=cols)), dtype=np.int8).reshape(-1, cols)
+
+
+# ----------------------------------------------------------------------------- worked example
+
+def test_worked_example_payload_bytes():
+    rows, cols, scale, w, payload = read_worked_example()
+    w = np.array(w, dtype=np.int8)
+    planes = oracle.pack(w)
+    assert planes.tobytes() == payload
+    assert oracle.byte_len(rows, cols) == len(payload) == 32
+    oracle.validate(np.frombuffer(payload, np.uint8), rows, cols)
+    assert np.array_equal(oracle.unpack(np.frombuffer(payload, np.uint8), rows, cols), w)
+
+
+def test_worked_example_products():
+    rows, cols, scale, w, payload = read_worked_example()
+    planes = np.frombuffer(payload, np.uint8)
+    for x in ([5, 7, 11], [-128, 127, -1], [0, 0, 0], [1, 1, 1]):
+        acc, y32, y64 = oracle.gemv(planes, rows, cols, np.array(x, np.int8), 1.0, scale)
+        # W = [[+1, -1, 0], [0, +1, +1]]: row 0 = x0 - x1, row 1 = x1 + x2.
+        assert acc.tolist() == [x[0] - x[1], x[1] + x[2]]
+        assert y64.tolist() == [0.5 * (x[0] - x[1]), 0.5 * (x[1] + x[2])]
+
+
+# ----------------------------------------------------------------------------- packing
+
+SHAPES_R = (1, 2, 3, 16, 17)
+SHAPES_C = (1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 2560, 6912)
+
+
+@pytest.mark.parametrize("cols", SHAPES_C)
+@pytest.mark.parametrize("rows", SHAPES_R)
+def test_pack_roundtrip_and_layout(rows, cols):
+    for kind in ("zero", "random"):
+        w = np.zeros((rows, cols), np.int8) if kind == "zero" else synth.trits(7 + rows * 100000 + cols, rows, cols)
+        planes = oracle.pack(w)
+        assert planes.size == rows * ((cols + 63) // 64) * 16
+        assert np.array_equal(planes, np_pack(w)), "bit/plane/row order differs from numpy.packbits"
+        oracle.validate(planes, rows, cols)
+        assert np.array_equal(oracle.unpack(planes, rows, cols), w), "round trip lost or moved a value"
+        # no column dropped at a ragged tail: every nonzero is present in the planes
+        pl = planes.reshape(rows, -1, 2, 8)
+        assert int(np.unpackbits(pl).sum()) == int(np.count_nonzero(w))
+
+
+def test_tail_mask_widths():
+    for c in range(0, 200):
+        t = oracle.tail_mask(c)
+        r = c % 64
+        assert t == ((1 << 64) - 1 if r == 0 else (1 << r) - 1)
+        assert bin(t).count("1") == (64 if r == 0 else r)
+    for r in (1, 31, 32, 33, 63):  # the remainders a 32-bit shift gets wrong
+        assert oracle.tail_mask(64 + r) == (1 << r) - 1
+
+
+@pytest.mark.parametrize("cols", (1, 31, 32, 33, 63, 64, 65, 100, 127, 128))
+def test_padding_bit_rejected_exactly_past_cols(cols):
+    rows = 3
+    w = synth.trits(99 + cols, rows, cols)
+    base = oracle.pack(w)
+    bpr = (cols + 63) // 64
+    r_valid = cols % 64 or 64
+    for plane in (0, 1):
+        for k in range(64):
+            p = base.copy().reshape(rows, bpr, 2, 8)
+            # set bit k of one plane in row 1's last beat and clear it in the other plane,
+            # so the only possible violation is a padding bit
+            word = int.from_bytes(p[1, bpr - 1, plane].tobytes(), "little")
+            other = int.from_bytes(p[1, bpr - 1, 1 - plane].tobytes(), "little")
+            word |= 1 << k
+            other &= ~(1 << k)
+            p[1, bpr - 1, plane] = np.frombuffer(word.to_bytes(8, "little"), np.uint8)
+            p[1, bpr - 1, 1 - plane] = np.frombuffer(other.to_bytes(8, "little"), np.uint8)
+            flat = p.reshape(-1)
+            if k < r_valid:
+                oracle.validate(flat, rows, cols)
+            else:
+                with pytest.raises(oracle.OracleError) as ei:
+                    oracle.validate(flat, rows, cols)
+                assert ei.value.code == oracle.E_P2
+                assert ei.value.row == 1 and ei.value.beat == bpr - 1
+                assert ei.value.col == 64 * (bpr - 1) + k
+
+
+def test_both_bits_rejected_with_position():
+    rows, cols = 5, 200
+    w = synth.trits(3, rows, cols)
+    planes = oracle.pack(w).reshape(rows, 4, 2, 8)
+    # set bit 37 of beat 2 of row 3 in both planes, and a later violation in row 4
+    for r, b, k in ((4, 0, 1), (3, 2, 37)):
+        for plane in (0, 1):
+            word = int.from_bytes(planes[r, b, plane].tobytes(), "little") | (1 << k)
+            planes[r, b, plane] = np.frombuffer(word.to_bytes(8, "little"), np.uint8)
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.validate(planes.reshape(-1), rows, cols)
+    assert (ei.value.code, ei.value.row, ei.value.beat, ei.value.col) == (oracle.E_P1, 3, 2, 2 * 64 + 37)
+    with pytest.raises(oracle.OracleError):
+        oracle.gemv(planes.reshape(-1), rows, cols, np.zeros(cols, np.int8))
+
+
+def test_p1_reported_before_p2_in_same_beat():
+    rows, cols = 1, 10
+    planes = np.zeros(16, np.uint8)
+    planes[0] = 0b1  # pos bit 0
+    planes[8] = 0b1  # neg bit 0 -> P1
+    planes[1] = 0b100  # pos bit 10 -> padding (P2)
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.validate(planes, rows, cols)
+    assert ei.value.code == oracle.E_P1 and ei.value.col == 0
+
+
+def test_length_and_value_errors():
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.validate(np.zeros(31, np.uint8), 2, 3)
+    assert ei.value.code == oracle.E_SIZE
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.validate(np.zeros(48, np.uint8), 2, 3)
+    assert ei.value.code == oracle.E_SIZE
+    w = np.zeros((3, 70), np.int8)
+    w[2, 66] = 2
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.pack(w)
+    assert (ei.value.code, ei.value.row, ei.value.beat, ei.value.col) == (oracle.E_INVAL, 2, 1, 66)
+
+
+# ----------------------------------------------------------------------------- brute force
+
+EXTREME_X = (-128, -1, 0, 1, 127)
+
+
+@pytest.mark.parametrize("cols", range(1, 9))
+def test_exhaustive_rows_against_dense_product(cols):
+    """Every ternary row of length cols (3^cols of them, rows are independent) against x vectors."""
+    w = all_rows(cols)
+    planes = oracle.pack(w)
+    if cols <= 4:
+        xs = list(itertools.product(EXTREME_X, repeat=cols))
+    else:
+        rng = np.random.default_rng(cols)
+        xs = [tuple(v) for v in rng.integers(-128, 128, size=(60, cols))]
+        xs += [tuple([e] * cols) for e in EXTREME_X]
+    for x in xs:
+        x = np.array(x, np.int8)
+        acc, _, _ = oracle.gemv(planes, w.shape[0], cols, x)
+        assert np.array_equal(acc, dense_acc(w, x))
+        assert np.array_equal(oracle.gemv_bitserial(planes, w.shape[0], cols, x), acc)
+
+
+def test_random_shapes_against_dense_product():
+    rng = np.random.default_rng(1234)
+    shapes = [(int(r), int(c)) for r, c in zip(rng.integers(1, 18, 40), rng.integers(1, 201, 40))]
+    shapes += [(64, 2560), (33, 6912), (7, 8193)]
+    for i, (r, c) in enumerate(shapes):
+        z = (0.0, 0.2966, 0.4219, 0.5148, 1.0)[i % 5]
+        w = synth.trits(500 + i, r, c, z)
+        x = rng.integers(-128, 128, size=c).astype(np.int8)
+        planes = oracle.pack(w)
+        acc, _, _ = oracle.gemv(planes, r, c, x)
+        assert np.array_equal(acc, dense_acc(w, x))
+        assert np.array_equal(oracle.gemv_bitserial(planes, r, c, x), acc)
+
+
+# ----------------------------------------------------------------------------- invariants
+
+def test_invariants():
+    rows, cols = 9, 777
+    x = synth.activation(42, cols)[0]
+    sx = int(x.astype(np.int64).sum())
+    zero = oracle.pack(np.zeros((rows, cols), np.int8))
+    plus = oracle.pack(np.ones((rows, cols), np.int8))
+    minus = oracle.pack(-np.ones((rows, cols), np.int8))
+    assert np.all(oracle.gemv(zero, rows, cols, x)[0] == 0)
+    assert np.all(oracle.gemv(plus, rows, cols, x)[0] == sx)
+    assert np.all(oracle.gemv(minus, rows, cols, x)[0] == -sx)
+
+    w = synth.trits(43, rows, cols)
+    planes = oracle.pack(w)
+    acc = oracle.gemv(planes, rows, cols, x)[0]
+    # swapping the planes negates every row
+    assert np.array_equal(oracle.gemv(swap_planes(planes), rows, cols, x)[0], -acc)
+    # additivity over disjoint supports
+    mask = synth.uniform(44, rows * cols).reshape(rows, cols) < 0.5
+    w1 = np.where(mask, w, 0).astype(np.int8)
+    w2 = np.where(mask, 0, w).astype(np.int8)
+    a1 = oracle.gemv(oracle.pack(w1), rows, cols, x)[0].astype(np.int64)
+    a2 = oracle.gemv(oracle.pack(w2), rows, cols, x)[0].astype(np.int64)
+    assert np.array_equal(a1 + a2, acc)
+    # a joint permutation of columns leaves every row unchanged
+    perm = np.argsort(synth.uniform(45, cols))
+    assert np.array_equal(oracle.gemv(oracle.pack(w[:, perm].copy()), rows, cols, x[perm].copy())[0], acc)
+    # x entries past cols are never read
+    xl = np.concatenate([x, np.full(100, 127, np.int8)])
+    assert np.array_equal(oracle.gemv(planes, rows, cols, xl)[0], acc)
+
+
+def test_extremes_minus128():
+    """6912 weights of -1 against x = -128 (the widening case the paper's golden set keeps)."""
+    cols = 6912
+    x = np.full(cols, -128, np.int8)
+    w = np.stack([-np.ones(cols, np.int8), np.ones(cols, np.int8), np.zeros(cols, np.int8)])
+    acc = oracle.gemv(oracle.pack(w), 3, cols, x)[0]
+    assert acc.tolist() == [884736, -884736, 0]
+    assert oracle.gemv_bitserial(oracle.pack(w), 3, cols, x).tolist() == [884736, -884736, 0]
+    one = oracle.pack(np.array([[-1], [1]], np.int8))
+    assert oracle.gemv(one, 2, 1, np.array([-128], np.int8))[0].tolist() == [128, -128]
+
+
+# ----------------------------------------------------------------------------- dequantisation
+
+def test_dequant_against_exact_rationals():
+    rows, cols = 64, 2560
+    case = synth.ternary_case(5, 0, 1, rows, cols)
+    planes = oracle.pack(case.w)
+    acc, y32, y64 = oracle.gemv(planes, rows, cols, case.x, case.x_scale, case.w_scale)
+    for a, f32, f64 in zip(acc.tolist(), y32.tolist(), y64.tolist()):
+        exact = Fraction(a) * Fraction(case.x_scale) * Fraction(case.w_scale)
+        assert f64 == float(exact)  # one rounding of the exact product
+        if a == 0:
+            assert f32 == 0.0
+        else:  # two binary32 roundings: relative error below 2 * 2^-24 (+ second order)
+            assert abs(Fraction(f32) - exact) <= Fraction(1, 2 ** 23) * abs(exact) * Fraction(1001, 1000)
+    # unit scales give the integer back exactly
+    acc1, y1, _ = oracle.gemv(planes, rows, cols, case.x, 1.0, 1.0)
+    assert np.array_equal(y1, acc1.astype(np.float32))
+
+
+# ----------------------------------------------------------------------------- small batch
+
+def test_small_batch_is_per_token_gemv():
+    rows, cols = 40, 300
+    w = synth.trits(77, rows, cols)
+    planes = oracle.pack(w)
+    X, sc = synth.small_batch_x(78, 5, cols)
+    ldx = cols + 17
+    Xl = np.full((5, ldx), -7, np.int8)
+    Xl[:, :cols] = X
+    acc, y32, y64 = oracle.gemm_small_batch(planes, rows, cols, Xl, sc, 1.25)
+    for t in range(5):
+        assert np.array_equal(acc[t], dense_acc(w, X[t]))
+        a1, f1, d1 = oracle.gemv(planes, rows, cols, X[t], sc[t], 1.25)
+        assert np.array_equal(a1, acc[t]) and np.array_equal(f1, y32[t]) and np.array_equal(d1, y64[t])
+
+
+# ----------------------------------------------------------------------------- dense head
+
+def bf16_to_f64(h: np.ndarray) -> np.ndarray:
+    return (h.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_dense_head_one_hot_columns():
+    w, _ = synth.head_case(11, rows=300, cols=256)
+    for h in (0, 1, 100, 255):
+        x = np.zeros(256, np.uint16)
+        x[h] = 0x3F80  # 1.0 in bfloat16
+        y, s = oracle.dense_head(w, x)
+        assert np.array_equal(y, bf16_to_f64(w[:, h]))
+        assert np.array_equal(s, np.abs(bf16_to_f64(w[:, h])))
+
+
+def test_dense_head_against_library_product():
+    w, x = synth.head_case(12, rows=1000, cols=2560)
+    y, s = oracle.dense_head(w, x)
+    wf, xf = bf16_to_f64(w), bf16_to_f64(x)
+    ref = wf @ xf
+    assert np.all(np.abs(y - ref) <= 1e-12 * np.abs(wf * xf).sum(axis=1) + 1e-300)
+    assert np.allclose(s, np.abs(wf * xf).sum(axis=1), rtol=1e-12, atol=0)
+
+
+# ----------------------------------------------------------------------------- byte accounting
+
+def test_decode_step_byte_accounting():
+    """BitNet b1.58 2B4T: 2,084,044,800 trits in 210 tensors (format page section 5; BITCOS
+    essay, worked example) and about 521 MB of ternary planes (format page section 2.4)."""
+    shapes = synth.decode_step_shapes()
+    assert len(shapes) == 210
+    assert sum(r * c for _, _, _, r, c in shapes) == 2_084_044_800
+    planes = sum(oracle.byte_len(r, c) for _, _, _, r, c in shapes)
+    assert planes == 521_011_200 and round(planes / 1e6) == 521
+    assert synth.VOCAB * synth.HIDDEN == 328_335_360
+
+
+def test_dequant_applies_scales_in_turn():
+    """The fp32 value is the integer times x_scale, rounded, then times w_scale, rounded (the
+    paper's "Why exactness, concretely": the reference multiplies by each scale in turn).
+    Each intermediate product is exact in float64 (24-bit by 24-bit significands), so one
+    float32 rounding of it is the correctly rounded binary32 result."""
+    rows, cols = 256, 2560
+    case = synth.ternary_case(6, 0, 3, rows, cols)
+    acc, y32, _ = oracle.gemv(oracle.pack(case.w), rows, cols, case.x, case.x_scale, case.w_scale)
+    t = (acc.astype(np.float64) * np.float64(np.float32(case.x_scale))).astype(np.float32)
+    y = (t.astype(np.float64) * np.float64(np.float32(case.w_scale))).astype(np.float32)
+    assert np.array_equal(y32, y)
