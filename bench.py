@@ -1,0 +1,373 @@
+#!/usr/bin/env python3
+"""Benchmark of the batch-1 ternary bit-plane GEMV on one MI355X.
+
+One step = one decode step's ternary GEMVs: the 210 matrices of BitNet b1.58 2B4T (30 layers x
+q, k, v, o, gate, up, down), each applied to its own int8 activation, as one grouped launch
+(activation staging + the weight-streaming GEMV). Inputs are seeded synthetic data of the
+model's shapes and zero density; they are resident in HBM before timing starts. The weight set
+is held in several HBM copies used in rotation, so no step finds the previous step's weights in
+the 256 MB last-level cache: every step streams its 521,011,200 plane bytes from HBM.
+
+Prints one JSON line: weight GB/s over the timed steps (value), microseconds per step, the
+dominant kernel's roofline (HIP events around each GEMV launch), the CPU oracle's rate on the
+host cores, and the companion measurements of the same workload family: streaming-read probe,
+bf16 dense head, zero-density sweep and small-batch GEMM.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Ternary GEMV weight GB/s (% HBM peak) + µs/decode-step, 2B4T shapes"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BASE_SEED = 0x2B47
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bitserial_decode_step_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_kernels.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def host_threads() -> int:
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class DecodeSet:
+    """The 210 matrices of one decode step in `copies` HBM copies, plus activations and outputs."""
+
+    def __init__(self, bpw, torch, synth, dev, copies: int, p_zero: float, base: int, layers=None,
+                 cpu_oracle=None):
+        self.plane_bytes = 0
+        self.weights = 0
+        self.copies = []
+        xs, outs, host_mats = [], [], []
+        shapes = synth.decode_step_shapes()
+        layer_cache = {}
+        for (layer, proj, name, rows, cols) in shapes:
+            src_layer = layer if layers is None else layers(layer)
+            key = (src_layer, proj)
+            case = layer_cache.get(key)
+            if case is None:
+                case = synth.ternary_case(base, src_layer, proj, rows, cols, p_zero)
+                if layers is not None:
+                    layer_cache[key] = case
+            planes = bpw.bpw_pack_i8(case.w)
+            if cpu_oracle is not None:
+                cpu_oracle(case)
+            hm = bpw.bpw_load(planes, rows, cols, case.w_scale)
+            host_mats.append(hm)
+            x = torch.from_numpy(case.x).to(dev)  # cols is a multiple of 64: bpr * 64 bytes
+            oi = torch.empty(rows, dtype=torch.int32, device=dev)
+            of = torch.empty(rows, dtype=torch.float32, device=dev)
+            xs.append((x, case.x_scale))
+            outs.append((oi, of))
+            self.plane_bytes += hm.nbytes
+            self.weights += rows * cols
+        for c in range(copies):
+            mats = []
+            for hm in host_mats:
+                buf = torch.empty(hm.nbytes, dtype=torch.uint8, device=dev)
+                mats.append(bpw.bpw_upload(hm, buf))
+            jobs = [bpw.gemv_job(m, x, s, oi, of) for m, (x, s), (oi, of) in zip(mats, xs, outs)]
+            ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+            self.copies.append((bpw.GemvPlan(jobs, ws), mats, ws))
+        for hm in host_mats:
+            hm.free()
+        self.xs, self.outs = xs, outs
+
+    def plan(self, i):
+        return self.copies[i % len(self.copies)][0]
+
+
+def time_main_kernel(torch, dset, reps: int) -> list[float]:
+    """Per-launch GEMV kernel times (ms) from HIP events on the launch stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        p = dset.plan(i)
+        p.run_stage()
+        ev[i][0].record()
+        p.run_main()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def probe_gbs(bpw, torch, dev) -> float:
+    """Streaming-read probe: best of 5 passes over 4 GiB (the pages' measured-roofline method)."""
+    n = 4 << 30
+    buf = torch.zeros(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    bpw.bpw_stream_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        bpw.bpw_stream_read_probe(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return best
+
+
+def head_measure(bpw, torch, synth, dev, reps: int = 20) -> dict:
+    """bf16 dense head 128256 x 2560 (two HBM copies in rotation), median over reps."""
+    rows, cols = synth.VOCAB, synth.HIDDEN
+    w, x = synth.head_case(BASE_SEED + 5)
+    import numpy as np
+    wd = [torch.from_numpy(w.view(np.int16)).to(dev) for _ in range(2)]
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    y = torch.empty(rows, dtype=torch.float32, device=dev)
+    for i in range(3):
+        bpw.bpw_dense_head_gemv(wd[i % 2], xd, y)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        ev[i][0].record()
+        bpw.bpw_dense_head_gemv(wd[i % 2], xd, y)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+    nbytes = rows * cols * 2
+    return {"shape": [rows, cols], "bytes": nbytes, "us": ms * 1e3, "gbs": nbytes / (ms * 1e-3) / 1e9,
+            "pct_hbm_peak": 100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def small_batch_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
+    """Small-batch GEMM at gate/up (6912x2560) and down (2560x6912), B in 1..16; 64 rotating HBM
+    copies of the matrix (283 MB) so weights come from HBM."""
+    out = []
+    for proj, rows, cols in ((4, 6912, 2560), (6, 2560, 6912)):
+        case = synth.ternary_case(BASE_SEED + 7, 0, proj, rows, cols)
+        hm = bpw.bpw_load(bpw.bpw_pack_i8(case.w), rows, cols, case.w_scale)
+        mats = []
+        for _ in range(64):
+            buf = torch.empty(hm.nbytes, dtype=torch.uint8, device=dev)
+            mats.append(bpw.bpw_upload(hm, buf))
+        nbytes = hm.nbytes
+        hm.free()
+        for batch in (1, 2, 4, 8, 16):
+            X, sc = synth.small_batch_x(BASE_SEED + 11, batch, cols)
+            Xd = torch.from_numpy(X).to(dev)
+            oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
+            of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
+            ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(mats[0], batch), dtype=torch.uint8,
+                             device=dev)
+            for i in range(3):
+                bpw.bpw_gemm_small_batch(mats[i], Xd, sc, oi, of, ws)
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+            for i in range(reps):
+                ev[i][0].record()
+                bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of, ws)
+                ev[i][1].record()
+            torch.cuda.synchronize()
+            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            out.append({"shape": [rows, cols], "batch": batch, "us": round(ms * 1e3, 2),
+                        "weight_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                        "tops_equiv": round(2.0 * rows * cols * batch / (ms * 1e-3) / 1e12, 2)})
+        del mats
+    torch.cuda.empty_cache()
+    return out
+
+
+def z_sweep_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
+    """Decode-step-shaped sets (one generated layer repeated over 30 layers, 2 HBM copies) at
+    P(0) in the sweep; GEMV kernel median per step."""
+    out = []
+    for z in synth.P_ZERO_SWEEP:
+        ds = DecodeSet(bpw, torch, synth, dev, copies=2, p_zero=z, base=BASE_SEED + 13, layers=lambda l: 0)
+        for i in range(4):
+            ds.plan(i).run()
+        torch.cuda.synchronize()
+        ms = statistics.median(time_main_kernel(torch, ds, reps))
+        out.append({"p_zero": z, "gemv_us": round(ms * 1e3, 2),
+                    "weight_gbs": round(ds.plane_bytes / (ms * 1e-3) / 1e9, 1)})
+        del ds
+        torch.cuda.empty_cache()
+    return out
+
+
+def traffic_from_profile() -> float | None:
+    """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=3, help="HBM copies of the weight set used in rotation")
+    ap.add_argument("--kernel", choices=("auto", "bitserial", "bytelane"), default="auto")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip probe, head, sweep and small batch")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import bit_plane_weight_amd as bpw
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bpw.bpw_device_check()
+    kernel = {"auto": bpw.KERNEL_AUTO, "bitserial": bpw.KERNEL_BITSERIAL, "bytelane": bpw.KERNEL_BYTELANE}[args.kernel]
+
+    # ---------------------------------------------------------------- CPU oracle baseline (host cores)
+    cpu = {"seconds": 0.0, "bytes": 0, "matrices": 0}
+    nthreads = host_threads()
+    oracle_fn = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def oracle_fn(case):
+            if cpu["seconds"] > 20.0:  # bounded sample
+                return
+            planes = oracle.pack(case.w)
+            t = time.perf_counter()
+            oracle.gemv(planes, case.rows, case.cols, case.x, case.x_scale, case.w_scale, nthreads=nthreads)
+            cpu["seconds"] += time.perf_counter() - t
+            cpu["bytes"] += planes.size
+            cpu["matrices"] += 1
+
+    log("generating, packing and uploading the decode-step set")
+    t0 = time.perf_counter()
+    ds = DecodeSet(bpw, torch, synth, dev, copies=args.copies, p_zero=synth.P_ZERO_2B4T, base=BASE_SEED,
+                   cpu_oracle=oracle_fn)
+    if kernel != bpw.KERNEL_AUTO:
+        for i, (plan, mats, ws) in enumerate(ds.copies):
+            plan.free()
+            jobs = [bpw.gemv_job(m, x, s, oi, of) for m, (x, s), (oi, of) in zip(mats, ds.xs, ds.outs)]
+            ds.copies[i] = (bpw.GemvPlan(jobs, ws, kernel), mats, ws)
+    log(f"setup {time.perf_counter() - t0:.1f}s: {ds.weights} weights, {ds.plane_bytes} plane bytes, "
+        f"{len(ds.copies)} copies")
+
+    # ---------------------------------------------------------------- timed steps
+    for i in range(args.warmup):
+        ds.plan(i).run()
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        p = ds.plan(i)
+        p.run_stage()
+        ev[i][0].record()
+        p.run_main()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    wall = t_end - t_start
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    ms_per_step = wall / K * 1e3
+    value = ds.plane_bytes * K / wall / 1e9
+    achieved = ds.plane_bytes / (kern_avg_ms * 1e-3) / 1e9
+    log(f"step {ms_per_step * 1e3:.1f} us, {value:.0f} GB/s; GEMV kernel avg {kern_avg_ms * 1e3:.1f} us "
+        f"(median {statistics.median(kern_ms) * 1e3:.1f}), {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i32",
+        "data": "synthetic",
+        "config": {
+            "workload": "decode-step ternary GEMV set: 210 .trit v1 matrices (30 layers x q 2560x2560, "
+                        "k/v 640x2560, o 2560x2560, gate/up 6912x2560, down 2560x6912), BitNet b1.58 2B4T "
+                        "shapes, batch 1, int8 absmax activations, P(0)=0.4219, weights streamed from HBM",
+            "matrices": 210,
+            "weights": ds.weights,
+            "plane_bytes": ds.plane_bytes,
+            "hbm_copies_in_rotation": len(ds.copies),
+            "kernel": args.kernel,
+        },
+        "decode_step_us": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile(),
+            "kernel": "gemv_bitserial_kernel" if kernel != bpw.KERNEL_BYTELANE else "gemv_bytelane_kernel",
+            "kernel_avg_us": round(kern_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": ds.plane_bytes,
+        },
+    }
+    if not args.no_cpu_baseline and cpu["seconds"] > 0:
+        result["cpu_baseline"] = {
+            "value": round(cpu["bytes"] / cpu["seconds"] / 1e9, 4),
+            "unit": "GB/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"{cpu['matrices']} of the 210 decode-step matrices ({cpu['bytes']} plane bytes), "
+                      f"one oracle GEMV each on {nthreads} host threads, {cpu['seconds']:.1f} s",
+        }
+
+    # ---------------------------------------------------------------- companion measurements
+    if not args.no_extras:
+        del ds
+        torch.cuda.empty_cache()
+        log("probe")
+        pg = probe_gbs(bpw, torch, dev)
+        result["probe_gbs"] = round(pg, 1)
+        result["pct_probe"] = round(100.0 * achieved / pg, 2)
+        log("dense head")
+        head = head_measure(bpw, torch, synth, dev)
+        result["head"] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in head.items()}
+        result["per_token_us"] = round(kern_avg_ms * 1e3 + head["us"], 2)
+        result["per_token_bytes"] = result["config"]["plane_bytes"] + head["bytes"]
+        log("zero-density sweep")
+        result["z_sweep"] = z_sweep_measure(bpw, torch, synth, dev)
+        log("small batch")
+        result["small_batch"] = small_batch_measure(bpw, torch, synth, dev)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

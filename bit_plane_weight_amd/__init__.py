@@ -1,0 +1,253 @@
+"""bit_plane_weight_amd - ternary bit-plane (.trit v1) GEMV on AMD Instinct MI355X (gfx950).
+
+A thin binding over libbpw's C ABI (include/bpw.h) with the same entry-point names. Every step
+of the computation runs in libbpw's HIP kernels; this module only marshals arguments. PyTorch
+is used for device memory (tensors passed by data_ptr()) and streams. Host buffers are numpy
+arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _lib
+from ._lib import (BpwDevMat, BpwError, BpwGemvJob, KERNEL_AUTO, KERNEL_BITSERIAL,  # noqa: F401
+                   KERNEL_BYTELANE)
+
+__all__ = [
+    "BpwError", "KERNEL_AUTO", "KERNEL_BITSERIAL", "KERNEL_BYTELANE",
+    "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
+    "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
+    "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
+    "bpw_gemm_small_batch_workspace_bytes", "bpw_gemm_small_batch",
+    "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
+]
+
+
+def _np(a: np.ndarray, dtype) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise TypeError(f"expected {np.dtype(dtype)}, got {a.dtype}")
+    return a
+
+
+def _dptr(t) -> int | None:
+    """Device address of a torch tensor (None stays NULL)."""
+    if t is None:
+        return None
+    if not getattr(t, "is_cuda", False):
+        raise TypeError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("GPU tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------------------ library
+
+
+def bpw_abi_version() -> int:
+    return _lib.lib().bpw_abi_version()
+
+
+def bpw_status_string(status: int) -> str:
+    return _lib.lib().bpw_status_string(status).decode()
+
+
+def bpw_last_error() -> str:
+    return _lib.lib().bpw_last_error().decode()
+
+
+def bpw_device_check() -> None:
+    _lib.check(_lib.lib().bpw_device_check())
+
+
+# ------------------------------------------------------------------------------ host side
+
+
+def bpw_pack_i8(w: np.ndarray) -> np.ndarray:
+    """int8 [rows, cols] in {-1, 0, +1} -> .trit v1 plane bytes (uint8 [rows * bpr * 16])."""
+    w = _np(w, np.int8)
+    rows, cols = w.shape
+    out = np.empty(rows * ((cols + 63) // 64) * 16, dtype=np.uint8)
+    err = _lib.BpwErr()
+    _lib.check(_lib.lib().bpw_pack_i8(w.ctypes.data, rows, cols, out.ctypes.data, out.size, ctypes.byref(err)),
+               err)
+    return out
+
+
+def bpw_validate(planes: np.ndarray, rows: int, cols: int) -> None:
+    planes = _np(planes, np.uint8)
+    err = _lib.BpwErr()
+    _lib.check(_lib.lib().bpw_validate(planes.ctypes.data, planes.size, rows, cols, ctypes.byref(err)), err)
+
+
+class HostMat:
+    """A validated, library-owned host copy of one matrix's planes (bpw_host_mat)."""
+
+    def __init__(self, handle: int, rows: int, cols: int, w_scale: float):
+        self._h = ctypes.c_void_p(handle)
+        self.rows, self.cols, self.w_scale = rows, cols, w_scale
+
+    @property
+    def nbytes(self) -> int:
+        return _lib.lib().bpw_host_mat_bytes(self._h)
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_host_mat_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def bpw_load(planes: np.ndarray, rows: int, cols: int, w_scale: float) -> HostMat:
+    planes = _np(planes, np.uint8)
+    h = ctypes.c_void_p()
+    err = _lib.BpwErr()
+    _lib.check(_lib.lib().bpw_load(planes.ctypes.data, planes.size, rows, cols, float(w_scale), ctypes.byref(h),
+                                   ctypes.byref(err)), err)
+    return HostMat(h.value, rows, cols, w_scale)
+
+
+class DevMat:
+    """A matrix resident on the GPU (bpw_dev_mat) plus the tensor that holds its planes."""
+
+    def __init__(self, desc: BpwDevMat, buf):
+        self.desc, self.buf = desc, buf
+
+    @property
+    def rows(self) -> int:
+        return self.desc.rows
+
+    @property
+    def cols(self) -> int:
+        return self.desc.cols
+
+    @property
+    def bpr(self) -> int:
+        return self.desc.bpr
+
+
+def bpw_upload(m: HostMat, d_buf, stream=None) -> DevMat:
+    """Copy m's planes into the uint8 GPU tensor d_buf (>= m.nbytes, 256-byte aligned)."""
+    desc = BpwDevMat()
+    nbytes = d_buf.numel() * d_buf.element_size()
+    _lib.check(_lib.lib().bpw_upload(m._h, _dptr(d_buf), nbytes, _stream(stream), ctypes.byref(desc)))
+    return DevMat(desc, d_buf)
+
+
+# ------------------------------------------------------------------------------ batch-1 GEMV
+
+
+def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None) -> BpwGemvJob:
+    """One bpw_gemv_job: x int8 GPU tensor (>= bpr * 64 bytes), outputs int32 / float32 [rows]."""
+    j = BpwGemvJob()
+    j.m = m.desc
+    j.d_x = _dptr(x)
+    j.x_len = x.numel() * x.element_size()
+    j.x_scale = float(x_scale)
+    j.d_out_i32 = _dptr(out_i32)
+    j.d_out_f32 = _dptr(out_f32)
+    return j
+
+
+def _jobs_array(jobs):
+    arr = (BpwGemvJob * max(1, len(jobs)))(*jobs)
+    return arr, len(jobs)
+
+
+def bpw_gemv_workspace_bytes(jobs) -> int:
+    arr, n = _jobs_array(jobs)
+    return _lib.lib().bpw_gemv_workspace_bytes(arr, n)
+
+
+def bpw_gemv(jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None) -> None:
+    arr, n = _jobs_array(jobs)
+    ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+    _lib.check(_lib.lib().bpw_gemv(arr, n, kernel, _dptr(d_ws), ws_len, _stream(stream)))
+
+
+class GemvPlan:
+    """bpw_gemv_plan: the job table written once into d_ws; run() queues the launches."""
+
+    def __init__(self, jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None):
+        arr, n = _jobs_array(jobs)
+        ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().bpw_gemv_plan_create(arr, n, kernel, _dptr(d_ws), ws_len, _stream(stream),
+                                                   ctypes.byref(h)))
+        self._h, self._keep = h, (jobs, d_ws)
+
+    def run(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_gemv_plan_run(self._h, _stream(stream)))
+
+    def run_stage(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_gemv_plan_run_stage(self._h, _stream(stream)))
+
+    def run_main(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_gemv_plan_run_main(self._h, _stream(stream)))
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_gemv_plan_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------ small batch
+
+
+def bpw_gemm_small_batch_workspace_bytes(m: DevMat, batch: int) -> int:
+    return _lib.lib().bpw_gemm_small_batch_workspace_bytes(ctypes.byref(m.desc), batch)
+
+
+def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, d_ws, kernel: int = KERNEL_AUTO,
+                         stream=None) -> None:
+    """X int8 GPU tensor [batch, ldx]; x_scales host float32 [batch]; outputs [batch, rows]."""
+    batch, ldx = X.shape
+    xs = np.ascontiguousarray(np.asarray(x_scales, dtype=np.float32))
+    ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+    _lib.check(_lib.lib().bpw_gemm_small_batch(ctypes.byref(m.desc), _dptr(X), batch, ldx, xs.ctypes.data,
+                                               _dptr(out_i32), _dptr(out_f32), kernel, _dptr(d_ws), ws_len,
+                                               _stream(stream)))
+
+
+# ------------------------------------------------------------------------------ dense head
+
+
+def bpw_dense_head_gemv(w_bf16, x_bf16, y, stream=None) -> None:
+    """w_bf16 [rows, cols] and x_bf16 [cols] GPU tensors of bf16 bits (int16/uint16/bfloat16); y float32."""
+    rows, cols = w_bf16.shape
+    _lib.check(_lib.lib().bpw_dense_head_gemv(_dptr(w_bf16), rows, cols, _dptr(x_bf16), _dptr(y),
+                                              _stream(stream)))
+
+
+# ------------------------------------------------------------------------------ measurement
+
+
+def bpw_stream_read_probe(d_buf, d_sink, stream=None) -> None:
+    _lib.check(_lib.lib().bpw_stream_read_probe(_dptr(d_buf), d_buf.numel() * d_buf.element_size(),
+                                                _dptr(d_sink), _stream(stream)))
+
+
+def bpw_cache_flush(d_buf, stream=None) -> None:
+    _lib.check(_lib.lib().bpw_cache_flush(_dptr(d_buf), d_buf.numel() * d_buf.element_size(), _stream(stream)))

@@ -1,0 +1,103 @@
+"""ctypes declarations of libbpw's C ABI (include/bpw.h). Loading fails loudly if the library
+is not built: there is no Python or CPU fallback for any entry point."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbpw.so")
+
+# bpw_status
+OK, E_INVAL, E_SIZE, E_P1_BOTH_BITS, E_P2_PADDING, E_NOT_VALIDATED, E_ARCH, E_HIP, E_UNSUPPORTED = range(9)
+# bpw_kernel
+KERNEL_AUTO, KERNEL_BITSERIAL, KERNEL_BYTELANE = 0, 1, 2
+ABI_VERSION = 1
+
+
+class BpwErr(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_int32), ("row", ctypes.c_int64), ("beat", ctypes.c_int64),
+                ("col", ctypes.c_int64)]
+
+
+class BpwDevMat(ctypes.Structure):
+    _fields_ = [("d_planes", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("bpr", ctypes.c_int64), ("w_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
+                ("seal", ctypes.c_uint64)]
+
+
+class BpwGemvJob(ctypes.Structure):
+    _fields_ = [("m", BpwDevMat), ("d_x", ctypes.c_void_p), ("x_len", ctypes.c_int64),
+                ("x_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
+                ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p)]
+
+
+class BpwError(RuntimeError):
+    """A non-OK bpw_status, with the library's reason and (for validation) the offending position."""
+
+    def __init__(self, status: int, reason: str, row: int = -1, beat: int = -1, col: int = -1):
+        self.status, self.reason, self.row, self.beat, self.col = status, reason, row, beat, col
+        where = f" (row {row}, beat {beat}, col {col})" if row >= 0 else ""
+        super().__init__(f"{_status_name(status)}: {reason}{where}")
+
+
+_lib = None
+
+
+def _status_name(s: int) -> str:
+    if _lib is None:
+        return str(s)
+    return _lib.bpw_status_string(s).decode()
+
+
+def lib():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() (hipcc, gfx950)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    E = ctypes.POINTER(BpwErr)
+    M = ctypes.POINTER(BpwDevMat)
+    J = ctypes.POINTER(BpwGemvJob)
+    sig = {
+        "bpw_abi_version": (i32, []),
+        "bpw_status_string": (ctypes.c_char_p, [i32]),
+        "bpw_last_error": (ctypes.c_char_p, []),
+        "bpw_device_check": (i32, []),
+        "bpw_pack_i8": (i32, [vp, i64, i64, vp, sz, E]),
+        "bpw_validate": (i32, [vp, sz, i64, i64, E]),
+        "bpw_load": (i32, [vp, sz, i64, i64, f32, ctypes.POINTER(vp), E]),
+        "bpw_host_mat_free": (None, [vp]),
+        "bpw_host_mat_bytes": (sz, [vp]),
+        "bpw_upload": (i32, [vp, vp, sz, vp, M]),
+        "bpw_gemv_workspace_bytes": (sz, [J, i32]),
+        "bpw_gemv": (i32, [J, i32, i32, vp, sz, vp]),
+        "bpw_gemv_plan_create": (i32, [J, i32, i32, vp, sz, vp, ctypes.POINTER(vp)]),
+        "bpw_gemv_plan_run": (i32, [vp, vp]),
+        "bpw_gemv_plan_run_stage": (i32, [vp, vp]),
+        "bpw_gemv_plan_run_main": (i32, [vp, vp]),
+        "bpw_gemv_plan_free": (None, [vp]),
+        "bpw_gemm_small_batch_workspace_bytes": (sz, [M, i32]),
+        "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp, sz, vp]),
+        "bpw_dense_head_gemv": (i32, [vp, i64, i64, vp, vp, vp]),
+        "bpw_stream_read_probe": (i32, [vp, sz, vp, vp]),
+        "bpw_cache_flush": (i32, [vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    if L.bpw_abi_version() != ABI_VERSION:
+        raise ImportError(f"libbpw ABI {L.bpw_abi_version()} != expected {ABI_VERSION}")
+    _lib = L
+    return L
+
+
+def check(status: int, err: BpwErr | None = None) -> None:
+    if status != OK:
+        reason = lib().bpw_last_error().decode()
+        if err is not None and err.row >= 0:
+            raise BpwError(status, reason, err.row, err.beat, err.col)
+        raise BpwError(status, reason)

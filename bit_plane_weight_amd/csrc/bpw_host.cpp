@@ -1,0 +1,683 @@
+// bpw_host.cpp - host side of libbpw: argument checks, .trit v1 packing and validation,
+// upload, grouped-GEMV planning and kernel dispatch. See include/bpw.h for the contract.
+//
+// Passages followed (cited by page title and section):
+//   "The .trit format, version 1": 2.2 (scale finite and > 0), 2.3 (beat layout, P1, P2 with a
+//   64-bit tail mask), section 4 (checks 15, 17, 18 and how violations are reported).
+//   "Tritium: One Weight Format for Ternary Inference ...": "Invariants", "CPU kernels" (a pinned
+//   kernel that cannot run is an error, never a fallback).
+#include <hip/hip_runtime.h>
+#include <emmintrin.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "../../include/bpw.h"
+#include "bpw_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+bpw_status fail(bpw_status code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+bpw_status fail(bpw_status code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+void set_err(bpw_err *e, bpw_status code, int64_t row, int64_t beat, int64_t col) {
+    if (e) {
+        e->code = code;
+        e->row = row;
+        e->beat = beat;
+        e->col = col;
+    }
+}
+
+inline int64_t beats_per_row(int64_t cols) { return (cols + 63) / 64; }
+
+inline uint64_t load_le64(const uint8_t *p) {
+    uint64_t v;
+    std::memcpy(&v, p, 8);  // hosts that run ROCm are little-endian, as the format is
+    return v;
+}
+
+inline void store_le64(uint8_t *p, uint64_t v) { std::memcpy(p, &v, 8); }
+
+// Mask of valid columns in a row's last beat, built in 64 bits (format page 2.3, P2).
+inline uint64_t tail_mask(int64_t cols) {
+    const int r = (int)(cols % 64);
+    return r == 0 ? ~UINT64_C(0) : ((UINT64_C(1) << r) - UINT64_C(1));
+}
+
+bool shape_ok(int64_t rows, int64_t cols) {
+    // rows * bpr * 16 must fit in size_t and the kernels address one matrix with 32-bit offsets.
+    return rows >= 0 && cols >= 0 && rows <= (int64_t)INT32_MAX && cols <= ((int64_t)1 << 40);
+}
+
+// ---------------------------------------------------------------- descriptor seal
+
+uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+    return z ^ (z >> 31);
+}
+
+uint64_t seal_key() {
+    static const uint64_t key = [] {
+        std::random_device rd;
+        uint64_t k = ((uint64_t)rd() << 32) ^ rd();
+        k ^= (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        return mix64(k | 1);
+    }();
+    return key;
+}
+
+uint64_t seal_of(const bpw_dev_mat &m) {
+    uint32_t sb;
+    std::memcpy(&sb, &m.w_scale, 4);
+    uint64_t h = seal_key();
+    h = mix64(h ^ (uint64_t)(uintptr_t)m.d_planes);
+    h = mix64(h ^ (uint64_t)m.rows);
+    h = mix64(h ^ (uint64_t)m.cols);
+    h = mix64(h ^ (uint64_t)m.bpr);
+    h = mix64(h ^ (uint64_t)sb ^ ((uint64_t)m.reserved << 32));
+    return h;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.0f; }
+
+// ---------------------------------------------------------------- device check
+
+std::atomic<int> g_arch_state[64];  // 0 unknown, 1 gfx950, 2 other
+
+bpw_status check_device() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(BPW_E_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    const char *force = std::getenv("BPW_FORCE_ARCH_MISMATCH");  // test hook: can only make calls fail
+    if (force && force[0] == '1') return fail(BPW_E_ARCH, "device %d: architecture check forced to fail", dev);
+    const int slot = dev >= 0 && dev < 64 ? dev : -1;
+    if (slot >= 0) {
+        const int st = g_arch_state[slot].load(std::memory_order_acquire);
+        if (st == 1) return BPW_OK;
+        if (st == 2) return fail(BPW_E_ARCH, "device %d is not gfx950", dev);
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(BPW_E_HIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                    (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':');
+    if (slot >= 0) g_arch_state[slot].store(ok ? 1 : 2, std::memory_order_release);
+    if (!ok) return fail(BPW_E_ARCH, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    return BPW_OK;
+}
+
+bpw_status hip_status(int e, const char *what) {
+    if (e == hipSuccess) return BPW_OK;
+    return fail(BPW_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
+}
+
+// ---------------------------------------------------------------- packing / validation
+
+// Pack one row. Returns the first bad column (or -1).
+int64_t pack_row(const int8_t *w, int64_t cols, int64_t bpr, uint8_t *out) {
+    const __m128i one = _mm_set1_epi8(1), mone = _mm_set1_epi8(-1), zero = _mm_setzero_si128();
+    for (int64_t b = 0; b < bpr; ++b) {
+        const int8_t *src = w + b * 64;
+        uint64_t pos = 0, neg = 0;
+        if ((b + 1) * 64 <= cols) {
+            for (int q = 0; q < 4; ++q) {
+                const __m128i v = _mm_loadu_si128(reinterpret_cast<const __m128i *>(src + 16 * q));
+                const uint32_t p = (uint32_t)_mm_movemask_epi8(_mm_cmpeq_epi8(v, one));
+                const uint32_t n = (uint32_t)_mm_movemask_epi8(_mm_cmpeq_epi8(v, mone));
+                const uint32_t z = (uint32_t)_mm_movemask_epi8(_mm_cmpeq_epi8(v, zero));
+                if ((p | n | z) != 0xFFFFu) {
+                    for (int k = 0; k < 16; ++k) {
+                        const int8_t x = src[16 * q + k];
+                        if (x != 0 && x != 1 && x != -1) return b * 64 + 16 * q + k;
+                    }
+                }
+                pos |= (uint64_t)p << (16 * q);
+                neg |= (uint64_t)n << (16 * q);
+            }
+        } else {
+            for (int64_t k = 0; b * 64 + k < cols; ++k) {
+                const int8_t x = src[k];
+                if (x == 1)
+                    pos |= UINT64_C(1) << k;
+                else if (x == -1)
+                    neg |= UINT64_C(1) << k;
+                else if (x != 0)
+                    return b * 64 + k;
+            }
+        }
+        store_le64(out + b * 16, pos);
+        store_le64(out + b * 16 + 8, neg);
+    }
+    return -1;
+}
+
+bpw_status validate_planes(const uint8_t *planes, size_t len, int64_t rows, int64_t cols, bpw_err *err) {
+    set_err(err, BPW_OK, -1, -1, -1);
+    if (!shape_ok(rows, cols)) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "bad shape rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    }
+    const int64_t bpr = beats_per_row(cols);
+    const uint64_t need = (uint64_t)rows * (uint64_t)bpr * 16u;
+    if ((uint64_t)len != need) {
+        set_err(err, BPW_E_SIZE, -1, -1, -1);
+        return fail(BPW_E_SIZE, "plane bytes %zu != rows * bpr * 16 = %llu", len, (unsigned long long)need);
+    }
+    if (need && !planes) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "planes is NULL");
+    }
+    const uint64_t tail = tail_mask(cols);
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t *row = planes + (size_t)r * (size_t)bpr * 16;
+        uint64_t both = 0;
+        for (int64_t b = 0; b < bpr; ++b) both |= load_le64(row + b * 16) & load_le64(row + b * 16 + 8);
+        const uint64_t last_pos = bpr ? load_le64(row + (bpr - 1) * 16) : 0;
+        const uint64_t last_neg = bpr ? load_le64(row + (bpr - 1) * 16 + 8) : 0;
+        const uint64_t pad = (last_pos | last_neg) & ~tail;
+        if (!both && !pad) continue;
+        // slow path: locate the first offending beat of this row (P1 before P2 within a beat)
+        for (int64_t b = 0; b < bpr; ++b) {
+            const uint64_t p = load_le64(row + b * 16), n = load_le64(row + b * 16 + 8);
+            if (p & n) {
+                const int64_t col = 64 * b + __builtin_ctzll(p & n);
+                set_err(err, BPW_E_P1_BOTH_BITS, r, b, col);
+                return fail(BPW_E_P1_BOTH_BITS, "both planes set at row %lld beat %lld column %lld", (long long)r,
+                            (long long)b, (long long)col);
+            }
+            if (b == bpr - 1 && ((p | n) & ~tail)) {
+                const int64_t col = 64 * b + __builtin_ctzll((p | n) & ~tail);
+                set_err(err, BPW_E_P2_PADDING, r, b, col);
+                return fail(BPW_E_P2_PADDING, "padding bit set in row %lld (column %lld >= cols %lld)", (long long)r,
+                            (long long)col, (long long)cols);
+            }
+        }
+    }
+    return BPW_OK;
+}
+
+}  // namespace
+
+struct bpw_host_mat {
+    uint8_t *planes;
+    size_t bytes;
+    int64_t rows, cols, bpr;
+    float w_scale;
+};
+
+// ---------------------------------------------------------------- grouped GEMV plan
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+struct Geometry {
+    int32_t glog, kblk, nchunk, tile_rows;
+};
+
+// Lanes per row G = 2^glog and blocks per lane K: the smallest power-of-two G with
+// ceil(bpr / G) <= kKMax, capped at a full wave; wider rows take several passes.
+Geometry geometry_for(int64_t bpr) {
+    Geometry g{0, 0, 0, 0};
+    if (bpr == 0) {
+        g.tile_rows = bpw::kWaves * bpw::kIters * 64;
+        return g;
+    }
+    int glog = 0;
+    while (glog < 6 && ((bpr + (1 << glog) - 1) >> glog) > bpw::kKMax) ++glog;
+    const int64_t G = (int64_t)1 << glog;
+    int64_t k = (bpr + G - 1) / G;
+    int64_t nchunk = 1;
+    if (k > bpw::kKMax) {
+        k = bpw::kKMax;
+        nchunk = (bpr + G * k - 1) / (G * k);
+    }
+    g.glog = glog;
+    g.kblk = (int32_t)k;
+    g.nchunk = (int32_t)nchunk;
+    g.tile_rows = bpw::kWaves * bpw::kIters * (int32_t)(64 >> glog);
+    return g;
+}
+
+struct Layout {
+    size_t jobs_off, tiles_off, stage_off, xplanes_off, total;
+    int64_t n_tiles, n_stage;
+    std::vector<size_t> xplane_offs;
+};
+
+Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool stage) {
+    Layout L{};
+    L.jobs_off = 0;
+    int64_t tiles = 0, stage_items = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const Geometry g = geometry_for(jobs[i].m.bpr);
+        tiles += (jobs[i].m.rows + g.tile_rows - 1) / g.tile_rows;
+        if (stage) stage_items += jobs[i].m.bpr;
+    }
+    L.n_tiles = tiles;
+    L.n_stage = stage_items;
+    L.tiles_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
+    L.stage_off = align_up(L.tiles_off + sizeof(bpw::DevTile) * (size_t)tiles);
+    L.xplanes_off = align_up(L.stage_off + sizeof(bpw::StageItem) * (size_t)stage_items);
+    size_t off = L.xplanes_off;
+    L.xplane_offs.resize((size_t)n);
+    for (int32_t i = 0; i < n; ++i) {
+        L.xplane_offs[(size_t)i] = off;
+        if (stage) off = align_up(off + (size_t)jobs[i].m.bpr * 64);
+    }
+    L.total = off;
+    return L;
+}
+
+bpw_status check_dev_mat(const bpw_dev_mat *m, const char *who) {
+    if (!m) return fail(BPW_E_INVAL, "%s: matrix descriptor is NULL", who);
+    if (m->seal != seal_of(*m))
+        return fail(BPW_E_NOT_VALIDATED, "%s: matrix descriptor was not produced by bpw_upload (or was modified)",
+                    who);
+    return BPW_OK;
+}
+
+bpw_status check_job(const bpw_gemv_job &j, int32_t i) {
+    char who[48];
+    std::snprintf(who, sizeof who, "job %d", i);
+    bpw_status st = check_dev_mat(&j.m, who);
+    if (st) return st;
+    const uint64_t bytes = (uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u;
+    const Geometry g = geometry_for(j.m.bpr);
+    if ((uint64_t)(j.m.rows + g.tile_rows) * (uint64_t)j.m.bpr * 16u >= 0xFFFFFFF0ull)
+        return fail(BPW_E_UNSUPPORTED, "%s: %llu plane bytes exceed the 32-bit offsets of one matrix", who,
+                    (unsigned long long)bytes);
+    if (!j.d_x) return fail(BPW_E_INVAL, "%s: d_x is NULL", who);
+    if (((uintptr_t)j.d_x & 15u) != 0) return fail(BPW_E_INVAL, "%s: d_x must be 16-byte aligned", who);
+    if (j.x_len < j.m.bpr * 64)
+        return fail(BPW_E_INVAL, "%s: x_len %lld < bpr * 64 = %lld", who, (long long)j.x_len,
+                    (long long)(j.m.bpr * 64));
+    if (!j.d_out_i32) return fail(BPW_E_INVAL, "%s: d_out_i32 is NULL", who);
+    if (!std::isfinite(j.x_scale)) return fail(BPW_E_INVAL, "%s: x_scale is not finite", who);
+    return BPW_OK;
+}
+
+}  // namespace
+
+struct bpw_gemv_plan {
+    int device;
+    int32_t kernel;
+    const bpw::DevJob *jobs;
+    const bpw::DevTile *tiles;
+    const bpw::StageItem *stage;
+    int64_t n_tiles, n_stage;
+};
+
+// ---------------------------------------------------------------- ABI
+
+extern "C" {
+
+int32_t bpw_abi_version(void) { return BPW_ABI_VERSION; }
+
+const char *bpw_status_string(int32_t s) {
+    switch (s) {
+        case BPW_OK: return "BPW_OK";
+        case BPW_E_INVAL: return "BPW_E_INVAL";
+        case BPW_E_SIZE: return "BPW_E_SIZE";
+        case BPW_E_P1_BOTH_BITS: return "BPW_E_P1_BOTH_BITS";
+        case BPW_E_P2_PADDING: return "BPW_E_P2_PADDING";
+        case BPW_E_NOT_VALIDATED: return "BPW_E_NOT_VALIDATED";
+        case BPW_E_ARCH: return "BPW_E_ARCH";
+        case BPW_E_HIP: return "BPW_E_HIP";
+        case BPW_E_UNSUPPORTED: return "BPW_E_UNSUPPORTED";
+        default: return "unknown status";
+    }
+}
+
+const char *bpw_last_error(void) { return g_last_error.c_str(); }
+
+bpw_status bpw_device_check(void) { return check_device(); }
+
+bpw_status bpw_pack_i8(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, size_t planes_len,
+                       bpw_err *err) {
+    set_err(err, BPW_OK, -1, -1, -1);
+    if (!shape_ok(rows, cols)) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "bad shape rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    }
+    const int64_t bpr = beats_per_row(cols);
+    const uint64_t need = (uint64_t)rows * (uint64_t)bpr * 16u;
+    if ((uint64_t)planes_len != need) {
+        set_err(err, BPW_E_SIZE, -1, -1, -1);
+        return fail(BPW_E_SIZE, "planes_len %zu != rows * bpr * 16 = %llu", planes_len, (unsigned long long)need);
+    }
+    if (need && (!w || !planes)) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "NULL input or output");
+    }
+    // Tail beats read past `cols` only through the scalar path, so a row buffer of exactly cols
+    // bytes is never overrun.
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t bad = pack_row(w + r * cols, cols, bpr, planes + (size_t)r * (size_t)bpr * 16);
+        if (bad >= 0) {
+            set_err(err, BPW_E_INVAL, r, bad / 64, bad);
+            return fail(BPW_E_INVAL, "weight %d at row %lld column %lld is not in {-1, 0, +1}",
+                        (int)w[r * cols + bad], (long long)r, (long long)bad);
+        }
+    }
+    return BPW_OK;
+}
+
+bpw_status bpw_validate(const uint8_t *planes, size_t len, int64_t rows, int64_t cols, bpw_err *err) {
+    return validate_planes(planes, len, rows, cols, err);
+}
+
+bpw_status bpw_load(const uint8_t *planes, size_t len, int64_t rows, int64_t cols, float w_scale,
+                    bpw_host_mat **out, bpw_err *err) {
+    set_err(err, BPW_OK, -1, -1, -1);
+    if (!out) return fail(BPW_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (!scale_ok(w_scale)) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "w_scale %g must be finite and > 0", (double)w_scale);
+    }
+    if (!shape_ok(rows, cols)) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "bad shape rows=%lld cols=%lld", (long long)rows, (long long)cols);
+    }
+    const int64_t bpr = beats_per_row(cols);
+    const uint64_t need = (uint64_t)rows * (uint64_t)bpr * 16u;
+    if ((uint64_t)len != need) {
+        set_err(err, BPW_E_SIZE, -1, -1, -1);
+        return fail(BPW_E_SIZE, "plane bytes %zu != rows * bpr * 16 = %llu", len, (unsigned long long)need);
+    }
+    if (need && !planes) {
+        set_err(err, BPW_E_INVAL, -1, -1, -1);
+        return fail(BPW_E_INVAL, "planes is NULL");
+    }
+    auto *m = new (std::nothrow) bpw_host_mat;
+    if (!m) return fail(BPW_E_INVAL, "out of host memory");
+    m->bytes = (size_t)need;
+    m->planes = need ? static_cast<uint8_t *>(std::aligned_alloc(64, align_up((size_t)need))) : nullptr;
+    if (need && !m->planes) {
+        delete m;
+        return fail(BPW_E_INVAL, "out of host memory for %zu bytes", (size_t)need);
+    }
+    if (need) std::memcpy(m->planes, planes, (size_t)need);
+    m->rows = rows;
+    m->cols = cols;
+    m->bpr = bpr;
+    m->w_scale = w_scale;
+    // validate the library's own copy, so later writes to the caller's buffer cannot matter
+    bpw_status st = validate_planes(m->planes, m->bytes, rows, cols, err);
+    if (st) {
+        std::free(m->planes);
+        delete m;
+        return st;
+    }
+    *out = m;
+    return BPW_OK;
+}
+
+void bpw_host_mat_free(bpw_host_mat *m) {
+    if (!m) return;
+    std::free(m->planes);
+    delete m;
+}
+
+size_t bpw_host_mat_bytes(const bpw_host_mat *m) { return m ? m->bytes : 0; }
+
+bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *stream, bpw_dev_mat *out) {
+    if (!m || !out) return fail(BPW_E_INVAL, "NULL matrix or output descriptor");
+    std::memset(out, 0, sizeof *out);
+    if (m->bytes && !d_dst) return fail(BPW_E_INVAL, "d_dst is NULL");
+    if (d_len < m->bytes) return fail(BPW_E_SIZE, "d_len %zu < plane bytes %zu", d_len, m->bytes);
+    if (((uintptr_t)d_dst & (kAlign - 1)) != 0) return fail(BPW_E_INVAL, "d_dst must be 256-byte aligned");
+    bpw_status st = check_device();
+    if (st) return st;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (m->bytes) {
+        st = hip_status(hipMemcpyAsync(d_dst, m->planes, m->bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+        if (st) return st;
+        st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
+        if (st) return st;
+    }
+    out->d_planes = d_dst;
+    out->rows = m->rows;
+    out->cols = m->cols;
+    out->bpr = m->bpr;
+    out->w_scale = m->w_scale;
+    out->reserved = 0;
+    out->seal = seal_of(*out);
+    return BPW_OK;
+}
+
+size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs) {
+    if (!jobs || n_jobs <= 0) return 0;
+    return layout_for(jobs, n_jobs, true).total;
+}
+
+bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
+                                size_t ws_len, void *stream, bpw_gemv_plan **out) {
+    if (!out) return fail(BPW_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad job list");
+    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_BYTELANE)
+        return fail(BPW_E_UNSUPPORTED, "unknown kernel %d", (int)kernel);
+    const int variant = (kernel == BPW_KERNEL_BYTELANE) ? 2 : 1;
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        bpw_status st = check_job(jobs[i], i);
+        if (st) return st;
+    }
+    const bool stage = (variant == 1);
+    Layout L = layout_for(jobs, n_jobs, stage);
+    if (L.n_tiles > (int64_t)INT32_MAX || L.n_stage > (int64_t)INT32_MAX)
+        return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
+    if (n_jobs > 0 && L.total > ws_len)
+        return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, L.total);
+    if (n_jobs > 0 && !d_ws) return fail(BPW_E_INVAL, "d_ws is NULL");
+    if (((uintptr_t)d_ws & (kAlign - 1)) != 0) return fail(BPW_E_INVAL, "d_ws must be 256-byte aligned");
+    bpw_status st = check_device();
+    if (st) return st;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+
+    auto *plan = new (std::nothrow) bpw_gemv_plan;
+    if (!plan) return fail(BPW_E_INVAL, "out of host memory");
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    plan->device = dev;
+    plan->kernel = kernel;
+    plan->jobs = reinterpret_cast<const bpw::DevJob *>(ws + L.jobs_off);
+    plan->tiles = reinterpret_cast<const bpw::DevTile *>(ws + L.tiles_off);
+    plan->stage = reinterpret_cast<const bpw::StageItem *>(ws + L.stage_off);
+    plan->n_tiles = L.n_tiles;
+    plan->n_stage = L.n_stage;
+    if (n_jobs == 0) {
+        *out = plan;
+        return BPW_OK;
+    }
+
+    const size_t table_bytes = L.xplanes_off;
+    std::vector<uint8_t> host(table_bytes, 0);
+    auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
+    auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.tiles_off);
+    auto *hs = reinterpret_cast<bpw::StageItem *>(host.data() + L.stage_off);
+    int64_t t = 0, si = 0;
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        const bpw_gemv_job &j = jobs[i];
+        const Geometry g = geometry_for(j.m.bpr);
+        bpw::DevJob d{};
+        d.planes = static_cast<const uint8_t *>(j.m.d_planes);
+        d.x = j.d_x;
+        d.xplanes = stage ? reinterpret_cast<uint32_t *>(ws + L.xplane_offs[(size_t)i]) : nullptr;
+        d.out_i32 = j.d_out_i32;
+        d.out_f32 = j.d_out_f32;
+        d.rows = (int32_t)j.m.rows;
+        d.bpr = (int32_t)j.m.bpr;
+        d.x_scale = j.x_scale;
+        d.w_scale = j.m.w_scale;
+        d.glog = g.glog;
+        d.kblk = g.kblk;
+        d.nchunk = g.nchunk;
+        d.tile_rows = g.tile_rows;
+        hj[i] = d;
+        for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
+        if (stage)
+            for (int64_t b = 0; b < j.m.bpr; ++b) hs[si++] = bpw::StageItem{i, (int32_t)b};
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+    if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
+    if (st) {
+        delete plan;
+        return st;
+    }
+    *out = plan;
+    return BPW_OK;
+}
+
+static bpw_status plan_ready(const bpw_gemv_plan *plan) {
+    if (!plan) return fail(BPW_E_INVAL, "plan is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+        return fail(BPW_E_INVAL, "plan was created on device %d, current device is %d", plan->device, dev);
+    return check_device();
+}
+
+bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream) {
+    bpw_status st = plan_ready(plan);
+    if (st) return st;
+    if (plan->kernel == BPW_KERNEL_BYTELANE || plan->n_stage == 0) return BPW_OK;
+    return hip_status(bpw::launch_stage_xplanes(plan->jobs, plan->stage, (int32_t)plan->n_stage, stream),
+                      "stage launch");
+}
+
+bpw_status bpw_gemv_plan_run_main(const bpw_gemv_plan *plan, void *stream) {
+    bpw_status st = plan_ready(plan);
+    if (st) return st;
+    if (plan->n_tiles == 0) return BPW_OK;
+    const int variant = (plan->kernel == BPW_KERNEL_BYTELANE) ? 2 : 1;
+    return hip_status(bpw::launch_gemv(variant, plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
+                      "gemv launch");
+}
+
+bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream) {
+    bpw_status st = bpw_gemv_plan_run_stage(plan, stream);
+    if (st) return st;
+    return bpw_gemv_plan_run_main(plan, stream);
+}
+
+void bpw_gemv_plan_free(bpw_gemv_plan *plan) { delete plan; }
+
+bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws, size_t ws_len,
+                    void *stream) {
+    if (n_jobs == 0) return BPW_OK;
+    bpw_gemv_plan *plan = nullptr;
+    bpw_status st = bpw_gemv_plan_create(jobs, n_jobs, kernel, d_ws, ws_len, stream, &plan);
+    if (st) return st;
+    st = bpw_gemv_plan_run(plan, stream);
+    bpw_gemv_plan_free(plan);
+    return st;
+}
+
+size_t bpw_gemm_small_batch_workspace_bytes(const bpw_dev_mat *m, int32_t batch) {
+    if (!m || batch <= 0) return 0;
+    return align_up((size_t)batch * (size_t)m->bpr * 64);
+}
+
+bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
+                                const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
+                                void *d_ws, size_t ws_len, void *stream) {
+    bpw_status st = check_dev_mat(m, "small batch");
+    if (st) return st;
+    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL)
+        return fail(BPW_E_UNSUPPORTED, "small batch: kernel %d is not available for this entry point", (int)kernel);
+    if (batch < 1 || batch > bpw::kMaxBatch) return fail(BPW_E_INVAL, "batch %d outside [1, 64]", (int)batch);
+    if (!d_X || !x_scales || !d_out_i32) return fail(BPW_E_INVAL, "small batch: NULL argument");
+    if (ldx < m->bpr * 64)
+        return fail(BPW_E_INVAL, "ldx %lld < bpr * 64 = %lld", (long long)ldx, (long long)(m->bpr * 64));
+    for (int32_t t = 0; t < batch; ++t)
+        if (!std::isfinite(x_scales[t])) return fail(BPW_E_INVAL, "x_scales[%d] is not finite", (int)t);
+    const size_t need = bpw_gemm_small_batch_workspace_bytes(m, batch);
+    if (ws_len < need) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, need);
+    if (need && (!d_ws || ((uintptr_t)d_ws & (kAlign - 1)) != 0))
+        return fail(BPW_E_INVAL, "d_ws must be non-NULL and 256-byte aligned");
+    if (need > 160u * 1024u)
+        return fail(BPW_E_UNSUPPORTED, "batch * bpr * 64 = %zu bytes of activation planes exceed the 160 KiB LDS",
+                    need);
+    const Geometry g = geometry_for(m->bpr);
+    if ((uint64_t)(m->rows + g.tile_rows) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
+        return fail(BPW_E_UNSUPPORTED, "plane bytes exceed the 32-bit offsets of one matrix");
+    st = check_device();
+    if (st) return st;
+    if (m->rows == 0) return BPW_OK;
+    bpw::SmallBatchArgs a{};
+    a.planes = static_cast<const uint8_t *>(m->d_planes);
+    a.xplanes = static_cast<const uint32_t *>(d_ws);
+    a.out_i32 = d_out_i32;
+    a.out_f32 = d_out_f32;
+    a.rows = (int32_t)m->rows;
+    a.bpr = (int32_t)m->bpr;
+    a.batch = batch;
+    a.glog = g.glog;
+    a.kblk = g.kblk;
+    a.nchunk = g.nchunk;
+    a.tile_rows = g.tile_rows;
+    a.w_scale = m->w_scale;
+    for (int32_t t = 0; t < batch; ++t) a.x_scales[t] = x_scales[t];
+    st = hip_status(bpw::launch_stage_batch(d_X, ldx, static_cast<uint32_t *>(d_ws), (int32_t)m->bpr, batch, stream),
+                    "stage launch");
+    if (st) return st;
+    const int32_t tiles = (int32_t)((m->rows + g.tile_rows - 1) / g.tile_rows);
+    return hip_status(bpw::launch_gemm_small_batch(a, tiles, stream), "small batch launch");
+}
+
+bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t cols, const uint16_t *d_x_bf16,
+                               float *d_y, void *stream) {
+    if (rows < 0 || cols < 0) return fail(BPW_E_INVAL, "bad shape");
+    if (rows == 0) return check_device();
+    if (!d_w_bf16 || !d_x_bf16 || !d_y) return fail(BPW_E_INVAL, "dense head: NULL argument");
+    if (cols % 8 != 0) return fail(BPW_E_UNSUPPORTED, "dense head: cols %lld is not a multiple of 8", (long long)cols);
+    if (((uintptr_t)d_w_bf16 & 15u) || ((uintptr_t)d_x_bf16 & 15u))
+        return fail(BPW_E_INVAL, "dense head: W and x must be 16-byte aligned");
+    if (cols * 2 > 64 * 1024)
+        return fail(BPW_E_UNSUPPORTED, "dense head: cols %lld exceed the 32768 staged in LDS", (long long)cols);
+    bpw_status st = check_device();
+    if (st) return st;
+    return hip_status(bpw::launch_dense_head(d_w_bf16, rows, cols, d_x_bf16, d_y, stream), "dense head launch");
+}
+
+bpw_status bpw_stream_read_probe(const void *d_buf, size_t len, uint32_t *d_sink, void *stream) {
+    if (!d_buf || !d_sink || (len % 16) || ((uintptr_t)d_buf & 15u))
+        return fail(BPW_E_INVAL, "probe: buffer must be non-NULL, 16-byte aligned, len %% 16 == 0");
+    bpw_status st = check_device();
+    if (st) return st;
+    return hip_status(bpw::launch_probe(d_buf, len, d_sink, stream), "probe launch");
+}
+
+bpw_status bpw_cache_flush(void *d_buf, size_t len, void *stream) {
+    if (!d_buf || (len % 16) || ((uintptr_t)d_buf & 15u))
+        return fail(BPW_E_INVAL, "flush: buffer must be non-NULL, 16-byte aligned, len %% 16 == 0");
+    bpw_status st = check_device();
+    if (st) return st;
+    return hip_status(bpw::launch_flush(d_buf, len, stream), "flush launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,64 @@
+// bpw_internal.h - device-side tables shared by the host dispatcher (bpw_host.cpp) and the
+// kernels (bpw_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace bpw {
+
+// Launch geometry of the ternary GEMV kernels.
+constexpr int kWaves = 4;                 // waves per workgroup
+constexpr int kThreads = 64 * kWaves;     // wave64
+constexpr int kKMax = 7;                  // 64-column blocks one lane keeps in registers per pass
+constexpr int kIters = 4;                 // row-iterations per wave per tile
+
+// One GEMV of a grouped launch, as the kernels read it (lives in the caller's workspace).
+struct DevJob {
+    const uint8_t *planes;  // rows * bpr beats of 16 bytes
+    const int8_t *x;        // activation codes, >= bpr * 64 bytes readable, 16-byte aligned
+    uint32_t *xplanes;      // workspace: bpr * 16 words of activation bit planes (bit-serial only)
+    int32_t *out_i32;
+    float *out_f32;         // may be null
+    int32_t rows;
+    int32_t bpr;
+    float x_scale;
+    float w_scale;
+    int32_t glog;           // log2 of lanes per row (G)
+    int32_t kblk;           // blocks per lane per pass (<= kKMax; 0 when cols == 0)
+    int32_t nchunk;         // passes over the row: bpr <= G * kblk * nchunk
+    int32_t tile_rows;      // rows per workgroup tile = kWaves * kIters * (64 / G)
+};
+
+struct DevTile {
+    int32_t job;
+    int32_t row0;
+};
+
+struct StageItem {
+    int32_t job;    // (gemv) job index, (small batch) token index
+    int32_t block;  // 64-column block
+};
+
+// Small-batch arguments (passed by value; <= 64 tokens).
+constexpr int kMaxBatch = 64;
+struct SmallBatchArgs {
+    const uint8_t *planes;
+    const uint32_t *xplanes;  // [batch][bpr][16]
+    int32_t *out_i32;         // [batch][rows]
+    float *out_f32;           // [batch][rows] or null
+    int32_t rows, bpr, batch, glog, kblk, nchunk, tile_rows, pad;
+    float w_scale;
+    float x_scales[kMaxBatch];
+};
+
+// Kernel launchers (bpw_kernels.hip). Each returns the hipError_t of its launch as int.
+int launch_stage_xplanes(const DevJob *jobs, const StageItem *items, int32_t n_items, void *stream);
+int launch_gemv(int variant, const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);
+int launch_stage_batch(const int8_t *X, int64_t ldx, uint32_t *xplanes, int32_t bpr, int32_t batch, void *stream);
+int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t n_tiles, void *stream);
+int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
+int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);
+int launch_flush(void *buf, size_t len, void *stream);
+
+}  // namespace bpw

@@ -1,0 +1,227 @@
+/*
+ * bpw.h - C ABI of libbpw: ternary bit-plane (.trit v1) GEMV on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. For a ternary matrix W (rows x cols, entries in {-1, 0, +1}) and an int8
+ * activation x, each output row is the select-accumulate sum
+ *     y[r] = sum of x[c] over W[r][c] = +1  minus  sum of x[c] over W[r][c] = -1
+ * ("Tritium: One Weight Format for Ternary Inference on Commodity CPUs and Multiplier-Free
+ * Hardware", introduction, Equations 2-3; "The .trit format, version 1", section 1). The sum is
+ * exact in int32 and independent of evaluation order (Tritium paper, "CPU kernels" and
+ * "Verification"); x is widened before it is negated, so x = -128 is exact (Tritium paper,
+ * "The hardware core"). The fp32 output applies the activation scale, then the per-tensor
+ * weight scale, each multiply rounded on its own: y = ((float)acc * x_scale) * w_scale
+ * (format page 2.3: the dequantised weight is scale * trit; Tritium paper, "Why exactness,
+ * concretely": scales are applied in turn, not folded).
+ *
+ * Weight layout ("The .trit format, version 1", 2.3 "Ternary payload"). beats_per_row
+ * (bpr) = ceil(cols / 64). Beat b of row r is the 16 bytes at offset (r * bpr + b) * 16:
+ * bytes 0..8 are the little-endian u64 pos plane (bit k set: W[r][64b + k] = +1), bytes 8..16
+ * the neg plane (bit k set: W[r][64b + k] = -1). Invariants: P1 pos & neg == 0 in every beat;
+ * P2 bits past cols in each row's last beat are clear (Tritium paper, "Invariants"). The
+ * library never rewrites these bytes: what is validated is what the GPU streams.
+ *
+ * Conventions for every entry point:
+ *   - Every function that can fail returns bpw_status; nothing is printed, no exception
+ *     crosses the ABI. A failing call also records a one-line reason, readable with
+ *     bpw_last_error() on the same host thread.
+ *   - "host" pointers are ordinary CPU memory; "device" pointers are GPU memory of the
+ *     current HIP device (for example a PyTorch tensor's data_ptr()). The library allocates
+ *     no device memory: all device buffers, workspaces and streams belong to the caller and
+ *     must outlive the work queued on them.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream. Launches are
+ *     asynchronous; faults inside a kernel surface at the caller's next synchronisation.
+ *   - Only gfx950 runs the kernels. Any other device returns BPW_E_ARCH; there is no slower
+ *     fallback path (Tritium paper, "CPU kernels": a pinned kernel that cannot run is an error).
+ *   - A shape the kernels cannot serve returns an error; nothing is silently skipped.
+ */
+#ifndef BPW_H
+#define BPW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BPW_ABI_VERSION 1
+
+typedef enum bpw_status {
+    BPW_OK = 0,
+    BPW_E_INVAL = 1,          /* bad argument: null pointer, negative size, value outside {-1,0,1}, bad scale */
+    BPW_E_SIZE = 2,           /* byte length does not match rows * bpr * 16, or a buffer is too small */
+    BPW_E_P1_BOTH_BITS = 3,   /* a beat has pos & neg != 0 (format page section 4, check 17) */
+    BPW_E_P2_PADDING = 4,     /* a padding bit past cols is set (format page section 4, check 18) */
+    BPW_E_NOT_VALIDATED = 5,  /* a device matrix descriptor that bpw_upload did not produce */
+    BPW_E_ARCH = 6,           /* the current device is not gfx950 */
+    BPW_E_HIP = 7,            /* a HIP runtime call failed (the reason names it) */
+    BPW_E_UNSUPPORTED = 8     /* valid input outside what the kernels serve (the reason says why) */
+} bpw_status;
+
+/* Where a validation error sits. Fields not meaningful for the error are -1. */
+typedef struct bpw_err {
+    int32_t code;  /* a bpw_status */
+    int64_t row;   /* offending row */
+    int64_t beat;  /* offending beat within the row */
+    int64_t col;   /* lowest offending column (P1: the doubly set weight; P2: first set padding bit) */
+} bpw_err;
+
+/* A validated host copy of one ternary matrix's planes (library-owned, opaque). */
+typedef struct bpw_host_mat bpw_host_mat;
+
+/* A ternary matrix resident on the GPU. Plain data, filled in by bpw_upload only: the `seal`
+ * binds the other fields, so a descriptor edited or built by hand is refused with
+ * BPW_E_NOT_VALIDATED. The kernels rely on P1 and P2 and carry no per-beat checks. */
+typedef struct bpw_dev_mat {
+    const void *d_planes; /* device, rows * bpr * 16 bytes, 256-byte aligned */
+    int64_t rows;
+    int64_t cols;
+    int64_t bpr;          /* beats per row = ceil(cols / 64) */
+    float w_scale;        /* per-tensor scale, finite and > 0 (format page 2.2) */
+    uint32_t reserved;
+    uint64_t seal;
+} bpw_dev_mat;
+
+/* One batch-1 GEMV of a grouped launch. */
+typedef struct bpw_gemv_job {
+    bpw_dev_mat m;
+    const int8_t *d_x;    /* device int8 activation codes */
+    int64_t x_len;        /* bytes readable at d_x; must be >= bpr * 64 (codes past cols are ignored) */
+    float x_scale;        /* activation scale: code q stands for x_scale * q */
+    uint32_t reserved;
+    int32_t *d_out_i32;   /* device int32 [rows]: exact sums */
+    float *d_out_f32;     /* device float [rows]: ((float)acc * x_scale) * w_scale, or NULL */
+} bpw_gemv_job;
+
+/* Inner-loop formulation, pinned by name; a pinned kernel that cannot serve the call errors. */
+typedef enum bpw_kernel {
+    BPW_KERNEL_AUTO = 0,      /* the fastest measured formulation (bit-serial) */
+    BPW_KERNEL_BITSERIAL = 1, /* x split into bit planes; per plane one 3-input bit select + popcount
+                                 (Tritium paper, "On popcount": the adder-tree formulation) */
+    BPW_KERNEL_BYTELANE = 2   /* each 4-bit mask group widened to byte lanes, then 4-way int8 dot
+                                 products (the masked-byte formulation of format page section 1) */
+} bpw_kernel;
+
+/* ------------------------------------------------------------------------ library */
+
+/* BPW_ABI_VERSION of the loaded library. */
+int32_t bpw_abi_version(void);
+
+/* Static name of a status code ("BPW_OK", ...); "unknown status" otherwise. */
+const char *bpw_status_string(int32_t status);
+
+/* Reason recorded by the last failing call on this host thread ("" if none). Valid until the
+ * next failing call on the same thread. */
+const char *bpw_last_error(void);
+
+/* BPW_OK if the current HIP device is gfx950, BPW_E_ARCH otherwise (BPW_E_HIP if no device).
+ * Every entry point that launches work runs this check first (cached per device). */
+bpw_status bpw_device_check(void);
+
+/* ------------------------------------------------------------------------ host: pack / validate / load */
+
+/* Pack row-major int8 trits w [rows x cols] into .trit v1 planes (format page 2.3).
+ * planes_len must equal rows * bpr * 16; padding bits are written clear (P2). A value outside
+ * {-1, 0, +1} returns BPW_E_INVAL with its row, beat and column in *err (err may be NULL). */
+bpw_status bpw_pack_i8(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, size_t planes_len,
+                       bpw_err *err);
+
+/* Check host planes in O(payload) (format page section 4, checks 15, 17, 18): length, then every
+ * beat in row-major order for P1, and each row's last beat for P2 with the 64-bit tail mask. The
+ * first offending beat is reported, its lowest bit; within a beat P1 is reported before P2. */
+bpw_status bpw_validate(const uint8_t *planes, size_t len, int64_t rows, int64_t cols, bpw_err *err);
+
+/* Copy host planes into a library-owned buffer, validate the copy (as bpw_validate) and check
+ * w_scale (finite, > 0: format page 2.2). On success *out owns the copy; free it with
+ * bpw_host_mat_free. Later changes to the caller's buffer do not affect a loaded matrix. */
+bpw_status bpw_load(const uint8_t *planes, size_t len, int64_t rows, int64_t cols, float w_scale,
+                    bpw_host_mat **out, bpw_err *err);
+
+void bpw_host_mat_free(bpw_host_mat *m);
+
+/* Plane bytes of a loaded matrix (rows * bpr * 16); 0 for NULL. */
+size_t bpw_host_mat_bytes(const bpw_host_mat *m);
+
+/* ------------------------------------------------------------------------ upload */
+
+/* Copy a loaded matrix's planes byte for byte into caller-owned device memory d_dst (d_len bytes,
+ * >= bpw_host_mat_bytes, 256-byte aligned) on `stream`, wait for the copy, and fill *out.
+ * The device copy is what later calls read; it must stay allocated and unmodified while *out is
+ * used. */
+bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *stream, bpw_dev_mat *out);
+
+/* ------------------------------------------------------------------------ batch-1 GEMV */
+
+/* Device workspace bytes that bpw_gemv / bpw_gemv_plan_create need for these jobs: the job and
+ * tile tables and each job's activation bit planes (bpr * 64 bytes per job). */
+size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs);
+
+/* Run n_jobs independent GEMVs as one grouped launch (plus one activation-staging launch) on
+ * `stream`. The job table is copied into d_ws (ws_len >= bpw_gemv_workspace_bytes); this call
+ * waits until that copy has landed, so it also waits for earlier work on `stream`. Callers that
+ * repeat the same jobs should build a plan once and call bpw_gemv_plan_run. n_jobs == 0 does
+ * nothing and returns BPW_OK. Jobs must not write overlapping outputs. */
+bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws, size_t ws_len,
+                    void *stream);
+
+/* A prepared grouped GEMV: the job table already sits in the caller's workspace. */
+typedef struct bpw_gemv_plan bpw_gemv_plan;
+
+/* Check the jobs, write their tables into d_ws (waiting for the copy, as bpw_gemv does) and return
+ * a host handle. The workspace, the matrices, activations and outputs named by the jobs must stay
+ * valid for the plan's lifetime; their contents may change between runs. */
+bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
+                                size_t ws_len, void *stream, bpw_gemv_plan **out);
+
+/* Queue one execution of a plan on `stream` (two kernel launches, no host-device copies). Runs
+ * queued on one stream execute in order; concurrent runs of one plan on different streams race on
+ * its workspace. */
+bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream);
+
+/* The two halves of bpw_gemv_plan_run, for callers that time or schedule them apart: the first
+ * writes each job's activation bit planes into the workspace (a no-op for BPW_KERNEL_BYTELANE),
+ * the second streams the weights and writes the outputs. Queue them in this order on one stream. */
+bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream);
+bpw_status bpw_gemv_plan_run_main(const bpw_gemv_plan *plan, void *stream);
+
+void bpw_gemv_plan_free(bpw_gemv_plan *plan);
+
+/* ------------------------------------------------------------------------ small-batch GEMM */
+
+/* Device workspace bytes bpw_gemm_small_batch needs for this matrix and batch. */
+size_t bpw_gemm_small_batch_workspace_bytes(const bpw_dev_mat *m, int32_t batch);
+
+/* out[t][r] = sum_c W[r][c] * X[t][c] for t < batch, one pass over the weights: each beat is read
+ * once and applied to every token. X is device int8, token-major, row t at d_X + t * ldx with
+ * ldx >= bpr * 64. x_scales is a HOST float[batch]. d_out_i32 is device int32 [batch x rows];
+ * d_out_f32 (device float [batch x rows], or NULL) gets ((float)acc * x_scales[t]) * w_scale.
+ * 1 <= batch <= 64. With batch == 1 the results equal bpw_gemv's bit for bit. */
+bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
+                                const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
+                                void *d_ws, size_t ws_len, void *stream);
+
+/* ------------------------------------------------------------------------ dense head */
+
+/* The dense tied LM head at batch 1 (Tritium paper, "Where the bytes are"; format page 2.4):
+ * y[v] = sum_h W[v][h] * x[h] with W device bfloat16 [rows x cols] row-major (uint16 bit patterns),
+ * x device bfloat16 [cols], y device float [rows], float32 accumulation. Rows must be 16-byte
+ * aligned: cols % 8 == 0 and d_w 16-byte aligned. */
+bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t cols, const uint16_t *d_x_bf16,
+                               float *d_y, void *stream);
+
+/* ------------------------------------------------------------------------ measurement helpers */
+
+/* Streaming-read probe (Tritium paper, "Method": achieved bandwidth is divided by a streaming-read
+ * probe on the same machine): reads len bytes at d_buf (16-byte aligned, len % 16 == 0) once and
+ * writes a data-dependent word to d_sink (device uint32 [1]) so the reads cannot be elided. */
+bpw_status bpw_stream_read_probe(const void *d_buf, size_t len, uint32_t *d_sink, void *stream);
+
+/* Read and rewrite len bytes at d_buf (16-byte aligned, len % 16 == 0) so that caches hold none of
+ * the bytes a following timed kernel will read (size it above L2 + the 256 MB last-level cache). */
+bpw_status bpw_cache_flush(void *d_buf, size_t len, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BPW_H */

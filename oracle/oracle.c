@@ -96,8 +96,12 @@ int oracle_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, in
     if (rows < 0 || cols < 0) return set_err(e, OR_E_INVAL, -1, -1, -1);
     int64_t bpr = oracle_beats_per_row(cols);
     if (len != rows * bpr * 16) return set_err(e, OR_E_SIZE, -1, -1, -1);
+    /* Rows are independent; each records its first bad column, and the first bad row wins. */
+    int64_t first_bad_row = rows, first_bad_col = -1;
+#pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < rows; ++r) {
-        for (int64_t b = 0; b < bpr; ++b) {
+        int64_t bad = -1;
+        for (int64_t b = 0; b < bpr && bad < 0; ++b) {
             uint64_t pos = 0, neg = 0;
             for (int k = 0; k < 64; ++k) {
                 int64_t c = 64 * b + k;
@@ -107,14 +111,24 @@ int oracle_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, in
                     pos |= UINT64_C(1) << k;
                 else if (v == -1)
                     neg |= UINT64_C(1) << k;
-                else if (v != 0)
-                    return set_err(e, OR_E_INVAL, r, b, c);
+                else if (v != 0) {
+                    bad = c;
+                    break;
+                }
             }
             uint8_t *beat = planes + (r * bpr + b) * 16;
             store_le64(beat, pos);
             store_le64(beat + 8, neg);
         }
+        if (bad >= 0) {
+#pragma omp critical
+            if (r < first_bad_row) {
+                first_bad_row = r;
+                first_bad_col = bad;
+            }
+        }
     }
+    if (first_bad_row < rows) return set_err(e, OR_E_INVAL, first_bad_row, first_bad_col / 64, first_bad_col);
     return set_err(e, OR_OK, -1, -1, -1);
 }
 

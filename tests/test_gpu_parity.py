@@ -1,0 +1,330 @@
+"""GPU parity: libbpw's HIP kernels, called through the C ABI, against the CPU oracle.
+
+Integers must be bit-identical. The ternary fp32 output must lie within rel 1e-6 of the
+oracle's float64 value (and, since both sides apply the scales in turn with the same two
+binary32 roundings, equal the oracle's fp32 bits). The bf16 head must satisfy
+|err| <= 1e-3 * sum|w*x| + 1e-5 per element. Inputs come from the seeded generator only;
+the oracle packs its own planes from the same trits.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+torch = pytest.importorskip("torch")
+import bit_plane_weight_amd as bpw  # noqa: E402
+from bit_plane_weight_amd import _lib  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+NT = min(16, len(os.sched_getaffinity(0)))
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU (they fail rather than skip)"
+    d = torch.device("cuda:0")
+    torch.cuda.set_device(d)
+    bpw.bpw_device_check()
+    return d
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class Uploaded:
+    """One ternary case resident on the GPU: packed by the library, loaded, uploaded."""
+
+    def __init__(self, case, dev, tail_junk=False):
+        self.case = case
+        planes = bpw.bpw_pack_i8(case.w)
+        hm = bpw.bpw_load(planes, case.rows, case.cols, case.w_scale)
+        self.buf = torch.empty(max(hm.nbytes, 1), dtype=torch.uint8, device=dev)
+        self.m = bpw.bpw_upload(hm, self.buf)
+        hm.free()
+        bpr = (case.cols + 63) // 64
+        xh = np.zeros(max(bpr * 64, 16), np.int8)
+        if tail_junk:  # codes past cols are never used (P2 keeps those weights zero)
+            xh[:] = synth.u64(case.cols + 5, xh.size).astype(np.uint8).view(np.int8)
+        xh[: case.cols] = case.x
+        self.x = torch.from_numpy(xh).to(dev)
+        self.oi = torch.full((max(case.rows, 1),), 0x7EADBEEF, dtype=torch.int32, device=dev)
+        self.of = torch.full((max(case.rows, 1),), float("nan"), dtype=torch.float32, device=dev)
+
+    def job(self):
+        return bpw.gemv_job(self.m, self.x, self.case.x_scale, self.oi, self.of)
+
+
+def oracle_ref(case):
+    return oracle.gemv(oracle.pack(case.w), case.rows, case.cols, case.x, case.x_scale, case.w_scale, nthreads=NT)
+
+
+def check_case(u, ref, what):
+    acc, y32, y64 = ref
+    rows = u.case.rows
+    gi = u.oi.cpu().numpy()[:rows]
+    gf = u.of.cpu().numpy()[:rows]
+    bad = np.nonzero(gi != acc)[0]
+    assert bad.size == 0, f"{what}: int32 differs at rows {bad[:8].tolist()} (got {gi[bad[:4]]}, want {acc[bad[:4]]})"
+    err = np.abs(gf.astype(np.float64) - y64)
+    assert np.all(err <= 1e-6 * np.abs(y64)), f"{what}: fp32 outside rel 1e-6 (max rel {np.max(err / np.maximum(np.abs(y64), 1e-300))})"
+    assert np.array_equal(gf.view(np.uint32), y32.view(np.uint32)), f"{what}: fp32 bits differ from scales-in-turn"
+
+
+def run_grouped(cases, dev, kernel=bpw.KERNEL_AUTO, tail_junk=False):
+    ups = [Uploaded(c, dev, tail_junk) for c in cases]
+    jobs = [u.job() for u in ups]
+    ws = torch.empty(max(bpw.bpw_gemv_workspace_bytes(jobs), 256), dtype=torch.uint8, device=dev)
+    bpw.bpw_gemv(jobs, ws, kernel)
+    torch.cuda.synchronize()
+    return ups
+
+
+KERNELS = [bpw.KERNEL_BITSERIAL, bpw.KERNEL_BYTELANE]
+
+
+# ----------------------------------------------------------------------------- configs
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_single_kproj_640x2560(dev, kernel):
+    log(f"case: single k_proj 640x2560 kernel={kernel}")
+    case = synth.ternary_case(101, 0, 1, 640, 2560)
+    (u,) = run_grouped([case], dev, kernel)
+    check_case(u, oracle_ref(case), "k_proj")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_one_layer_seven_projections_grouped(dev, kernel):
+    log(f"case: one layer, 7 projections grouped, kernel={kernel}")
+    cases = synth.layer_cases(202, 3)
+    ups = run_grouped(cases, dev, kernel)
+    for u in ups:
+        check_case(u, oracle_ref(u.case), u.case.name)
+
+
+def test_decode_step_210_matrices_full(dev):
+    """All 210 matrices of a decode step in one grouped plan launch, every output checked."""
+    log("case: decode step, 210 matrices, plan + run (the benchmark's launch)")
+    ups = []
+    for layer in range(synth.N_LAYERS):
+        for c in synth.layer_cases(303, layer):
+            ups.append(Uploaded(c, dev))
+    jobs = [u.job() for u in ups]
+    ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+    plan = bpw.GemvPlan(jobs, ws)
+    plan.run()
+    plan.run()  # a second run over the same tables must give the same results
+    torch.cuda.synchronize()
+    log("  GPU done; oracle over 210 matrices")
+    for u in ups:
+        check_case(u, oracle_ref(u.case), u.case.name)
+    plan.free()
+
+
+@pytest.mark.parametrize("z", synth.P_ZERO_SWEEP)
+def test_zero_density_sweep_layer(dev, z):
+    log(f"case: layer at P(0)={z}")
+    cases = synth.layer_cases(404, 0, p_zero=z)
+    for u in run_grouped(cases, dev):
+        check_case(u, oracle_ref(u.case), f"{u.case.name} z={z}")
+
+
+@pytest.mark.parametrize("batch", (1, 2, 3, 4, 8, 16))
+@pytest.mark.parametrize("shape", ((6912, 2560), (2560, 6912)))
+def test_small_batch(dev, shape, batch):
+    rows, cols = shape
+    log(f"case: small batch {rows}x{cols} B={batch}")
+    case = synth.ternary_case(505, 0, 4 if rows == 6912 else 6, rows, cols)
+    u = Uploaded(case, dev)
+    bpr = (cols + 63) // 64
+    X, sc = synth.small_batch_x(506 + batch, batch, cols)
+    ldx = bpr * 64 + (64 if batch % 2 else 0)
+    Xh = np.full((batch, ldx), 77, np.int8)
+    Xh[:, :cols] = X
+    Xd = torch.from_numpy(Xh).to(dev)
+    oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
+    of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
+    ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(u.m, batch), dtype=torch.uint8, device=dev)
+    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of, ws)
+    torch.cuda.synchronize()
+    acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), rows, cols, Xh, sc, case.w_scale, nthreads=NT)
+    assert np.array_equal(oi.cpu().numpy(), acc)
+    gf = of.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(gf - y64) <= 1e-6 * np.abs(y64))
+    assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    if batch == 1:  # batch 1 equals the GEMV bit for bit
+        case1 = synth.TernaryCase("b1", case.w, X[0], float(sc[0]), case.w_scale)
+        (g,) = run_grouped([case1], dev)
+        assert np.array_equal(g.oi.cpu().numpy(), oi.cpu().numpy()[0])
+        assert np.array_equal(g.of.cpu().numpy().view(np.uint32), of.cpu().numpy()[0].view(np.uint32))
+
+
+def test_dense_head_full_128256x2560(dev):
+    log("case: dense bf16 head 128256x2560")
+    w, x = synth.head_case(606)
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    y = torch.empty(w.shape[0], dtype=torch.float32, device=dev)
+    bpw.bpw_dense_head_gemv(wd, xd, y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.dense_head(w, x, nthreads=NT)
+    err = np.abs(y.cpu().numpy().astype(np.float64) - ry)
+    assert np.all(err <= 1e-3 * rs + 1e-5), f"max err/bound {np.max(err / (1e-3 * rs + 1e-5))}"
+
+
+@pytest.mark.parametrize("rows,cols", ((1, 8), (3, 64), (17, 136), (1000, 2560), (129, 32768), (64, 1024)))
+def test_dense_head_shapes(dev, rows, cols):
+    log(f"case: dense head {rows}x{cols}")
+    w, x = synth.head_case(rows * 7 + cols, rows=rows, cols=cols)
+    wd = torch.from_numpy(w.view(np.int16)).to(dev)
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    y = torch.empty(rows, dtype=torch.float32, device=dev)
+    bpw.bpw_dense_head_gemv(wd, xd, y)
+    torch.cuda.synchronize()
+    ry, rs = oracle.dense_head(w, x)
+    assert np.all(np.abs(y.cpu().numpy().astype(np.float64) - ry) <= 1e-3 * rs + 1e-5)
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+RAGGED_ROWS = (1, 7, 63, 64, 65, 129, 1025)
+RAGGED_COLS = (1, 63, 64, 65, 127, 129, 448, 2500, 7169, 8193)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_ragged_shapes_grouped(dev, kernel):
+    log(f"case: ragged rows x cols grid, kernel={kernel}")
+    cases = []
+    i = 0
+    for r in RAGGED_ROWS:
+        for c in RAGGED_COLS:
+            cases.append(synth.ternary_case(707, i // 7, i % 7, r, c, name=f"{r}x{c}"))
+            i += 1
+    ups = run_grouped(cases, dev, kernel, tail_junk=True)
+    for u in ups:
+        check_case(u, oracle_ref(u.case), u.case.name)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_wide_rows_multi_pass(dev, kernel):
+    """Rows wider than one pass of register-resident blocks (bpr > 7 * 64) take several passes."""
+    log(f"case: wide rows (several passes), kernel={kernel}")
+    cases = [synth.ternary_case(808, 0, 0, 33, 28673, name="33x28673"),
+             synth.ternary_case(808, 0, 1, 5, 65536, name="5x65536"),
+             synth.ternary_case(808, 0, 2, 200, 40000, name="200x40000")]
+    for u in run_grouped(cases, dev, kernel, tail_junk=True):
+        check_case(u, oracle_ref(u.case), u.case.name)
+
+
+def test_empty_rows_and_cols_and_zero_jobs(dev):
+    log("case: empty matrices")
+    cases = [synth.ternary_case(909, 0, 0, 5, 0, name="5x0"), synth.ternary_case(909, 0, 1, 0, 100, name="0x100"),
+             synth.ternary_case(909, 0, 2, 40, 64, name="40x64")]
+    ups = run_grouped(cases, dev)
+    assert np.all(ups[0].oi.cpu().numpy()[:5] == 0)
+    assert np.all(ups[0].of.cpu().numpy()[:5] == 0.0)
+    check_case(ups[2], oracle_ref(cases[2]), "40x64")
+    bpw.bpw_gemv([], None)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_extremes_minus128(dev, kernel):
+    """6912 columns of -1 (and of +1) against x = -128: +-884736, the widening case."""
+    log(f"case: -128 extremes, kernel={kernel}")
+    cols = 6912
+    w = np.stack([-np.ones(cols, np.int8), np.ones(cols, np.int8), np.zeros(cols, np.int8),
+                  synth.trits(1, 1, cols)[0]])
+    cases = [synth.TernaryCase("ext", w, np.full(cols, -128, np.int8), 1.0, 1.0),
+             synth.TernaryCase("ext127", w, np.full(cols, 127, np.int8), 0.5, 2.0),
+             synth.TernaryCase("mix", w, synth.u64(9, cols).astype(np.uint8).view(np.int8), 0.01, 1.5)]
+    ups = run_grouped(cases, dev, kernel)
+    assert ups[0].oi.cpu().numpy()[:3].tolist() == [884736, -884736, 0]
+    for u in ups:
+        check_case(u, oracle_ref(u.case), u.case.name)
+
+
+def test_kernels_agree_and_runs_are_deterministic(dev):
+    log("case: bit-serial == byte-lane, repeated runs identical")
+    cases = synth.layer_cases(1111, 0)
+    a = [u.oi.cpu().numpy().copy() for u in run_grouped(cases, dev, bpw.KERNEL_BITSERIAL)]
+    b = [u.oi.cpu().numpy().copy() for u in run_grouped(cases, dev, bpw.KERNEL_BYTELANE)]
+    c = [u.oi.cpu().numpy().copy() for u in run_grouped(cases, dev, bpw.KERNEL_AUTO)]
+    for x, y, z in zip(a, b, c):
+        assert np.array_equal(x, y) and np.array_equal(x, z)
+
+
+def test_plan_reads_current_activation_contents(dev):
+    log("case: plan reuse with new activations")
+    cases = synth.layer_cases(1212, 0)[:3]
+    ups = [Uploaded(c, dev) for c in cases]
+    jobs = [u.job() for u in ups]
+    ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+    plan = bpw.GemvPlan(jobs, ws)
+    for rep in range(3):
+        for u in ups:
+            x, xs = synth.activation(5000 + rep, u.case.cols)
+            u.case.x, u.case.x_scale = x, xs
+            u.x[: u.case.cols] = torch.from_numpy(x).to(dev)
+        # x_scale lives in the plan's table: keep the scale of the plan, check the integers
+        plan.run()
+        torch.cuda.synchronize()
+        for u in ups:
+            acc = oracle.gemv(oracle.pack(u.case.w), u.case.rows, u.case.cols, u.case.x, nthreads=NT)[0]
+            assert np.array_equal(u.oi.cpu().numpy(), acc)
+    plan.free()
+
+
+# ----------------------------------------------------------------------------- errors from the host
+
+
+def test_argument_errors_on_gpu(dev):
+    log("case: argument errors")
+    case = synth.ternary_case(1313, 0, 0, 64, 256)
+    u = Uploaded(case, dev)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    short = torch.zeros(200, dtype=torch.int8, device=dev)
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_gemv([bpw.gemv_job(u.m, short, 1.0, u.oi)], ws)
+    assert ei.value.status == _lib.E_INVAL
+    big = torch.zeros(1024, dtype=torch.int8, device=dev)
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_gemv([bpw.gemv_job(u.m, big[1:257], 1.0, u.oi)], ws)
+    assert ei.value.status == _lib.E_INVAL  # misaligned activation
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_gemv([u.job()], ws[:16])
+    assert ei.value.status == _lib.E_SIZE
+    forged = bpw.DevMat(_lib.BpwDevMat.from_buffer_copy(u.m.desc), u.buf)
+    forged.desc.rows = 65
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_gemv([bpw.gemv_job(forged, u.x, 1.0, u.oi)], ws)
+    assert ei.value.status == _lib.E_NOT_VALIDATED
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_gemv([u.job()], ws, kernel=9)
+    assert ei.value.status == _lib.E_UNSUPPORTED
+    os.environ["BPW_FORCE_ARCH_MISMATCH"] = "1"
+    try:
+        with pytest.raises(bpw.BpwError) as ei:
+            bpw.bpw_gemv([u.job()], ws)
+        assert ei.value.status == _lib.E_ARCH
+    finally:
+        del os.environ["BPW_FORCE_ARCH_MISMATCH"]
+    bpw.bpw_gemv([u.job()], ws)  # and the same call succeeds again
+    torch.cuda.synchronize()
+    check_case(u, oracle_ref(case), "after errors")
+
+
+def test_probe_and_flush_run(dev):
+    log("case: probe and flush")
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    bpw.bpw_stream_read_probe(buf, sink)
+    bpw.bpw_cache_flush(buf)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    assert int(buf.sum().item()) == 0
