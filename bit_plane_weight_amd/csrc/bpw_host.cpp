@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 #include <emmintrin.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <chrono>
@@ -237,21 +238,30 @@ struct Geometry {
     int32_t glog, kblk, nchunk, tile_rows;
 };
 
-// Lanes per row G = 2^glog and blocks per lane K: the smallest power-of-two G with
-// ceil(bpr / G) <= kKMax, capped at a full wave; wider rows take several passes.
-Geometry geometry_for(int64_t bpr) {
+// Lanes per row G = 2^glog and beats per lane K.
+// Tiled (byte-lane) kernel: the smallest power-of-two G with ceil(bpr / G) <= kKMax, capped at a
+// full wave; wider rows take passes of G * kKMax blocks.
+// Persistent (bit-serial) kernel: the same rule with K <= kKMaxPersistent for rows of up to
+// kXPassBlocks blocks (one LDS pass); wider rows take passes of kXPassBlocks = 32 lanes x 8 beats.
+Geometry geometry_for(int64_t bpr, bool persistent) {
     Geometry g{0, 0, 0, 0};
     if (bpr == 0) {
         g.tile_rows = bpw::kWaves * bpw::kIters * 64;
         return g;
     }
+    const int kmax = persistent ? bpw::kKMaxPersistent : bpw::kKMax;
     int glog = 0;
-    while (glog < 6 && ((bpr + (1 << glog) - 1) >> glog) > bpw::kKMax) ++glog;
-    const int64_t G = (int64_t)1 << glog;
+    while (glog < 6 && ((bpr + (1 << glog) - 1) >> glog) > kmax) ++glog;
+    int64_t G = (int64_t)1 << glog;
     int64_t k = (bpr + G - 1) / G;
     int64_t nchunk = 1;
-    if (k > bpw::kKMax) {
-        k = bpw::kKMax;
+    if (persistent && bpr > bpw::kXPassBlocks) {
+        glog = 5;
+        G = 32;
+        k = bpw::kXPassBlocks / G;
+        nchunk = (bpr + bpw::kXPassBlocks - 1) / bpw::kXPassBlocks;
+    } else if (k > kmax) {
+        k = kmax;
         nchunk = (bpr + G * k - 1) / (G * k);
     }
     g.glog = glog;
@@ -261,34 +271,106 @@ Geometry geometry_for(int64_t bpr) {
     return g;
 }
 
+// The persistent kernel's workgroup count is bounded so workspace sizes do not depend on the device.
+constexpr int32_t kMaxPersistentWG = 8192;
+
 struct Layout {
-    size_t jobs_off, tiles_off, stage_off, xplanes_off, total;
-    int64_t n_tiles, n_stage;
+    size_t jobs_off, work_off, wg_off, stage_off, xplanes_off, total;
+    int64_t n_work, n_stage;  // tiles (byte-lane) or segment capacity (bit-serial); stage items
     std::vector<size_t> xplane_offs;
 };
 
-Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool stage) {
+// Row-groups of one job for the persistent kernel: 64/G rows each (64 rows when cols == 0).
+inline int64_t units_of(int64_t rows, const Geometry &g) {
+    const int64_t rpi = 64 >> g.glog;
+    return (rows + rpi - 1) / rpi;
+}
+
+Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial) {
     Layout L{};
     L.jobs_off = 0;
     int64_t tiles = 0, stage_items = 0;
     for (int32_t i = 0; i < n; ++i) {
-        const Geometry g = geometry_for(jobs[i].m.bpr);
+        const Geometry g = geometry_for(jobs[i].m.bpr, false);
         tiles += (jobs[i].m.rows + g.tile_rows - 1) / g.tile_rows;
-        if (stage) stage_items += jobs[i].m.bpr;
+        if (bitserial) stage_items += jobs[i].m.bpr;
     }
-    L.n_tiles = tiles;
+    // segments: one per (workgroup, job) overlap, plus one per kSegRows rows of each job
+    int64_t seg_cap = (int64_t)n + kMaxPersistentWG;
+    for (int32_t i = 0; i < n; ++i) seg_cap += jobs[i].m.rows / bpw::kSegRows + 1;
+    L.n_work = bitserial ? seg_cap : tiles;
     L.n_stage = stage_items;
-    L.tiles_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
-    L.stage_off = align_up(L.tiles_off + sizeof(bpw::DevTile) * (size_t)tiles);
+    L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
+    const size_t work_bytes =
+        bitserial ? sizeof(bpw::Segment) * (size_t)L.n_work : sizeof(bpw::DevTile) * (size_t)tiles;
+    L.wg_off = align_up(L.work_off + work_bytes);
+    L.stage_off = align_up(L.wg_off + (bitserial ? sizeof(int32_t) * (size_t)(kMaxPersistentWG + 1) : 0));
     L.xplanes_off = align_up(L.stage_off + sizeof(bpw::StageItem) * (size_t)stage_items);
     size_t off = L.xplanes_off;
     L.xplane_offs.resize((size_t)n);
     for (int32_t i = 0; i < n; ++i) {
         L.xplane_offs[(size_t)i] = off;
-        if (stage) off = align_up(off + (size_t)jobs[i].m.bpr * 64);
+        if (bitserial) off = align_up(off + (size_t)jobs[i].m.bpr * 64);
     }
     L.total = off;
     return L;
+}
+
+// Split all jobs' row-groups over `nwg` workgroups so each streams about the same number of plane
+// bytes: workgroup w owns the row-groups whose first byte falls in [w * total / nwg,
+// (w+1) * total / nwg). Jobs with no columns (nothing to stream) go to workgroup 0.
+bool partition_units(const bpw_gemv_job *jobs, int32_t n, int64_t nwg, std::vector<bpw::Segment> &segs,
+                     std::vector<int32_t> &wg_seg) {
+    segs.clear();
+    wg_seg.assign((size_t)nwg + 1, 0);
+    int64_t total = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const Geometry g = geometry_for(jobs[i].m.bpr, true);
+        const int64_t U = units_of(jobs[i].m.rows, g);
+        if (jobs[i].m.bpr == 0) {
+            if (U > 0) segs.push_back(bpw::Segment{i, 0, (int32_t)U, 0});
+            continue;
+        }
+        total += U * (int64_t)(64 >> g.glog) * jobs[i].m.bpr * 16;
+    }
+    int64_t w = 0, base = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (jobs[i].m.bpr == 0) continue;
+        const Geometry g = geometry_for(jobs[i].m.bpr, true);
+        const int64_t U = units_of(jobs[i].m.rows, g);
+        const int64_t ub = (int64_t)(64 >> g.glog) * jobs[i].m.bpr * 16;
+        int64_t u = 0;
+        while (u < U) {
+            const int64_t end_byte = (w + 1 >= nwg) ? total : (total * (w + 1)) / nwg;
+            int64_t uend = end_byte <= base ? u : std::min(U, (end_byte - base + ub - 1) / ub);
+            if (uend < u) uend = u;
+            // a segment holds at most kSegRows rows (the kernel keeps its sums in LDS)
+            const int64_t max_units = bpw::kSegRows / (64 >> g.glog);
+            while (uend > u) {
+                const int64_t e = std::min(uend, u + max_units);
+                segs.push_back(bpw::Segment{i, (int32_t)u, (int32_t)e, 0});
+                u = e;
+            }
+            if (u < U) {
+                ++w;
+                wg_seg[(size_t)w] = (int32_t)segs.size();
+            }
+        }
+        base += U * ub;
+    }
+    while (w < nwg) {
+        ++w;
+        wg_seg[(size_t)w] = (int32_t)segs.size();
+    }
+    // every job's row-groups are covered exactly once, in order
+    std::vector<int64_t> next((size_t)n, 0);
+    for (const auto &sg : segs) {
+        if (sg.u0 != next[(size_t)sg.job] || sg.u1 <= sg.u0) return false;
+        next[(size_t)sg.job] = sg.u1;
+    }
+    for (int32_t i = 0; i < n; ++i)
+        if (next[(size_t)i] != units_of(jobs[i].m.rows, geometry_for(jobs[i].m.bpr, true))) return false;
+    return wg_seg[(size_t)nwg] == (int32_t)segs.size();
 }
 
 bpw_status check_dev_mat(const bpw_dev_mat *m, const char *who) {
@@ -305,7 +387,7 @@ bpw_status check_job(const bpw_gemv_job &j, int32_t i) {
     bpw_status st = check_dev_mat(&j.m, who);
     if (st) return st;
     const uint64_t bytes = (uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u;
-    const Geometry g = geometry_for(j.m.bpr);
+    const Geometry g = geometry_for(j.m.bpr, false);
     if ((uint64_t)(j.m.rows + g.tile_rows) * (uint64_t)j.m.bpr * 16u >= 0xFFFFFFF0ull)
         return fail(BPW_E_UNSUPPORTED, "%s: %llu plane bytes exceed the 32-bit offsets of one matrix", who,
                     (unsigned long long)bytes);
@@ -325,9 +407,13 @@ struct bpw_gemv_plan {
     int device;
     int32_t kernel;
     const bpw::DevJob *jobs;
-    const bpw::DevTile *tiles;
+    const bpw::DevTile *tiles;     // byte-lane
+    const bpw::Segment *segs;      // bit-serial
+    const int32_t *wave_seg;       // bit-serial: per-wave segment offsets
     const bpw::StageItem *stage;
     int64_t n_tiles, n_stage;
+    int32_t n_wg;                  // bit-serial persistent workgroups
+    int32_t has_work;
 };
 
 // ---------------------------------------------------------------- ABI
@@ -471,7 +557,7 @@ bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *st
 
 size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs) {
     if (!jobs || n_jobs <= 0) return 0;
-    return layout_for(jobs, n_jobs, true).total;
+    return layout_for(jobs, n_jobs, true).total;  // the bit-serial layout is the larger one
 }
 
 bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
@@ -481,17 +567,16 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad job list");
     if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_BYTELANE)
         return fail(BPW_E_UNSUPPORTED, "unknown kernel %d", (int)kernel);
-    const int variant = (kernel == BPW_KERNEL_BYTELANE) ? 2 : 1;
+    const bool bitserial = (kernel != BPW_KERNEL_BYTELANE);
     for (int32_t i = 0; i < n_jobs; ++i) {
         bpw_status st = check_job(jobs[i], i);
         if (st) return st;
     }
-    const bool stage = (variant == 1);
-    Layout L = layout_for(jobs, n_jobs, stage);
-    if (L.n_tiles > (int64_t)INT32_MAX || L.n_stage > (int64_t)INT32_MAX)
+    Layout L = layout_for(jobs, n_jobs, bitserial);
+    if (L.n_work > (int64_t)INT32_MAX || L.n_stage > (int64_t)INT32_MAX)
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
-    if (n_jobs > 0 && L.total > ws_len)
-        return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, L.total);
+    if (n_jobs > 0 && bpw_gemv_workspace_bytes(jobs, n_jobs) > ws_len)
+        return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, bpw_gemv_workspace_bytes(jobs, n_jobs));
     if (n_jobs > 0 && !d_ws) return fail(BPW_E_INVAL, "d_ws is NULL");
     if (((uintptr_t)d_ws & (kAlign - 1)) != 0) return fail(BPW_E_INVAL, "d_ws must be 256-byte aligned");
     bpw_status st = check_device();
@@ -499,16 +584,30 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     int dev = 0;
     (void)hipGetDevice(&dev);
 
+    int32_t n_wg = 0;
+    std::vector<bpw::Segment> segs;
+    std::vector<int32_t> wave_seg;
+    if (bitserial && n_jobs > 0) {
+        n_wg = std::min(bpw::persistent_workgroups(), kMaxPersistentWG);
+        if (n_wg <= 0) return fail(BPW_E_HIP, "could not size the persistent grid (occupancy query failed)");
+        if (!partition_units(jobs, n_jobs, n_wg, segs, wave_seg) || (int64_t)segs.size() > L.n_work)
+            return fail(BPW_E_UNSUPPORTED, "internal: row-group partition failed (%zu segments)", segs.size());
+    }
+
     auto *plan = new (std::nothrow) bpw_gemv_plan;
     if (!plan) return fail(BPW_E_INVAL, "out of host memory");
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     plan->device = dev;
     plan->kernel = kernel;
     plan->jobs = reinterpret_cast<const bpw::DevJob *>(ws + L.jobs_off);
-    plan->tiles = reinterpret_cast<const bpw::DevTile *>(ws + L.tiles_off);
+    plan->tiles = reinterpret_cast<const bpw::DevTile *>(ws + L.work_off);
+    plan->segs = reinterpret_cast<const bpw::Segment *>(ws + L.work_off);
+    plan->wave_seg = reinterpret_cast<const int32_t *>(ws + L.wg_off);
     plan->stage = reinterpret_cast<const bpw::StageItem *>(ws + L.stage_off);
-    plan->n_tiles = L.n_tiles;
+    plan->n_tiles = bitserial ? 0 : L.n_work;
     plan->n_stage = L.n_stage;
+    plan->n_wg = n_wg;
+    plan->has_work = 0;
     if (n_jobs == 0) {
         *out = plan;
         return BPW_OK;
@@ -517,16 +616,16 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     const size_t table_bytes = L.xplanes_off;
     std::vector<uint8_t> host(table_bytes, 0);
     auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
-    auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.tiles_off);
+    auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
     auto *hs = reinterpret_cast<bpw::StageItem *>(host.data() + L.stage_off);
     int64_t t = 0, si = 0;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const bpw_gemv_job &j = jobs[i];
-        const Geometry g = geometry_for(j.m.bpr);
+        const Geometry g = geometry_for(j.m.bpr, bitserial);
         bpw::DevJob d{};
         d.planes = static_cast<const uint8_t *>(j.m.d_planes);
         d.x = j.d_x;
-        d.xplanes = stage ? reinterpret_cast<uint32_t *>(ws + L.xplane_offs[(size_t)i]) : nullptr;
+        d.xplanes = bitserial ? reinterpret_cast<uint32_t *>(ws + L.xplane_offs[(size_t)i]) : nullptr;
         d.out_i32 = j.d_out_i32;
         d.out_f32 = j.d_out_f32;
         d.rows = (int32_t)j.m.rows;
@@ -537,10 +636,17 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         d.kblk = g.kblk;
         d.nchunk = g.nchunk;
         d.tile_rows = g.tile_rows;
+        d.plane_bytes = (uint32_t)((uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u);
         hj[i] = d;
-        for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
-        if (stage)
+        if (!bitserial)
+            for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
+        if (bitserial)
             for (int64_t b = 0; b < j.m.bpr; ++b) hs[si++] = bpw::StageItem{i, (int32_t)b};
+        if (j.m.rows > 0) plan->has_work = 1;
+    }
+    if (bitserial) {
+        std::memcpy(host.data() + L.work_off, segs.data(), segs.size() * sizeof(bpw::Segment));
+        std::memcpy(host.data() + L.wg_off, wave_seg.data(), wave_seg.size() * sizeof(int32_t));
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
@@ -564,7 +670,7 @@ static bpw_status plan_ready(const bpw_gemv_plan *plan) {
 bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream) {
     bpw_status st = plan_ready(plan);
     if (st) return st;
-    if (plan->kernel == BPW_KERNEL_BYTELANE || plan->n_stage == 0) return BPW_OK;
+    if (plan->kernel == BPW_KERNEL_BYTELANE || plan->n_stage == 0 || !plan->has_work) return BPW_OK;
     return hip_status(bpw::launch_stage_xplanes(plan->jobs, plan->stage, (int32_t)plan->n_stage, stream),
                       "stage launch");
 }
@@ -572,9 +678,11 @@ bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream) {
 bpw_status bpw_gemv_plan_run_main(const bpw_gemv_plan *plan, void *stream) {
     bpw_status st = plan_ready(plan);
     if (st) return st;
-    if (plan->n_tiles == 0) return BPW_OK;
-    const int variant = (plan->kernel == BPW_KERNEL_BYTELANE) ? 2 : 1;
-    return hip_status(bpw::launch_gemv(variant, plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
+    if (!plan->has_work) return BPW_OK;
+    if (plan->kernel == BPW_KERNEL_BYTELANE)
+        return hip_status(bpw::launch_gemv_tiles(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
+                          "gemv launch");
+    return hip_status(bpw::launch_gemv_persistent(plan->jobs, plan->segs, plan->wave_seg, plan->n_wg, stream),
                       "gemv launch");
 }
 
@@ -622,7 +730,7 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
     if (need > 160u * 1024u)
         return fail(BPW_E_UNSUPPORTED, "batch * bpr * 64 = %zu bytes of activation planes exceed the 160 KiB LDS",
                     need);
-    const Geometry g = geometry_for(m->bpr);
+    const Geometry g = geometry_for(m->bpr, false);
     if ((uint64_t)(m->rows + g.tile_rows) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
         return fail(BPW_E_UNSUPPORTED, "plane bytes exceed the 32-bit offsets of one matrix");
     st = check_device();

@@ -10,7 +10,10 @@ namespace bpw {
 // Launch geometry of the ternary GEMV kernels.
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // wave64
-constexpr int kKMax = 7;                  // 64-column blocks one lane keeps in registers per pass
+constexpr int kKMax = 7;                  // 64-column blocks one lane handles per pass (tiled byte-lane kernel)
+constexpr int kKMaxPersistent = 8;        // beats one lane holds per row-group (persistent bit-serial kernel)
+constexpr int kXPassBlocks = 256;         // activation-plane blocks held in LDS per pass (16 KiB)
+constexpr int kSegRows = 1024;            // rows of one persistent-kernel segment (its sums sit in LDS)
 constexpr int kIters = 4;                 // row-iterations per wave per tile
 
 // One GEMV of a grouped launch, as the kernels read it (lives in the caller's workspace).
@@ -27,7 +30,18 @@ struct DevJob {
     int32_t glog;           // log2 of lanes per row (G)
     int32_t kblk;           // blocks per lane per pass (<= kKMax; 0 when cols == 0)
     int32_t nchunk;         // passes over the row: bpr <= G * kblk * nchunk
-    int32_t tile_rows;      // rows per workgroup tile = kWaves * kIters * (64 / G)
+    int32_t tile_rows;      // rows per workgroup tile = kWaves * kIters * (64 / G) (tiled kernels)
+    uint32_t plane_bytes;   // rows * bpr * 16 (the buffer range of the weight loads)
+    int32_t pad;
+};
+
+// A run of consecutive row-groups ("units" of 64 / G rows) of one job, owned by one workgroup of
+// the persistent bit-serial kernel. Units [u0, u1).
+struct Segment {
+    int32_t job;
+    int32_t u0;
+    int32_t u1;
+    int32_t pad;
 };
 
 struct DevTile {
@@ -54,7 +68,12 @@ struct SmallBatchArgs {
 
 // Kernel launchers (bpw_kernels.hip). Each returns the hipError_t of its launch as int.
 int launch_stage_xplanes(const DevJob *jobs, const StageItem *items, int32_t n_items, void *stream);
-int launch_gemv(int variant, const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);
+int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
+int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
+                           void *stream);  // bit-serial
+// Workgroups of the persistent bit-serial kernel that are resident at once on the current device
+// (CUs x occupancy); 0 on error.
+int32_t persistent_workgroups();
 int launch_stage_batch(const int8_t *X, int64_t ldx, uint32_t *xplanes, int32_t bpr, int32_t batch, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);

@@ -103,107 +103,166 @@ __global__ __launch_bounds__(kThreads) void stage_batch_kernel(const int8_t *__r
 }
 
 // ------------------------------------------------------------------------------------------
-// Batch-1 GEMV, bit-serial select. Workgroup = one tile of tile_rows consecutive rows of one job.
-// A row is served by G = 2^glog consecutive lanes; lane g of the group reads beats g, g+G, ...
-// (so each wave load covers G*16 contiguous bytes of 64/G rows) and keeps the activation planes
-// of its K blocks in registers for the whole tile.
+// Batch-1 GEMV, bit-serial select, persistent. The grid is the set of workgroups the device holds
+// at once; each workgroup walks its own list of segments (runs of consecutive row-groups of one job)
+// that the host balanced by plane bytes. Per segment the workgroup copies the job's activation
+// planes into LDS, then its four waves take row-groups in turn. A row is served by G = 2^glog
+// consecutive lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes
+// of each of 64/G rows), holding only those K beats in registers, so many waves fit per SIMD and
+// keep loads in flight. Loads past the matrix use an offset that the buffer range check answers
+// with zeros, which also covers the partial last row-group.
+//
+// LDS layout of the planes: block b's four 16-byte quarters are rotated by (b >> 1) & 3, so the G
+// blocks one wave reads at a time spread over all 32 banks instead of piling onto two groups.
 
+__device__ __forceinline__ int xq_slot(int b, int i) { return b * 4 + ((i + (b >> 1)) & 3); }
+
+// Beats b = bbase + k*G of one row (zeros past bpr or past the matrix).
 template <int K>
-__device__ __forceinline__ void gemv_bitserial_tile(const DevJob &J, int row0, int lane, int wave) {
-    const int glog = J.glog;
+__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, int bbase, int G,
+                                          int bpr) {
+    const uint32_t rowoff = row * (uint32_t)bpr;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int b = bbase + k * G;
+        const uint32_t off = (b < bpr) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
+        B[k] = load_beat(wr, off);
+    }
+}
+
+// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
+//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
+// Blocks past the pass (b >= nb) hold zero beats and contribute nothing; their LDS reads are clamped
+// to block 0 so they stay inside the copy.
+template <int K>
+__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G, int nb) {
+    const int b = (g + k * G) < nb ? g + k * G : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 w = xl[xq_slot(b, i)];
+        X[4 * i + 0] = w.x;
+        X[4 * i + 1] = w.y;
+        X[4 * i + 2] = w.z;
+        X[4 * i + 3] = w.w;
+    }
+}
+
+// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
+//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
+// Blocks past the pass (b >= nb) hold zero beats and contribute nothing; their LDS reads are clamped
+// to block 0 so they stay inside the copy. The planes of beat k+1 are read while beat k is reduced;
+// scheduling barriers keep the compiler from hoisting every beat's reads (which would cost 16
+// registers per beat and the occupancy this kernel relies on).
+template <int K>
+__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G, int nb) {
+    uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t cn = 0;
+    uint32_t Xa[16], Xb[16];
+    read_planes<K>(Xa, xl, 0, g, G, nb);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
+        uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
+        if (k + 1 < K) read_planes<K>(Xn, xl, k + 1, g, G, nb);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
+            c[j] = __builtin_popcount(select_bits(X[2 * j + 1], B[k].y, B[k].w)) + c[j];
+        }
+        cn = __builtin_popcount(B[k].z) + cn;
+        cn = __builtin_popcount(B[k].w) + cn;
+        // beat k is finished here: its counts must exist before any later LDS read is issued
+        asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
+                     "+v"(c[7]), "+v"(cn)::"memory");
+    }
+    int32_t acc = (int32_t)cn;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
+    acc -= (int32_t)(c[7] << 7);
+    return acc;
+}
+
+// Copy planes of blocks [b0, b0 + nb) into LDS (swizzled), all threads of the workgroup.
+__device__ __forceinline__ void stage_pass(u32x4 *xl, const uint32_t *xplanes, int b0, int nb) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(xplanes) + (int64_t)b0 * 4;
+    for (int t = threadIdx.x; t < nb * 4; t += kThreads) xl[xq_slot(t >> 2, t & 3)] = src[t];
+}
+
+// Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced
+// pass at the end: a vector store inside the streaming loop would share the vector-memory counter
+// with the weight loads and make every wait in the loop a wait for all loads in flight.
+template <int K, int GLOG>
+__device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
+                                           int32_t *sums) {
+    const int glog = GLOG >= 0 ? GLOG : J.glog;
     const int G = 1 << glog;
     const int g = lane & (G - 1);
     const int q = lane >> glog;
     const int rpi = 64 >> glog;
     const int bpr = J.bpr;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, (uint32_t)((uint64_t)J.rows * bpr * 16));
-    const u32x4 *__restrict__ xp = reinterpret_cast<const u32x4 *>(J.xplanes);
-
+    const int pass_blocks = K * G;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, J.plane_bytes);
     for (int ch = 0; ch < J.nchunk; ++ch) {
-        const int bbase = ch * K * G + g;
-        uint32_t X[K][16];
-#pragma unroll
-        for (int k = 0; k < K; ++k) {
-            const int b = bbase + k * G;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (b < bpr) v = xp[b * 4 + i];
-                X[k][4 * i + 0] = v.x;
-                X[k][4 * i + 1] = v.y;
-                X[k][4 * i + 2] = v.z;
-                X[k][4 * i + 3] = v.w;
+        const int b0 = ch * pass_blocks;
+        const int nb = min(pass_blocks, bpr - b0);
+        __syncthreads();  // every wave is done with the previous planes and sums
+        stage_pass(xl, J.xplanes, b0, nb);
+        __syncthreads();
+        for (int u = u0 + wave; u < u1; u += kWaves) {
+            const uint32_t row = (uint32_t)(u * rpi + q);
+            u32x4 B[K];
+            issue_row<K>(B, wr, row, b0 + g, G, bpr);
+            asm volatile("" ::: "memory");  // all K weight loads leave before the first LDS read
+            const int32_t tot = group_sum(row_partial<K>(xl, B, g, G, nb), glog);
+            if (g == 0) {
+                const int i = (u - u0) * rpi + q;
+                sums[i] = ch == 0 ? tot : sums[i] + tot;  // the same lane owns this slot in every pass
             }
         }
-        int32_t s[kIters];
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int row = row0 + (it * kWaves + wave) * rpi + q;
-            u32x4 v[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int b = bbase + k * G;
-                const uint32_t off = (b < bpr) ? (uint32_t)(((uint32_t)row * (uint32_t)bpr + (uint32_t)b) * 16u)
-                                               : kOutOfRange;
-                v[k] = load_beat(wr, off);
-            }
-            uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-            uint32_t cn = 0;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    c[j] = __builtin_popcount(select_bits(X[k][2 * j], v[k].x, v[k].z)) + c[j];
-                    c[j] = __builtin_popcount(select_bits(X[k][2 * j + 1], v[k].y, v[k].w)) + c[j];
-                }
-                cn = __builtin_popcount(v[k].z) + cn;
-                cn = __builtin_popcount(v[k].w) + cn;
-            }
-            int32_t acc = (int32_t)cn;
-#pragma unroll
-            for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
-            acc -= (int32_t)(c[7] << 7);
-            s[it] = acc;
-        }
-        // One pass writes the row; wider rows add each pass's partial sum into out_i32 (the same
-        // lane reads back its own earlier store) and apply the scales after the last pass.
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int row = row0 + (it * kWaves + wave) * rpi + q;
-            const int32_t tot = group_sum(s[it], glog);
-            if (g == 0 && row < J.rows) {
-                if (J.nchunk == 1) {
-                    write_row(J, row, tot);
-                } else {
-                    const int32_t prev = (ch == 0) ? 0 : J.out_i32[row];
-                    if (ch + 1 < J.nchunk)
-                        J.out_i32[row] = prev + tot;
-                    else
-                        write_row(J, row, prev + tot);
-                }
-            }
-        }
+    }
+    __syncthreads();
+    const int row0 = u0 * rpi, n = (u1 - u0) * rpi;
+    for (int i = threadIdx.x; i < n; i += kThreads)
+        if (row0 + i < J.rows) write_row(J, row0 + i, sums[i]);
+}
+
+// cols == 0: every row is the empty sum (row-groups of 64 rows).
+__device__ __forceinline__ void bs_segment_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
+    for (int u = u0 + wave; u < u1; u += kWaves) {
+        const int row = u * 64 + lane;
+        if (row < J.rows) write_row(J, row, 0);
     }
 }
 
 __global__ __launch_bounds__(kThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
-                                                                  const DevTile *__restrict__ tiles) {
-    const DevTile tile = tiles[blockIdx.x];
-    const DevJob J = jobs[tile.job];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    switch (J.kblk) {
-        case 1: gemv_bitserial_tile<1>(J, tile.row0, lane, wave); break;
-        case 2: gemv_bitserial_tile<2>(J, tile.row0, lane, wave); break;
-        case 3: gemv_bitserial_tile<3>(J, tile.row0, lane, wave); break;
-        case 4: gemv_bitserial_tile<4>(J, tile.row0, lane, wave); break;
-        case 5: gemv_bitserial_tile<5>(J, tile.row0, lane, wave); break;
-        case 6: gemv_bitserial_tile<6>(J, tile.row0, lane, wave); break;
-        case 7: gemv_bitserial_tile<7>(J, tile.row0, lane, wave); break;
-        default: {  // cols == 0: every row is the empty sum
-            for (int it = 0; it < kIters; ++it) {
-                const int row = tile.row0 + (it * kWaves + wave) * 64 + lane;
-                if (row < J.rows) write_row(J, row, 0);
-            }
+                                                                  const Segment *__restrict__ segs,
+                                                                  const int32_t *__restrict__ wg_seg) {
+    __shared__ u32x4 xl[kXPassBlocks * 4];
+    __shared__ int32_t sums[kSegRows];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s0 = wg_seg[blockIdx.x], s1 = wg_seg[blockIdx.x + 1];
+    for (int si = s0; si < s1; ++si) {
+        const Segment sg = segs[si];
+        const DevJob J = jobs[sg.job];
+        if (J.kblk == 5 && J.glog == 3) {  // 2560-column rows: 8 lanes x 5 beats
+            bs_segment<5, 3>(J, sg.u0, sg.u1, wave, lane, xl, sums);
+            continue;
+        }
+        if (J.kblk == 7 && J.glog == 4) {  // 6912-column rows: 16 lanes x 7 beats (108 of 112 used)
+            bs_segment<7, 4>(J, sg.u0, sg.u1, wave, lane, xl, sums);
+            continue;
+        }
+        switch (J.kblk) {
+            case 0: bs_segment_empty(J, sg.u0, sg.u1, wave, lane); break;
+            case 1: bs_segment<1, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 2: bs_segment<2, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 3: bs_segment<3, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 4: bs_segment<4, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 5: bs_segment<5, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 6: bs_segment<6, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 7: bs_segment<7, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            default: bs_segment<8, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
         }
     }
 }
@@ -523,14 +582,29 @@ int launch_stage_xplanes(const DevJob *jobs, const StageItem *items, int32_t n_i
     return hipGetLastError();
 }
 
-int launch_gemv(int variant, const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream) {
+int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream) {
     if (n_tiles <= 0) return hipSuccess;
-    if (variant == 2)
-        hipLaunchKernelGGL(gemv_bytelane_kernel, dim3((unsigned)n_tiles), dim3(kThreads), 0, as_stream(stream), jobs,
-                           tiles);
-    else
-        hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_tiles), dim3(kThreads), 0, as_stream(stream),
-                           jobs, tiles);
+    hipLaunchKernelGGL(gemv_bytelane_kernel, dim3((unsigned)n_tiles), dim3(kThreads), 0, as_stream(stream), jobs,
+                       tiles);
+    return hipGetLastError();
+}
+
+int32_t persistent_workgroups() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_bitserial_kernel),
+                                                     kThreads, 0) != hipSuccess)
+        return 0;
+    if (cus <= 0 || per_cu <= 0) return 0;
+    return cus * per_cu;
+}
+
+int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
+                           void *stream) {
+    if (n_wg <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_wg), dim3(kThreads), 0, as_stream(stream), jobs, segs,
+                       wg_seg);
     return hipGetLastError();
 }
 

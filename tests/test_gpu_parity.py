@@ -287,7 +287,7 @@ def test_argument_errors_on_gpu(dev):
     log("case: argument errors")
     case = synth.ternary_case(1313, 0, 0, 64, 256)
     u = Uploaded(case, dev)
-    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    ws = torch.empty(bpw.bpw_gemv_workspace_bytes([u.job()]), dtype=torch.uint8, device=dev)
     short = torch.zeros(200, dtype=torch.int8, device=dev)
     with pytest.raises(bpw.BpwError) as ei:
         bpw.bpw_gemv([bpw.gemv_job(u.m, short, 1.0, u.oi)], ws)
