@@ -182,7 +182,7 @@ def bpw_gemv(jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None) -> None:
 
 
 class GemvPlan:
-    """bpw_gemv_plan: the job table written once into d_ws; run() queues the launches."""
+    """bpw_gemv_plan: the job table written once into d_ws; run() queues the one launch."""
 
     def __init__(self, jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None):
         arr, n = _jobs_array(jobs)
@@ -194,12 +194,6 @@ class GemvPlan:
 
     def run(self, stream=None) -> None:
         _lib.check(_lib.lib().bpw_gemv_plan_run(self._h, _stream(stream)))
-
-    def run_stage(self, stream=None) -> None:
-        _lib.check(_lib.lib().bpw_gemv_plan_run_stage(self._h, _stream(stream)))
-
-    def run_main(self, stream=None) -> None:
-        _lib.check(_lib.lib().bpw_gemv_plan_run_main(self._h, _stream(stream)))
 
     def free(self) -> None:
         if self._h:

@@ -76,8 +76,6 @@ def lib():
         "bpw_gemv": (i32, [J, i32, i32, vp, sz, vp]),
         "bpw_gemv_plan_create": (i32, [J, i32, i32, vp, sz, vp, ctypes.POINTER(vp)]),
         "bpw_gemv_plan_run": (i32, [vp, vp]),
-        "bpw_gemv_plan_run_stage": (i32, [vp, vp]),
-        "bpw_gemv_plan_run_main": (i32, [vp, vp]),
         "bpw_gemv_plan_free": (None, [vp]),
         "bpw_gemm_small_batch_workspace_bytes": (sz, [M, i32]),
         "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp, sz, vp]),

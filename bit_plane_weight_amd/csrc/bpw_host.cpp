@@ -241,12 +241,21 @@ struct Geometry {
 // Lanes per row G = 2^glog and beats per lane K.
 // Tiled (byte-lane) kernel: the smallest power-of-two G with ceil(bpr / G) <= kKMax, capped at a
 // full wave; wider rows take passes of G * kKMax blocks.
-// Persistent (bit-serial) kernel: the same rule with K <= kKMaxPersistent for rows of up to
-// kXPassBlocks blocks (one LDS pass); wider rows take passes of kXPassBlocks = 32 lanes x 8 beats.
+// Persistent (bit-serial) kernel: the two row widths of the model have compiled-in geometry
+// (2560 columns: 8 lanes x 5 beats; 6912 columns: 32 lanes x 4 beats). Other widths take the same
+// rule as above with K <= kKMaxPersistent for rows of up to kXPassBlocks blocks (one LDS pass);
+// wider rows take passes of kXPassBlocks = 64 lanes x kKMaxPersistent beats.
 Geometry geometry_for(int64_t bpr, bool persistent) {
     Geometry g{0, 0, 0, 0};
     if (bpr == 0) {
         g.tile_rows = bpw::kWaves * bpw::kIters * 64;
+        return g;
+    }
+    if (persistent && (bpr == 40 || bpr == 108)) {
+        g.glog = bpr == 40 ? 3 : 5;
+        g.kblk = bpr == 40 ? 5 : 4;
+        g.nchunk = 1;
+        g.tile_rows = bpw::kWaves * bpw::kIters * (int32_t)(64 >> g.glog);
         return g;
     }
     const int kmax = persistent ? bpw::kKMaxPersistent : bpw::kKMax;
@@ -256,8 +265,8 @@ Geometry geometry_for(int64_t bpr, bool persistent) {
     int64_t k = (bpr + G - 1) / G;
     int64_t nchunk = 1;
     if (persistent && bpr > bpw::kXPassBlocks) {
-        glog = 5;
-        G = 32;
+        glog = 6;
+        G = 64;
         k = bpw::kXPassBlocks / G;
         nchunk = (bpr + bpw::kXPassBlocks - 1) / bpw::kXPassBlocks;
     } else if (k > kmax) {
@@ -275,9 +284,8 @@ Geometry geometry_for(int64_t bpr, bool persistent) {
 constexpr int32_t kMaxPersistentWG = 8192;
 
 struct Layout {
-    size_t jobs_off, work_off, wg_off, stage_off, xplanes_off, total;
-    int64_t n_work, n_stage;  // tiles (byte-lane) or segment capacity (bit-serial); stage items
-    std::vector<size_t> xplane_offs;
+    size_t jobs_off, work_off, wg_off, total;
+    int64_t n_work;  // tiles (byte-lane) or segment capacity (bit-serial)
 };
 
 // Row-groups of one job for the persistent kernel: 64/G rows each (64 rows when cols == 0).
@@ -289,30 +297,20 @@ inline int64_t units_of(int64_t rows, const Geometry &g) {
 Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial) {
     Layout L{};
     L.jobs_off = 0;
-    int64_t tiles = 0, stage_items = 0;
+    int64_t tiles = 0;
     for (int32_t i = 0; i < n; ++i) {
         const Geometry g = geometry_for(jobs[i].m.bpr, false);
         tiles += (jobs[i].m.rows + g.tile_rows - 1) / g.tile_rows;
-        if (bitserial) stage_items += jobs[i].m.bpr;
     }
     // segments: one per (workgroup, job) overlap, plus one per kSegRows rows of each job
     int64_t seg_cap = (int64_t)n + kMaxPersistentWG;
     for (int32_t i = 0; i < n; ++i) seg_cap += jobs[i].m.rows / bpw::kSegRows + 1;
     L.n_work = bitserial ? seg_cap : tiles;
-    L.n_stage = stage_items;
     L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
     const size_t work_bytes =
         bitserial ? sizeof(bpw::Segment) * (size_t)L.n_work : sizeof(bpw::DevTile) * (size_t)tiles;
     L.wg_off = align_up(L.work_off + work_bytes);
-    L.stage_off = align_up(L.wg_off + (bitserial ? sizeof(int32_t) * (size_t)(kMaxPersistentWG + 1) : 0));
-    L.xplanes_off = align_up(L.stage_off + sizeof(bpw::StageItem) * (size_t)stage_items);
-    size_t off = L.xplanes_off;
-    L.xplane_offs.resize((size_t)n);
-    for (int32_t i = 0; i < n; ++i) {
-        L.xplane_offs[(size_t)i] = off;
-        if (bitserial) off = align_up(off + (size_t)jobs[i].m.bpr * 64);
-    }
-    L.total = off;
+    L.total = align_up(L.wg_off + (bitserial ? sizeof(int32_t) * (size_t)(kMaxPersistentWG + 1) : 0));
     return L;
 }
 
@@ -409,9 +407,8 @@ struct bpw_gemv_plan {
     const bpw::DevJob *jobs;
     const bpw::DevTile *tiles;     // byte-lane
     const bpw::Segment *segs;      // bit-serial
-    const int32_t *wave_seg;       // bit-serial: per-wave segment offsets
-    const bpw::StageItem *stage;
-    int64_t n_tiles, n_stage;
+    const int32_t *wg_seg;         // bit-serial: per-workgroup segment offsets
+    int64_t n_tiles;
     int32_t n_wg;                  // bit-serial persistent workgroups
     int32_t has_work;
 };
@@ -573,7 +570,7 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         if (st) return st;
     }
     Layout L = layout_for(jobs, n_jobs, bitserial);
-    if (L.n_work > (int64_t)INT32_MAX || L.n_stage > (int64_t)INT32_MAX)
+    if (L.n_work > (int64_t)INT32_MAX)
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
     if (n_jobs > 0 && bpw_gemv_workspace_bytes(jobs, n_jobs) > ws_len)
         return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, bpw_gemv_workspace_bytes(jobs, n_jobs));
@@ -586,11 +583,11 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
 
     int32_t n_wg = 0;
     std::vector<bpw::Segment> segs;
-    std::vector<int32_t> wave_seg;
+    std::vector<int32_t> wg_seg;
     if (bitserial && n_jobs > 0) {
         n_wg = std::min(bpw::persistent_workgroups(), kMaxPersistentWG);
         if (n_wg <= 0) return fail(BPW_E_HIP, "could not size the persistent grid (occupancy query failed)");
-        if (!partition_units(jobs, n_jobs, n_wg, segs, wave_seg) || (int64_t)segs.size() > L.n_work)
+        if (!partition_units(jobs, n_jobs, n_wg, segs, wg_seg) || (int64_t)segs.size() > L.n_work)
             return fail(BPW_E_UNSUPPORTED, "internal: row-group partition failed (%zu segments)", segs.size());
     }
 
@@ -602,10 +599,8 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     plan->jobs = reinterpret_cast<const bpw::DevJob *>(ws + L.jobs_off);
     plan->tiles = reinterpret_cast<const bpw::DevTile *>(ws + L.work_off);
     plan->segs = reinterpret_cast<const bpw::Segment *>(ws + L.work_off);
-    plan->wave_seg = reinterpret_cast<const int32_t *>(ws + L.wg_off);
-    plan->stage = reinterpret_cast<const bpw::StageItem *>(ws + L.stage_off);
+    plan->wg_seg = reinterpret_cast<const int32_t *>(ws + L.wg_off);
     plan->n_tiles = bitserial ? 0 : L.n_work;
-    plan->n_stage = L.n_stage;
     plan->n_wg = n_wg;
     plan->has_work = 0;
     if (n_jobs == 0) {
@@ -613,19 +608,17 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         return BPW_OK;
     }
 
-    const size_t table_bytes = L.xplanes_off;
+    const size_t table_bytes = L.total;
     std::vector<uint8_t> host(table_bytes, 0);
     auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
     auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
-    auto *hs = reinterpret_cast<bpw::StageItem *>(host.data() + L.stage_off);
-    int64_t t = 0, si = 0;
+    int64_t t = 0;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const bpw_gemv_job &j = jobs[i];
         const Geometry g = geometry_for(j.m.bpr, bitserial);
         bpw::DevJob d{};
         d.planes = static_cast<const uint8_t *>(j.m.d_planes);
         d.x = j.d_x;
-        d.xplanes = bitserial ? reinterpret_cast<uint32_t *>(ws + L.xplane_offs[(size_t)i]) : nullptr;
         d.out_i32 = j.d_out_i32;
         d.out_f32 = j.d_out_f32;
         d.rows = (int32_t)j.m.rows;
@@ -640,13 +633,11 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         hj[i] = d;
         if (!bitserial)
             for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
-        if (bitserial)
-            for (int64_t b = 0; b < j.m.bpr; ++b) hs[si++] = bpw::StageItem{i, (int32_t)b};
         if (j.m.rows > 0) plan->has_work = 1;
     }
     if (bitserial) {
         std::memcpy(host.data() + L.work_off, segs.data(), segs.size() * sizeof(bpw::Segment));
-        std::memcpy(host.data() + L.wg_off, wave_seg.data(), wave_seg.size() * sizeof(int32_t));
+        std::memcpy(host.data() + L.wg_off, wg_seg.data(), wg_seg.size() * sizeof(int32_t));
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
@@ -667,29 +658,15 @@ static bpw_status plan_ready(const bpw_gemv_plan *plan) {
     return check_device();
 }
 
-bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream) {
-    bpw_status st = plan_ready(plan);
-    if (st) return st;
-    if (plan->kernel == BPW_KERNEL_BYTELANE || plan->n_stage == 0 || !plan->has_work) return BPW_OK;
-    return hip_status(bpw::launch_stage_xplanes(plan->jobs, plan->stage, (int32_t)plan->n_stage, stream),
-                      "stage launch");
-}
-
-bpw_status bpw_gemv_plan_run_main(const bpw_gemv_plan *plan, void *stream) {
+bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream) {
     bpw_status st = plan_ready(plan);
     if (st) return st;
     if (!plan->has_work) return BPW_OK;
     if (plan->kernel == BPW_KERNEL_BYTELANE)
         return hip_status(bpw::launch_gemv_tiles(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
                           "gemv launch");
-    return hip_status(bpw::launch_gemv_persistent(plan->jobs, plan->segs, plan->wave_seg, plan->n_wg, stream),
+    return hip_status(bpw::launch_gemv_persistent(plan->jobs, plan->segs, plan->wg_seg, plan->n_wg, stream),
                       "gemv launch");
-}
-
-bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream) {
-    bpw_status st = bpw_gemv_plan_run_stage(plan, stream);
-    if (st) return st;
-    return bpw_gemv_plan_run_main(plan, stream);
 }
 
 void bpw_gemv_plan_free(bpw_gemv_plan *plan) { delete plan; }

@@ -11,8 +11,11 @@ namespace bpw {
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // wave64
 constexpr int kKMax = 7;                  // 64-column blocks one lane handles per pass (tiled byte-lane kernel)
-constexpr int kKMaxPersistent = 8;        // beats one lane holds per row-group (persistent bit-serial kernel)
-constexpr int kXPassBlocks = 256;         // activation-plane blocks held in LDS per pass (16 KiB)
+constexpr int kKMaxPersistent = 2;        // beats one lane holds per row-group (persistent bit-serial kernel,
+                                          // shapes other than 2560 and 6912 columns)
+constexpr int kXPassBlocks = 128;         // activation-plane blocks held in LDS per pass (8 KiB)
+static_assert(kXPassBlocks == 64 * kKMaxPersistent, "a wide row's pass is one full wave of lanes x kKMaxPersistent");
+static_assert(kXPassBlocks * 4 % (64 * 4) == 0, "planes are staged in whole rounds of the workgroup");
 constexpr int kSegRows = 1024;            // rows of one persistent-kernel segment (its sums sit in LDS)
 constexpr int kIters = 4;                 // row-iterations per wave per tile
 
@@ -20,7 +23,6 @@ constexpr int kIters = 4;                 // row-iterations per wave per tile
 struct DevJob {
     const uint8_t *planes;  // rows * bpr beats of 16 bytes
     const int8_t *x;        // activation codes, >= bpr * 64 bytes readable, 16-byte aligned
-    uint32_t *xplanes;      // workspace: bpr * 16 words of activation bit planes (bit-serial only)
     int32_t *out_i32;
     float *out_f32;         // may be null
     int32_t rows;
@@ -49,11 +51,6 @@ struct DevTile {
     int32_t row0;
 };
 
-struct StageItem {
-    int32_t job;    // (gemv) job index, (small batch) token index
-    int32_t block;  // 64-column block
-};
-
 // Small-batch arguments (passed by value; <= 64 tokens).
 constexpr int kMaxBatch = 64;
 struct SmallBatchArgs {
@@ -67,7 +64,6 @@ struct SmallBatchArgs {
 };
 
 // Kernel launchers (bpw_kernels.hip). Each returns the hipError_t of its launch as int.
-int launch_stage_xplanes(const DevJob *jobs, const StageItem *items, int32_t n_items, void *stream);
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
 int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
                            void *stream);  // bit-serial

@@ -62,84 +62,89 @@ __device__ __forceinline__ void write_row(const DevJob &J, int row, int32_t s) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Activation staging: x int8 [bpr * 64] -> bit planes [bpr][16] (word 2j + h = bit j of columns
-// 32h .. 32h+31 of the block). One wave per 64-column block; lane l holds column l and eight
-// ballots give the eight 64-bit planes.
+// Activation bit planes. Block b of x (64 int8 codes) becomes 16 words: word 2j + h holds bit j of
+// columns 32h .. 32h+31, column 32h + k at bit k. In LDS, block b's four 16-byte quarters are
+// rotated by (b >> 1) & 3, so the G blocks one wave reads at a time spread over all banks.
 
-__global__ __launch_bounds__(kThreads) void stage_xplanes_kernel(const DevJob *__restrict__ jobs,
-                                                                 const StageItem *__restrict__ items,
-                                                                 int32_t n_items) {
-    const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (item >= n_items) return;  // whole waves only: the ballots below see all 64 lanes
-    const int lane = threadIdx.x & 63;
-    const StageItem it = items[item];
-    const DevJob &J = jobs[it.job];
-    const uint32_t xv = (uint8_t)J.x[(int64_t)it.block * 64 + lane];
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint64_t m = __ballot((xv >> j) & 1u);
-        if ((lane >> 1) == j) word = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
-    }
-    if (lane < 16) J.xplanes[(int64_t)it.block * 16 + lane] = word;
+__device__ __forceinline__ int xq_slot(int b, int i) { return b * 4 + ((i + (b >> 1)) & 3); }
+
+// Bit j of each byte of d, gathered into bits 0..3 (byte i -> bit i). After the mask the four bits
+// sit at 0, 8, 16 and 24; multiplying by 2^24 + 2^17 + 2^10 + 2^3 lands them on 24..27, and no two
+// of the sixteen shifted copies share a bit position, so nothing carries into that field.
+__device__ __forceinline__ uint32_t byte_bits(uint32_t d, int j) {
+    return (((d >> j) & 0x01010101u) * 0x01020408u) >> 24;
 }
 
-// Same transform for a token-major batch X [batch][ldx] -> [batch][bpr][16].
-__global__ __launch_bounds__(kThreads) void stage_batch_kernel(const int8_t *__restrict__ X, int64_t ldx,
-                                                               uint32_t *__restrict__ xplanes, int32_t bpr,
-                                                               int32_t batch) {
-    const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (item >= bpr * batch) return;
-    const int lane = threadIdx.x & 63;
-    const int t = item / bpr, b = item - t * bpr;
-    const uint32_t xv = (uint8_t)X[(int64_t)t * ldx + (int64_t)b * 64 + lane];
-    uint32_t word = 0;
+// Planes of one 16-column piece of x (the 16 bytes in v) for bit j: column k of the piece at bit k.
+__device__ __forceinline__ uint32_t piece_plane(const u32x4 &v, int j) {
+    return byte_bits(v.x, j) | (byte_bits(v.y, j) << 4) | (byte_bits(v.z, j) << 8) | (byte_bits(v.w, j) << 12);
+}
+
+// Build the planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks) in LDS, all waves of the
+// workgroup. A lane takes one 16-byte piece (block p / 4, quarter p % 4) and stores its 16 bits of
+// each plane as one 16-bit LDS write. ROUNDS (a compile-time count, so nothing here branches) must
+// cover the nb * 4 pieces; pieces past them read zeros through the buffer range check and write
+// zero planes into blocks no beat of this pass selects from.
+template <int ROUNDS>
+__device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
+    static_assert(ROUNDS >= 1 && ROUNDS * kThreads <= kXPassBlocks * 4, "pieces must fit the LDS copy");
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
+    uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
+    u32x4 v[ROUNDS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint64_t m = __ballot((xv >> j) & 1u);
-        if ((lane >> 1) == j) word = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+    for (int i = 0; i < ROUNDS; ++i) {
+        const int p = i * kThreads + wave * 64 + lane;
+        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
     }
-    if (lane < 16) xplanes[((int64_t)t * bpr + b) * 16 + lane] = word;
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+        const int p = i * kThreads + wave * 64 + lane;
+        const int b = p >> 2, qq = p & 3;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int w = 2 * j + (qq >> 1);
+            xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)piece_plane(v[i], j);
+        }
+    }
 }
 
 // ------------------------------------------------------------------------------------------
 // Batch-1 GEMV, bit-serial select, persistent. The grid is the set of workgroups the device holds
 // at once; each workgroup walks its own list of segments (runs of consecutive row-groups of one job)
-// that the host balanced by plane bytes. Per segment the workgroup copies the job's activation
-// planes into LDS, then its four waves take row-groups in turn. A row is served by G = 2^glog
+// that the host balanced by plane bytes. Per segment the workgroup builds the job's activation
+// planes in LDS, then its four waves take row-groups in turn. A row is served by G = 2^glog
 // consecutive lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes
-// of each of 64/G rows), holding only those K beats in registers, so many waves fit per SIMD and
-// keep loads in flight. Loads past the matrix use an offset that the buffer range check answers
-// with zeros, which also covers the partial last row-group.
-//
-// LDS layout of the planes: block b's four 16-byte quarters are rotated by (b >> 1) & 3, so the G
-// blocks one wave reads at a time spread over all 32 banks instead of piling onto two groups.
+// of each of 64/G rows), holding only those K beats in registers. Each wave keeps the next row's
+// loads in flight while it reduces the current one. Loads past the matrix use an offset that the
+// buffer range check answers with zeros, which also covers the partial last row-group.
 
-__device__ __forceinline__ int xq_slot(int b, int i) { return b * 4 + ((i + (b >> 1)) & 3); }
-
-// Beats b = bbase + k*G of one row (zeros past bpr or past the matrix).
-template <int K>
-__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, int bbase, int G,
-                                          int bpr) {
+// Beats b = bbase + k*G of one row: zeros past bpr, past the matrix, or for a row-group that does
+// not exist (live == false), all through offsets the buffer range check turns into zeros. The loads
+// are issued on every path, so the compiler can count them and wait for exactly the older ones.
+// NB > 0 is bpr known at compile time, which removes the bound checks that cannot fail.
+template <int K, int NB>
+__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, bool live, int bbase,
+                                          int G, int bpr) {
     const uint32_t rowoff = row * (uint32_t)bpr;
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         const int b = bbase + k * G;
-        const uint32_t off = (b < bpr) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
+        const bool in = NB > 0 ? (b < NB) : (b < bpr);
+        const uint32_t off = (live && in) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
         B[k] = load_beat(wr, off);
     }
 }
 
-// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
-//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
-// Blocks past the pass (b >= nb) hold zero beats and contribute nothing; their LDS reads are clamped
-// to block 0 so they stay inside the copy.
-template <int K>
-__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G, int nb) {
-    const int b = (g + k * G) < nb ? g + k * G : 0;
+// The 16 plane words of block g + k*G (the block beat k of lane g covers). The index stays below
+// K * G <= kXPassBlocks, inside the LDS copy, even past the pass or past bpr: there the beat is zero
+// and the select yields zero whatever the words hold. When G is a multiple of 8 every block a lane
+// reads has the rotation of block g, so the addresses are one base plus constant offsets.
+template <int GLOG>
+__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G) {
+    const int b = g + k * G;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const u32x4 w = xl[xq_slot(b, i)];
+        const u32x4 w = GLOG >= 3 ? xl[g * 4 + k * (4 << GLOG) + ((i + (g >> 1)) & 3)] : xl[xq_slot(b, i)];
         X[4 * i + 0] = w.x;
         X[4 * i + 1] = w.y;
         X[4 * i + 2] = w.z;
@@ -149,21 +154,20 @@ __device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, 
 
 // Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
 //   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
-// Blocks past the pass (b >= nb) hold zero beats and contribute nothing; their LDS reads are clamped
-// to block 0 so they stay inside the copy. The planes of beat k+1 are read while beat k is reduced;
-// scheduling barriers keep the compiler from hoisting every beat's reads (which would cost 16
-// registers per beat and the occupancy this kernel relies on).
-template <int K>
-__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G, int nb) {
+// The planes of beat k+1 are read while beat k is reduced; the empty asm statements keep the
+// compiler from hoisting every beat's reads (16 registers per beat, and the occupancy this kernel
+// relies on).
+template <int K, int GLOG>
+__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G) {
     uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
     uint32_t cn = 0;
     uint32_t Xa[16], Xb[16];
-    read_planes<K>(Xa, xl, 0, g, G, nb);
+    read_planes<GLOG>(Xa, xl, 0, g, G);
 #pragma unroll
     for (int k = 0; k < K; ++k) {
         uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
         uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
-        if (k + 1 < K) read_planes<K>(Xn, xl, k + 1, g, G, nb);
+        if (k + 1 < K) read_planes<GLOG>(Xn, xl, k + 1, g, G);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
@@ -171,7 +175,6 @@ __device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)
         }
         cn = __builtin_popcount(B[k].z) + cn;
         cn = __builtin_popcount(B[k].w) + cn;
-        // beat k is finished here: its counts must exist before any later LDS read is issued
         asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
                      "+v"(c[7]), "+v"(cn)::"memory");
     }
@@ -182,16 +185,12 @@ __device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)
     return acc;
 }
 
-// Copy planes of blocks [b0, b0 + nb) into LDS (swizzled), all threads of the workgroup.
-__device__ __forceinline__ void stage_pass(u32x4 *xl, const uint32_t *xplanes, int b0, int nb) {
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(xplanes) + (int64_t)b0 * 4;
-    for (int t = threadIdx.x; t < nb * 4; t += kThreads) xl[xq_slot(t >> 2, t & 3)] = src[t];
-}
-
-// Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced
-// pass at the end: a vector store inside the streaming loop would share the vector-memory counter
-// with the weight loads and make every wait in the loop a wait for all loads in flight.
-template <int K, int GLOG>
+// Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced pass
+// at the end: a vector store inside the streaming loop would share the vector-memory counter with
+// the weight loads and make every wait in the loop a wait for all loads in flight.
+// GLOG >= 0 and NB > 0 fix the geometry at compile time (one pass, NB == bpr); otherwise it is read
+// from the job.
+template <int K, int GLOG, int NB>
 __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
                                            int32_t *sums) {
     const int glog = GLOG >= 0 ? GLOG : J.glog;
@@ -199,24 +198,39 @@ __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int 
     const int g = lane & (G - 1);
     const int q = lane >> glog;
     const int rpi = 64 >> glog;
-    const int bpr = J.bpr;
+    const int bpr = NB > 0 ? NB : J.bpr;
     const int pass_blocks = K * G;
+    const int nchunk = NB > 0 ? 1 : J.nchunk;
+    constexpr int kStageRounds = NB > 0 ? (NB * 4 + kThreads - 1) / kThreads : kXPassBlocks * 4 / kThreads;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, J.plane_bytes);
-    for (int ch = 0; ch < J.nchunk; ++ch) {
+    for (int ch = 0; ch < nchunk; ++ch) {
         const int b0 = ch * pass_blocks;
         const int nb = min(pass_blocks, bpr - b0);
+        const int bb = b0 + g;
+        u32x4 B0[K], B1[K];
+        int u = u0 + wave;
+        issue_row<K, NB>(B0, wr, (uint32_t)(u * rpi + q), u < u1, bb, G, bpr);
         __syncthreads();  // every wave is done with the previous planes and sums
-        stage_pass(xl, J.xplanes, b0, nb);
+        stage_planes<kStageRounds>(xl, J.x, b0, nb, wave, lane);
         __syncthreads();
-        for (int u = u0 + wave; u < u1; u += kWaves) {
-            const uint32_t row = (uint32_t)(u * rpi + q);
-            u32x4 B[K];
-            issue_row<K>(B, wr, row, b0 + g, G, bpr);
-            asm volatile("" ::: "memory");  // all K weight loads leave before the first LDS read
-            const int32_t tot = group_sum(row_partial<K>(xl, B, g, G, nb), glog);
-            if (g == 0) {
+        // Two register sets alternate: the loads of row-group u + kWaves leave before row-group u
+        // is reduced. One trip handles row-groups u and u + kWaves with no exit in between, so every
+        // load is issued on every path (row-groups past u1 read zeros and store nothing) and the
+        // compiler's waits cover exactly the older set.
+        for (; u < u1; u += 2 * kWaves) {
+            issue_row<K, NB>(B1, wr, (uint32_t)((u + kWaves) * rpi + q), u + kWaves < u1, bb, G, bpr);
+            asm volatile("" ::: "memory");
+            {
+                const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B0, g, G), glog);
                 const int i = (u - u0) * rpi + q;
-                sums[i] = ch == 0 ? tot : sums[i] + tot;  // the same lane owns this slot in every pass
+                if (g == 0) sums[i] = ch == 0 ? tot : sums[i] + tot;  // one lane owns a slot in every pass
+            }
+            issue_row<K, NB>(B0, wr, (uint32_t)((u + 2 * kWaves) * rpi + q), u + 2 * kWaves < u1, bb, G, bpr);
+            asm volatile("" ::: "memory");
+            {
+                const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B1, g, G), glog);
+                const int i = (u + kWaves - u0) * rpi + q;
+                if (g == 0 && u + kWaves < u1) sums[i] = ch == 0 ? tot : sums[i] + tot;
             }
         }
     }
@@ -245,26 +259,40 @@ __global__ __launch_bounds__(kThreads) void gemv_bitserial_kernel(const DevJob *
     for (int si = s0; si < s1; ++si) {
         const Segment sg = segs[si];
         const DevJob J = jobs[sg.job];
-        if (J.kblk == 5 && J.glog == 3) {  // 2560-column rows: 8 lanes x 5 beats
-            bs_segment<5, 3>(J, sg.u0, sg.u1, wave, lane, xl, sums);
+        if (J.bpr == 40) {  // 2560-column rows: 8 lanes x 5 beats
+            bs_segment<5, 3, 40>(J, sg.u0, sg.u1, wave, lane, xl, sums);
             continue;
         }
-        if (J.kblk == 7 && J.glog == 4) {  // 6912-column rows: 16 lanes x 7 beats (108 of 112 used)
-            bs_segment<7, 4>(J, sg.u0, sg.u1, wave, lane, xl, sums);
+        if (J.bpr == 108) {  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
+            bs_segment<4, 5, 108>(J, sg.u0, sg.u1, wave, lane, xl, sums);
             continue;
         }
         switch (J.kblk) {
             case 0: bs_segment_empty(J, sg.u0, sg.u1, wave, lane); break;
-            case 1: bs_segment<1, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 2: bs_segment<2, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 3: bs_segment<3, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 4: bs_segment<4, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 5: bs_segment<5, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 6: bs_segment<6, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            case 7: bs_segment<7, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            default: bs_segment<8, -1>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            case 1: bs_segment<1, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
+            default: bs_segment<2, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
         }
     }
+}
+
+// ------------------------------------------------------------------------------------------
+// Small-batch activation planes: a token-major batch X [batch][ldx] -> [batch][bpr][16], the same
+// word order as above, one wave per 64-column block (eight ballots give the eight planes).
+__global__ __launch_bounds__(kThreads) void stage_batch_kernel(const int8_t *__restrict__ X, int64_t ldx,
+                                                               uint32_t *__restrict__ xplanes, int32_t bpr,
+                                                               int32_t batch) {
+    const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (item >= bpr * batch) return;
+    const int lane = threadIdx.x & 63;
+    const int t = item / bpr, b = item - t * bpr;
+    const uint32_t xv = (uint8_t)X[(int64_t)t * ldx + (int64_t)b * 64 + lane];
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint64_t m = __ballot((xv >> j) & 1u);
+        if ((lane >> 1) == j) word = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+    }
+    if (lane < 16) xplanes[((int64_t)t * bpr + b) * 16 + lane] = word;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -574,13 +602,6 @@ __global__ __launch_bounds__(kThreads) void flush_kernel(u32x4 *__restrict__ p, 
 // Launchers.
 
 static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
-
-int launch_stage_xplanes(const DevJob *jobs, const StageItem *items, int32_t n_items, void *stream) {
-    if (n_items <= 0) return hipSuccess;
-    const unsigned grid = (unsigned)((n_items + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(stage_xplanes_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), jobs, items, n_items);
-    return hipGetLastError();
-}
 
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream) {
     if (n_tiles <= 0) return hipSuccess;

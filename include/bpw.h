@@ -152,15 +152,15 @@ bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *st
 
 /* ------------------------------------------------------------------------ batch-1 GEMV */
 
-/* Device workspace bytes that bpw_gemv / bpw_gemv_plan_create need for these jobs: the job and
- * tile tables and each job's activation bit planes (bpr * 64 bytes per job). */
+/* Device workspace bytes that bpw_gemv / bpw_gemv_plan_create need for these jobs: the job table,
+ * the row-group segments of the persistent grid and their per-workgroup offsets. */
 size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs);
 
-/* Run n_jobs independent GEMVs as one grouped launch (plus one activation-staging launch) on
- * `stream`. The job table is copied into d_ws (ws_len >= bpw_gemv_workspace_bytes); this call
- * waits until that copy has landed, so it also waits for earlier work on `stream`. Callers that
- * repeat the same jobs should build a plan once and call bpw_gemv_plan_run. n_jobs == 0 does
- * nothing and returns BPW_OK. Jobs must not write overlapping outputs. */
+/* Run n_jobs independent GEMVs as one kernel launch on `stream`. The job table is copied into d_ws
+ * (ws_len >= bpw_gemv_workspace_bytes); this call waits until that copy has landed, so it also
+ * waits for earlier work on `stream`. Callers that repeat the same jobs should build a plan once
+ * and call bpw_gemv_plan_run. n_jobs == 0 does nothing and returns BPW_OK. Jobs must not write
+ * overlapping outputs. */
 bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws, size_t ws_len,
                     void *stream);
 
@@ -169,20 +169,14 @@ typedef struct bpw_gemv_plan bpw_gemv_plan;
 
 /* Check the jobs, write their tables into d_ws (waiting for the copy, as bpw_gemv does) and return
  * a host handle. The workspace, the matrices, activations and outputs named by the jobs must stay
- * valid for the plan's lifetime; their contents may change between runs. */
+ * valid for the plan's lifetime; their contents may change between runs (each run reads the
+ * activations as they are when it executes). */
 bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
                                 size_t ws_len, void *stream, bpw_gemv_plan **out);
 
-/* Queue one execution of a plan on `stream` (two kernel launches, no host-device copies). Runs
- * queued on one stream execute in order; concurrent runs of one plan on different streams race on
- * its workspace. */
+/* Queue one execution of a plan on `stream`: a single kernel launch, no host-device copies, no
+ * writes to the workspace (runs of one plan on different streams only race on the outputs). */
 bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream);
-
-/* The two halves of bpw_gemv_plan_run, for callers that time or schedule them apart: the first
- * writes each job's activation bit planes into the workspace (a no-op for BPW_KERNEL_BYTELANE),
- * the second streams the weights and writes the outputs. Queue them in this order on one stream. */
-bpw_status bpw_gemv_plan_run_stage(const bpw_gemv_plan *plan, void *stream);
-bpw_status bpw_gemv_plan_run_main(const bpw_gemv_plan *plan, void *stream);
 
 void bpw_gemv_plan_free(bpw_gemv_plan *plan);
 
