@@ -406,7 +406,7 @@ struct bpw_gemv_plan {
     int32_t kernel;
     const bpw::DevJob *jobs;
     const bpw::DevTile *tiles;     // byte-lane
-    const bpw::Segment *segs;      // bit-serial
+    const bpw::Segment *segs;      // bit-serial: segments, grouped by workgroup
     const int32_t *wg_seg;         // bit-serial: per-workgroup segment offsets
     int64_t n_tiles;
     int32_t n_wg;                  // bit-serial persistent workgroups

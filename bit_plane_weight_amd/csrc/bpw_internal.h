@@ -13,10 +13,12 @@ constexpr int kThreads = 64 * kWaves;     // wave64
 constexpr int kKMax = 7;                  // 64-column blocks one lane handles per pass (tiled byte-lane kernel)
 constexpr int kKMaxPersistent = 2;        // beats one lane holds per row-group (persistent bit-serial kernel,
                                           // shapes other than 2560 and 6912 columns)
+constexpr int kPWaves = 16;               // waves of the persistent GEMV workgroup (one workgroup per CU)
+constexpr int kPThreads = 64 * kPWaves;
 constexpr int kXPassBlocks = 128;         // activation-plane blocks held in LDS per pass (8 KiB)
 static_assert(kXPassBlocks == 64 * kKMaxPersistent, "a wide row's pass is one full wave of lanes x kKMaxPersistent");
-static_assert(kXPassBlocks * 4 % (64 * 4) == 0, "planes are staged in whole rounds of the workgroup");
-constexpr int kSegRows = 1024;            // rows of one persistent-kernel segment (its sums sit in LDS)
+static_assert(kXPassBlocks * 4 <= kPThreads, "one lane per 16-byte piece stages a whole pass");
+constexpr int kSegRows = 4096;            // rows of one persistent-kernel segment (its sums sit in LDS)
 constexpr int kIters = 4;                 // row-iterations per wave per tile
 
 // One GEMV of a grouped launch, as the kernels read it (lives in the caller's workspace).
@@ -37,8 +39,8 @@ struct DevJob {
     int32_t pad;
 };
 
-// A run of consecutive row-groups ("units" of 64 / G rows) of one job, owned by one workgroup of
-// the persistent bit-serial kernel. Units [u0, u1).
+// A run of consecutive row-groups ("units" of 64 / G rows) of one job, run by one workgroup of the
+// persistent bit-serial kernel. Units [u0, u1), at most kSegRows rows.
 struct Segment {
     int32_t job;
     int32_t u0;
@@ -65,8 +67,9 @@ struct SmallBatchArgs {
 
 // Kernel launchers (bpw_kernels.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
+// bit-serial: workgroup w runs segments [wg_seg[w], wg_seg[w + 1]) in order
 int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
-                           void *stream);  // bit-serial
+                           void *stream);
 // Workgroups of the persistent bit-serial kernel that are resident at once on the current device
 // (CUs x occupancy); 0 on error.
 int32_t persistent_workgroups();

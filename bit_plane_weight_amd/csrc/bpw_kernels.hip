@@ -80,43 +80,37 @@ __device__ __forceinline__ uint32_t piece_plane(const u32x4 &v, int j) {
     return byte_bits(v.x, j) | (byte_bits(v.y, j) << 4) | (byte_bits(v.z, j) << 8) | (byte_bits(v.w, j) << 12);
 }
 
-// Build the planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks) in LDS, all waves of the
-// workgroup. A lane takes one 16-byte piece (block p / 4, quarter p % 4) and stores its 16 bits of
-// each plane as one 16-bit LDS write. ROUNDS (a compile-time count, so nothing here branches) must
-// cover the nb * 4 pieces; pieces past them read zeros through the buffer range check and write
-// zero planes into blocks no beat of this pass selects from.
-template <int ROUNDS>
+// Planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks), built in LDS by the first
+// ceil(nb / 16) waves of the workgroup: a lane loads one 16-byte piece (piece p = block p / 4,
+// quarter p % 4) and stores its 16 bits of every plane as one 16-bit LDS write. Pieces of the last
+// wave past nb * 4 read zeros through the buffer range check and write zero planes into blocks no
+// beat of this pass selects from. The branch is uniform per wave and each wave consumes its load
+// inside it, so no load is left outstanding behind it.
 __device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
-    static_assert(ROUNDS >= 1 && ROUNDS * kThreads <= kXPassBlocks * 4, "pieces must fit the LDS copy");
+    if (wave >= (nb * 4 + 63) / 64) return;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
+    const int p = wave * 64 + lane;
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
     uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
-    u32x4 v[ROUNDS];
+    const int b = p >> 2, qq = p & 3;
 #pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-        const int p = i * kThreads + wave * 64 + lane;
-        v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-        const int p = i * kThreads + wave * 64 + lane;
-        const int b = p >> 2, qq = p & 3;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int w = 2 * j + (qq >> 1);
-            xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)piece_plane(v[i], j);
-        }
+    for (int j = 0; j < 8; ++j) {
+        const int w = 2 * j + (qq >> 1);
+        xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)piece_plane(v, j);
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Batch-1 GEMV, bit-serial select, persistent. The grid is the set of workgroups the device holds
-// at once; each workgroup walks its own list of segments (runs of consecutive row-groups of one job)
-// that the host balanced by plane bytes. Per segment the workgroup builds the job's activation
-// planes in LDS, then its four waves take row-groups in turn. A row is served by G = 2^glog
-// consecutive lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes
-// of each of 64/G rows), holding only those K beats in registers. Each wave keeps the next row's
-// loads in flight while it reduces the current one. Loads past the matrix use an offset that the
-// buffer range check answers with zeros, which also covers the partial last row-group.
+// Batch-1 GEMV, bit-serial select, persistent. One workgroup of kPWaves waves per compute unit;
+// the host splits all jobs' row-groups over the workgroups by plane bytes into segments (runs of
+// consecutive row-groups of one job). Per segment the workgroup builds the job's activation planes
+// in LDS, then its waves claim row-groups from an LDS counter: the compute unit serves older waves
+// first, so a fixed share per wave would leave the younger ones finishing last, while claiming
+// keeps every wave busy until the segment runs out. A row is served by G = 2^glog consecutive
+// lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes of each of
+// 64/G rows), holding only those K beats in registers. Each wave keeps its next row-group's loads in
+// flight while it reduces the current one. Loads past the matrix use an offset that the buffer range
+// check answers with zeros, which also covers the partial last row-group.
 
 // Beats b = bbase + k*G of one row: zeros past bpr, past the matrix, or for a row-group that does
 // not exist (live == false), all through offsets the buffer range check turns into zeros. The loads
@@ -185,14 +179,21 @@ __device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)
     return acc;
 }
 
+// Next row-group for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
+__device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(v);
+}
+
 // Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced pass
-// at the end: a vector store inside the streaming loop would share the vector-memory counter with
-// the weight loads and make every wait in the loop a wait for all loads in flight.
+// at the end: a vector store inside the streaming loop would count against the same vector-memory
+// counter as the weight loads.
 // GLOG >= 0 and NB > 0 fix the geometry at compile time (one pass, NB == bpr); otherwise it is read
 // from the job.
 template <int K, int GLOG, int NB>
 __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
-                                           int32_t *sums) {
+                                           int32_t *sums, uint32_t *claim) {
     const int glog = GLOG >= 0 ? GLOG : J.glog;
     const int G = 1 << glog;
     const int g = lane & (G - 1);
@@ -201,77 +202,78 @@ __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int 
     const int bpr = NB > 0 ? NB : J.bpr;
     const int pass_blocks = K * G;
     const int nchunk = NB > 0 ? 1 : J.nchunk;
-    constexpr int kStageRounds = NB > 0 ? (NB * 4 + kThreads - 1) / kThreads : kXPassBlocks * 4 / kThreads;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, J.plane_bytes);
     for (int ch = 0; ch < nchunk; ++ch) {
         const int b0 = ch * pass_blocks;
         const int nb = min(pass_blocks, bpr - b0);
         const int bb = b0 + g;
         u32x4 B0[K], B1[K];
-        int u = u0 + wave;
+        int u = u0 + wave;  // every wave's first row-group is fixed; the rest are claimed
         issue_row<K, NB>(B0, wr, (uint32_t)(u * rpi + q), u < u1, bb, G, bpr);
-        __syncthreads();  // every wave is done with the previous planes and sums
-        stage_planes<kStageRounds>(xl, J.x, b0, nb, wave, lane);
+        __syncthreads();  // every wave is done with the previous planes, sums and counter
+        if (threadIdx.x == 0) *claim = (uint32_t)(u0 + kPWaves);
+        stage_planes(xl, J.x, b0, nb, wave, lane);
         __syncthreads();
-        // Two register sets alternate: the loads of row-group u + kWaves leave before row-group u
-        // is reduced. One trip handles row-groups u and u + kWaves with no exit in between, so every
-        // load is issued on every path (row-groups past u1 read zeros and store nothing) and the
-        // compiler's waits cover exactly the older set.
-        for (; u < u1; u += 2 * kWaves) {
-            issue_row<K, NB>(B1, wr, (uint32_t)((u + kWaves) * rpi + q), u + kWaves < u1, bb, G, bpr);
+        // Two register sets alternate: the loads of the next row-group leave before the current one
+        // is reduced. One trip handles two row-groups with no exit in between, so every load is
+        // issued on every path (row-groups past u1 read zeros and store nothing) and the compiler's
+        // waits cover exactly the older set.
+        while (u < u1) {
+            const int ua = claim_next(claim, lane);
+            issue_row<K, NB>(B1, wr, (uint32_t)(ua * rpi + q), ua < u1, bb, G, bpr);
             asm volatile("" ::: "memory");
             {
                 const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B0, g, G), glog);
                 const int i = (u - u0) * rpi + q;
-                if (g == 0) sums[i] = ch == 0 ? tot : sums[i] + tot;  // one lane owns a slot in every pass
+                if (g == 0) sums[i] = ch == 0 ? tot : sums[i] + tot;  // passes are separated by barriers
             }
-            issue_row<K, NB>(B0, wr, (uint32_t)((u + 2 * kWaves) * rpi + q), u + 2 * kWaves < u1, bb, G, bpr);
+            const int ub = claim_next(claim, lane);
+            issue_row<K, NB>(B0, wr, (uint32_t)(ub * rpi + q), ub < u1, bb, G, bpr);
             asm volatile("" ::: "memory");
             {
                 const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B1, g, G), glog);
-                const int i = (u + kWaves - u0) * rpi + q;
-                if (g == 0 && u + kWaves < u1) sums[i] = ch == 0 ? tot : sums[i] + tot;
+                const int i = (ua - u0) * rpi + q;
+                if (g == 0 && ua < u1) sums[i] = ch == 0 ? tot : sums[i] + tot;
             }
+            u = ub;
         }
     }
     __syncthreads();
     const int row0 = u0 * rpi, n = (u1 - u0) * rpi;
-    for (int i = threadIdx.x; i < n; i += kThreads)
+    for (int i = threadIdx.x; i < n; i += kPThreads)
         if (row0 + i < J.rows) write_row(J, row0 + i, sums[i]);
 }
 
 // cols == 0: every row is the empty sum (row-groups of 64 rows).
 __device__ __forceinline__ void bs_segment_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
-    for (int u = u0 + wave; u < u1; u += kWaves) {
+    for (int u = u0 + wave; u < u1; u += kPWaves) {
         const int row = u * 64 + lane;
         if (row < J.rows) write_row(J, row, 0);
     }
 }
 
-__global__ __launch_bounds__(kThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
-                                                                  const Segment *__restrict__ segs,
-                                                                  const int32_t *__restrict__ wg_seg) {
+__global__ __launch_bounds__(kPThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
+                                                                   const Segment *__restrict__ segs,
+                                                                   const int32_t *__restrict__ wg_seg) {
     __shared__ u32x4 xl[kXPassBlocks * 4];
     __shared__ int32_t sums[kSegRows];
+    __shared__ uint32_t claim;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int s0 = wg_seg[blockIdx.x], s1 = wg_seg[blockIdx.x + 1];
     for (int si = s0; si < s1; ++si) {
         const Segment sg = segs[si];
         const DevJob J = jobs[sg.job];
-        if (J.bpr == 40) {  // 2560-column rows: 8 lanes x 5 beats
-            bs_segment<5, 3, 40>(J, sg.u0, sg.u1, wave, lane, xl, sums);
-            continue;
-        }
-        if (J.bpr == 108) {  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
-            bs_segment<4, 5, 108>(J, sg.u0, sg.u1, wave, lane, xl, sums);
-            continue;
-        }
-        switch (J.kblk) {
-            case 0: bs_segment_empty(J, sg.u0, sg.u1, wave, lane); break;
-            case 1: bs_segment<1, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-            default: bs_segment<2, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums); break;
-        }
+        if (J.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
+            bs_segment<5, 3, 40>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else if (J.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
+            bs_segment<4, 5, 108>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else if (J.kblk == 0)
+            bs_segment_empty(J, sg.u0, sg.u1, wave, lane);
+        else if (J.kblk == 1)
+            bs_segment<1, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else
+            bs_segment<2, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
     }
 }
 
@@ -615,7 +617,7 @@ int32_t persistent_workgroups() {
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_bitserial_kernel),
-                                                     kThreads, 0) != hipSuccess)
+                                                     kPThreads, 0) != hipSuccess)
         return 0;
     if (cus <= 0 || per_cu <= 0) return 0;
     return cus * per_cu;
@@ -624,7 +626,7 @@ int32_t persistent_workgroups() {
 int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
                            void *stream) {
     if (n_wg <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_wg), dim3(kThreads), 0, as_stream(stream), jobs, segs,
+    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_wg), dim3(kPThreads), 0, as_stream(stream), jobs, segs,
                        wg_seg);
     return hipGetLastError();
 }
