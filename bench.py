@@ -31,7 +31,9 @@ METRIC = "Ternary GEMV weight GB/s (% HBM peak) + µs/decode-step, 2B4T shapes"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BASE_SEED = 0x2B47
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bitserial_decode_step_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_kernels.hip")
+# sources of the decode-step GEMV kernel; the committed counter summary holds their hash
+KERNEL_SRCS = [os.path.join(ROOT, "bit_plane_weight_amd", "csrc", f)
+               for f in ("bpw_gemv.hip", "bpw_device.h", "bpw_internal.h")]
 
 
 def log(msg: str) -> None:
@@ -39,8 +41,11 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def host_threads() -> int:
@@ -249,6 +254,9 @@ def main() -> int:
     ap.add_argument("--kernel", choices=("auto", "bitserial", "bytelane"), default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip probe, head, sweep and small batch")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the steps, read 1 GiB with the streaming probe and rewrite 1 GiB with the cache "
+                         "flush (3 times each): kernels of known traffic for scaling hardware byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -352,6 +360,17 @@ def main() -> int:
     }
     if sample:
         result["cpu_baseline"] = cpu_baseline(sample, nthreads)
+
+    if args.copy_calibration:
+        log("copy calibration: probe reads 1 GiB, flush reads and writes 1 GiB, 3 times each")
+        cal = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            bpw.bpw_stream_read_probe(cal, sink)
+        for _ in range(3):
+            bpw.bpw_cache_flush(cal)
+        torch.cuda.synchronize()
+        del cal
 
     # ---------------------------------------------------------------- companion measurements
     if not args.no_extras:

@@ -1,0 +1,244 @@
+// bpw_gemv.hip - batch-1 grouped ternary GEMV (bit-serial select) for gfx950.
+//
+// Written for CDNA4 (wave64, 4 SIMDs per CU, 160 KB LDS); launched only by bpw_host.cpp after its
+// argument and architecture checks.
+//
+// Batch-1 select-accumulate (Tritium paper, introduction, Equations 2-3). Weights stream as
+// .trit v1 beats ("The .trit format, version 1", 2.3): 16 bytes = pos[64] | neg[64]. With the
+// activation split into its eight two's-complement bit planes X_j (Tritium paper, "On popcount"),
+// the exact row sum is
+//     acc = sum_j w_j * (popc(pos & X_j) - popc(neg & X_j)),   w_j = 2^j (j < 7), w_7 = -128.
+// Because pos and neg are disjoint (P1), f_j = (pos & X_j) | (neg & ~X_j) is one 3-input bitwise
+// select (v_bitop3_b32), and popc(f_j) = popc(pos & X_j) + popc(neg) - popc(neg & X_j). Summing
+// with the weights w_j, whose total is -1, gives
+//     acc = sum_j w_j * popc(f_j) + popc(neg)
+// so one beat costs 16 selects + 18 accumulating popcounts (v_bcnt_u32_b32) for both planes,
+// against ~128 ops for widening mask bits to byte lanes. Padding bits are clear (P2), so whole
+// 64-column blocks are processed with no tail loop; the sum is an exact integer, so lane order and
+// reduction order cannot change it (Tritium paper, "Verification").
+#include <hip/hip_runtime.h>
+
+#include "bpw_device.h"
+
+namespace bpw {
+
+// Planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks), built in LDS by the first
+// ceil(nb / 16) waves of the workgroup: a lane loads one 16-byte piece (piece p = block p / 4,
+// quarter p % 4) and stores its 16 bits of every plane as one 16-bit LDS write. Pieces of the last
+// wave past nb * 4 read zeros through the buffer range check and write zero planes into blocks no
+// beat of this pass selects from. The branch is uniform per wave and each wave consumes its load
+// inside it, so no load is left outstanding behind it.
+__device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
+    if (wave >= (nb * 4 + 63) / 64) return;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
+    const int p = wave * 64 + lane;
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
+    uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
+    const int b = p >> 2, qq = p & 3;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int w = 2 * j + (qq >> 1);
+        xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)piece_plane(v, j);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Batch-1 GEMV, bit-serial select, persistent. One workgroup of kPWaves waves per compute unit;
+// the host splits all jobs' row-groups over the workgroups by plane bytes into segments (runs of
+// consecutive row-groups of one job). Per segment the workgroup builds the job's activation planes
+// in LDS, then its waves claim row-groups from an LDS counter: the compute unit serves older waves
+// first, so a fixed share per wave would leave the younger ones finishing last, while claiming
+// keeps every wave busy until the segment runs out. A row is served by G = 2^glog consecutive
+// lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes of each of
+// 64/G rows), holding only those K beats in registers. Each wave keeps its next row-group's loads in
+// flight while it reduces the current one. Loads past the matrix use an offset that the buffer range
+// check answers with zeros, which also covers the partial last row-group.
+
+// Beats b = bbase + k*G of one row: zeros past bpr, past the matrix, or for a row-group that does
+// not exist (live == false), all through offsets the buffer range check turns into zeros. The loads
+// are issued on every path, so the compiler can count them and wait for exactly the older ones.
+// NB > 0 is bpr known at compile time, which removes the bound checks that cannot fail.
+template <int K, int NB>
+__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, bool live, int bbase,
+                                          int G, int bpr) {
+    const uint32_t rowoff = row * (uint32_t)bpr;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int b = bbase + k * G;
+        const bool in = NB > 0 ? (b < NB) : (b < bpr);
+        const uint32_t off = (live && in) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
+        B[k] = load_beat(wr, off);
+    }
+}
+
+// The 16 plane words of block g + k*G (the block beat k of lane g covers). The index stays below
+// K * G <= kXPassBlocks, inside the LDS copy, even past the pass or past bpr: there the beat is zero
+// and the select yields zero whatever the words hold. When G is a multiple of 8 every block a lane
+// reads has the rotation of block g, so the addresses are one base plus constant offsets.
+template <int GLOG>
+__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G) {
+    const int b = g + k * G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 w = GLOG >= 3 ? xl[g * 4 + k * (4 << GLOG) + ((i + (g >> 1)) & 3)] : xl[xq_slot(b, i)];
+        X[4 * i + 0] = w.x;
+        X[4 * i + 1] = w.y;
+        X[4 * i + 2] = w.z;
+        X[4 * i + 3] = w.w;
+    }
+}
+
+// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
+//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
+// The planes of beat k+1 are read while beat k is reduced; the empty asm statements keep the
+// compiler from hoisting every beat's reads (16 registers per beat, and the occupancy this kernel
+// relies on).
+template <int K, int GLOG>
+__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G) {
+    uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t cn = 0;
+    uint32_t Xa[16], Xb[16];
+    read_planes<GLOG>(Xa, xl, 0, g, G);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
+        uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
+        if (k + 1 < K) read_planes<GLOG>(Xn, xl, k + 1, g, G);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
+            c[j] = __builtin_popcount(select_bits(X[2 * j + 1], B[k].y, B[k].w)) + c[j];
+        }
+        cn = __builtin_popcount(B[k].z) + cn;
+        cn = __builtin_popcount(B[k].w) + cn;
+        asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
+                     "+v"(c[7]), "+v"(cn)::"memory");
+    }
+    int32_t acc = (int32_t)cn;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
+    acc -= (int32_t)(c[7] << 7);
+    return acc;
+}
+
+// Next row-group for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
+__device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(v);
+}
+
+// Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced pass
+// at the end: a vector store inside the streaming loop would count against the same vector-memory
+// counter as the weight loads.
+// GLOG >= 0 and NB > 0 fix the geometry at compile time (one pass, NB == bpr); otherwise it is read
+// from the job.
+template <int K, int GLOG, int NB>
+__device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
+                                           int32_t *sums, uint32_t *claim) {
+    const int glog = GLOG >= 0 ? GLOG : J.glog;
+    const int G = 1 << glog;
+    const int g = lane & (G - 1);
+    const int q = lane >> glog;
+    const int rpi = 64 >> glog;
+    const int bpr = NB > 0 ? NB : J.bpr;
+    const int pass_blocks = K * G;
+    const int nchunk = NB > 0 ? 1 : J.nchunk;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, J.plane_bytes);
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int b0 = ch * pass_blocks;
+        const int nb = min(pass_blocks, bpr - b0);
+        const int bb = b0 + g;
+        u32x4 B0[K], B1[K];
+        int u = u0 + wave;  // every wave's first row-group is fixed; the rest are claimed
+        issue_row<K, NB>(B0, wr, (uint32_t)(u * rpi + q), u < u1, bb, G, bpr);
+        __syncthreads();  // every wave is done with the previous planes, sums and counter
+        if (threadIdx.x == 0) *claim = (uint32_t)(u0 + kPWaves);
+        stage_planes(xl, J.x, b0, nb, wave, lane);
+        __syncthreads();
+        // Two register sets alternate: the loads of the next row-group leave before the current one
+        // is reduced. One trip handles two row-groups with no exit in between, so every load is
+        // issued on every path (row-groups past u1 read zeros and store nothing) and the compiler's
+        // waits cover exactly the older set.
+        while (u < u1) {
+            const int ua = claim_next(claim, lane);
+            issue_row<K, NB>(B1, wr, (uint32_t)(ua * rpi + q), ua < u1, bb, G, bpr);
+            asm volatile("" ::: "memory");
+            {
+                const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B0, g, G), glog);
+                const int i = (u - u0) * rpi + q;
+                if (g == 0) sums[i] = ch == 0 ? tot : sums[i] + tot;  // passes are separated by barriers
+            }
+            const int ub = claim_next(claim, lane);
+            issue_row<K, NB>(B0, wr, (uint32_t)(ub * rpi + q), ub < u1, bb, G, bpr);
+            asm volatile("" ::: "memory");
+            {
+                const int32_t tot = group_sum(row_partial<K, GLOG>(xl, B1, g, G), glog);
+                const int i = (ua - u0) * rpi + q;
+                if (g == 0 && ua < u1) sums[i] = ch == 0 ? tot : sums[i] + tot;
+            }
+            u = ub;
+        }
+    }
+    __syncthreads();
+    const int row0 = u0 * rpi, n = (u1 - u0) * rpi;
+    for (int i = threadIdx.x; i < n; i += kPThreads)
+        if (row0 + i < J.rows) write_row(J, row0 + i, sums[i]);
+}
+
+// cols == 0: every row is the empty sum (row-groups of 64 rows).
+__device__ __forceinline__ void bs_segment_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
+    for (int u = u0 + wave; u < u1; u += kPWaves) {
+        const int row = u * 64 + lane;
+        if (row < J.rows) write_row(J, row, 0);
+    }
+}
+
+__global__ __launch_bounds__(kPThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
+                                                                   const Segment *__restrict__ segs,
+                                                                   const int32_t *__restrict__ wg_seg) {
+    __shared__ u32x4 xl[kXPassBlocks * 4];
+    __shared__ int32_t sums[kSegRows];
+    __shared__ uint32_t claim;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int s0 = wg_seg[blockIdx.x], s1 = wg_seg[blockIdx.x + 1];
+    for (int si = s0; si < s1; ++si) {
+        const Segment sg = segs[si];
+        const DevJob J = jobs[sg.job];
+        if (J.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
+            bs_segment<5, 3, 40>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else if (J.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
+            bs_segment<4, 5, 108>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else if (J.kblk == 0)
+            bs_segment_empty(J, sg.u0, sg.u1, wave, lane);
+        else if (J.kblk == 1)
+            bs_segment<1, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+        else
+            bs_segment<2, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers.
+
+int32_t persistent_workgroups() {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_bitserial_kernel),
+                                                     kPThreads, 0) != hipSuccess)
+        return 0;
+    if (cus <= 0 || per_cu <= 0) return 0;
+    return cus * per_cu;
+}
+
+int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
+                           void *stream) {
+    if (n_wg <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_wg), dim3(kPThreads), 0, as_stream(stream), jobs, segs,
+                       wg_seg);
+    return hipGetLastError();
+}
+
+}  // namespace bpw

@@ -1,5 +1,5 @@
 // bpw_internal.h - device-side tables shared by the host dispatcher (bpw_host.cpp) and the
-// kernels (bpw_kernels.hip). Not part of the public ABI.
+// kernels (bpw_*.hip). Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -65,7 +65,7 @@ struct SmallBatchArgs {
     float x_scales[kMaxBatch];
 };
 
-// Kernel launchers (bpw_kernels.hip). Each returns the hipError_t of its launch as int.
+// Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
 // bit-serial: workgroup w runs segments [wg_seg[w], wg_seg[w + 1]) in order
 int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
