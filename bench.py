@@ -154,16 +154,20 @@ def head_measure(bpw, torch, synth, dev, reps: int = 20) -> dict:
             "pct_hbm_peak": 100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def small_batch_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
+def small_batch_measure(bpw, torch, synth, dev, reps: int = 64) -> list[dict]:
     """Small-batch GEMM at gate/up (6912x2560) and down (2560x6912), B in 1..16; 64 rotating HBM
-    copies of the matrix (283 MB) so weights come from HBM."""
+    copies of the matrix (283 MB) so weights come from HBM. One call is a few microseconds, less
+    than the host needs to issue it, so `reps` calls (one per copy) are captured in a HIP graph and
+    the graph replay is timed: per-call time = replay time / reps (kernel plus the gap between
+    graph nodes)."""
     out = []
     for proj, rows, cols in ((4, 6912, 2560), (6, 2560, 6912)):
         case = synth.ternary_case(BASE_SEED + 7, 0, proj, rows, cols)
         hm = bpw.bpw_load(bpw.bpw_pack_i8(case.w), rows, cols, case.w_scale)
-        mats = []
+        mats, bufs = [], []
         for _ in range(64):
             buf = torch.empty(hm.nbytes, dtype=torch.uint8, device=dev)
+            bufs.append(buf)
             mats.append(bpw.bpw_upload(hm, buf))
         nbytes = hm.nbytes
         hm.free()
@@ -172,22 +176,29 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
             Xd = torch.from_numpy(X).to(dev)
             oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
             of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
-            ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(mats[0], batch), dtype=torch.uint8,
-                             device=dev)
             for i in range(3):
-                bpw.bpw_gemm_small_batch(mats[i], Xd, sc, oi, of, ws)
+                bpw.bpw_gemm_small_batch(mats[i], Xd, sc, oi, of)
             torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-            for i in range(reps):
-                ev[i][0].record()
-                bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of, ws)
-                ev[i][1].record()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for i in range(reps):
+                    bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of)
+            graph.replay()
             torch.cuda.synchronize()
-            ms = statistics.median(a.elapsed_time(b) for a, b in ev)
+            times = []
+            for _ in range(5):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                graph.replay()
+                b.record()
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) / reps)
+            ms = statistics.median(times)
+            del graph
             out.append({"shape": [rows, cols], "batch": batch, "us": round(ms * 1e3, 2),
                         "weight_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
                         "tops_equiv": round(2.0 * rows * cols * batch / (ms * 1e-3) / 1e12, 2)})
-        del mats
+        del mats, bufs
     torch.cuda.empty_cache()
     return out
 

@@ -20,7 +20,7 @@ __all__ = [
     "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
-    "bpw_gemm_small_batch_workspace_bytes", "bpw_gemm_small_batch",
+    "bpw_gemm_small_batch",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
 ]
 
@@ -210,19 +210,14 @@ class GemvPlan:
 # ------------------------------------------------------------------------------ small batch
 
 
-def bpw_gemm_small_batch_workspace_bytes(m: DevMat, batch: int) -> int:
-    return _lib.lib().bpw_gemm_small_batch_workspace_bytes(ctypes.byref(m.desc), batch)
-
-
-def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, d_ws, kernel: int = KERNEL_AUTO,
-                         stream=None) -> None:
+def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, kernel: int = KERNEL_AUTO, stream=None) -> None:
     """X int8 GPU tensor [batch, ldx]; x_scales host float32 [batch]; outputs [batch, rows]."""
     batch, ldx = X.shape
     xs = np.ascontiguousarray(np.asarray(x_scales, dtype=np.float32))
-    ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+    if xs.shape != (batch,):
+        raise ValueError(f"x_scales must hold {batch} values")
     _lib.check(_lib.lib().bpw_gemm_small_batch(ctypes.byref(m.desc), _dptr(X), batch, ldx, xs.ctypes.data,
-                                               _dptr(out_i32), _dptr(out_f32), kernel, _dptr(d_ws), ws_len,
-                                               _stream(stream)))
+                                               _dptr(out_i32), _dptr(out_f32), kernel, _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ dense head

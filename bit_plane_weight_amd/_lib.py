@@ -77,8 +77,7 @@ def lib():
         "bpw_gemv_plan_create": (i32, [J, i32, i32, vp, sz, vp, ctypes.POINTER(vp)]),
         "bpw_gemv_plan_run": (i32, [vp, vp]),
         "bpw_gemv_plan_free": (None, [vp]),
-        "bpw_gemm_small_batch_workspace_bytes": (sz, [M, i32]),
-        "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp, sz, vp]),
+        "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp]),
         "bpw_dense_head_gemv": (i32, [vp, i64, i64, vp, vp, vp]),
         "bpw_stream_read_probe": (i32, [vp, sz, vp, vp]),
         "bpw_cache_flush": (i32, [vp, sz, vp]),

@@ -53,16 +53,112 @@ __device__ __forceinline__ void write_row(const DevJob &J, int row, int32_t s) {
 
 __device__ __forceinline__ int xq_slot(int b, int i) { return b * 4 + ((i + (b >> 1)) & 3); }
 
-// Bit j of each byte of d, gathered into bits 0..3 (byte i -> bit i). After the mask the four bits
-// sit at 0, 8, 16 and 24; multiplying by 2^24 + 2^17 + 2^10 + 2^3 lands them on 24..27, and no two
-// of the sixteen shifted copies share a bit position, so nothing carries into that field.
-__device__ __forceinline__ uint32_t byte_bits(uint32_t d, int j) {
-    return (((d >> j) & 0x01010101u) * 0x01020408u) >> 24;
+// Exchange of the bit fields selected by m (in x = hi:lo) with the fields S bits above them
+// (a "delta swap"): t = (x ^ (x >> S)) & m; x ^= t ^ (t << S). Written on 32-bit halves; the 64-bit
+// shifts of the halves become funnel shifts.
+template <int S>
+__device__ __host__ __forceinline__ void delta_swap(uint32_t &lo, uint32_t &hi, uint32_t mlo, uint32_t mhi) {
+    const uint64_t x = ((uint64_t)hi << 32) | lo;
+    const uint32_t tlo = (lo ^ (uint32_t)(x >> S)) & mlo;
+    const uint32_t thi = (hi ^ (hi >> S)) & mhi;
+    const uint64_t t = ((uint64_t)thi << 32) | tlo;
+    lo ^= tlo ^ (tlo << S);
+    hi ^= thi ^ (uint32_t)(t >> (32 - S));
 }
 
-// Planes of one 16-column piece of x (the 16 bytes in v) for bit j: column k of the piece at bit k.
-__device__ __forceinline__ uint32_t piece_plane(const u32x4 &v, int j) {
-    return byte_bits(v.x, j) | (byte_bits(v.y, j) << 4) | (byte_bits(v.z, j) << 8) | (byte_bits(v.w, j) << 12);
+// 8 x 8 bit-matrix transpose of the eight bytes in hi:lo (byte i = row i, bit j = column j): after
+// it, byte j holds bit j of every input byte, input byte i at bit i. Three delta swaps at distances
+// 7, 14 and 28 exchange the off-diagonal 1x1, 2x2 and 4x4 blocks.
+__device__ __host__ __forceinline__ void transpose8x8(uint32_t &lo, uint32_t &hi) {
+    delta_swap<7>(lo, hi, 0x00AA00AAu, 0x00AA00AAu);
+    delta_swap<14>(lo, hi, 0x0000CCCCu, 0x0000CCCCu);
+    delta_swap<28>(lo, hi, 0xF0F0F0F0u, 0u);
+}
+
+// Bit planes of one 16-byte piece of x (16 consecutive int8 codes, little-endian in w0..w3):
+// plane[j] bit k = bit j of code k (j = 7 is the two's-complement sign bit).
+__device__ __host__ __forceinline__ void piece_planes(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                                      uint32_t (&plane)[8]) {
+    transpose8x8(w0, w1);  // codes 0..7
+    transpose8x8(w2, w3);  // codes 8..15
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t a = j < 4 ? w0 : w1, b = j < 4 ? w2 : w3;
+        const int sh = 8 * (j & 3);
+        plane[j] = ((a >> sh) & 0xFFu) | (((b >> sh) & 0xFFu) << 8);
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Select-accumulate core shared by the batch-1 and small-batch kernels. A row is served by
+// G = 2^glog consecutive lanes; lane g holds beats g, g+G, ... of its row and reads the activation
+// planes of those blocks from LDS (kXPassBlocks blocks, rotated as xq_slot says).
+
+// Beats b = bbase + k*G of one row: zeros past bpr, past the matrix, or for a row-group that does
+// not exist (live == false), all through offsets the buffer range check turns into zeros. The loads
+// are issued on every path, so the compiler can count them and wait for exactly the older ones.
+// NB > 0 is bpr known at compile time, which removes the bound checks that cannot fail.
+template <int K, int NB>
+__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, bool live, int bbase,
+                                          int G, int bpr) {
+    const uint32_t rowoff = row * (uint32_t)bpr;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        const int b = bbase + k * G;
+        const bool in = NB > 0 ? (b < NB) : (b < bpr);
+        const uint32_t off = (live && in) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
+        B[k] = load_beat(wr, off);
+    }
+}
+
+// The 16 plane words of block g + k*G (the block beat k of lane g covers). The index stays below
+// K * G <= kXPassBlocks, inside the LDS copy, even past the pass or past bpr: there the beat is zero
+// and the select yields zero whatever the words hold. When G is a multiple of 8 every block a lane
+// reads has the rotation of block g, so the addresses are one base plus constant offsets.
+template <int GLOG>
+__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G) {
+    const int b = g + k * G;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 w = GLOG >= 3 ? xl[g * 4 + k * (4 << GLOG) + ((i + (g >> 1)) & 3)] : xl[xq_slot(b, i)];
+        X[4 * i + 0] = w.x;
+        X[4 * i + 1] = w.y;
+        X[4 * i + 2] = w.z;
+        X[4 * i + 3] = w.w;
+    }
+}
+
+// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
+//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
+// The planes of beat k+1 are read while beat k is reduced; the empty asm statements keep the
+// compiler from hoisting every beat's reads (16 registers per beat, and the occupancy this kernel
+// relies on).
+template <int K, int GLOG>
+__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G) {
+    uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    uint32_t cn = 0;
+    uint32_t Xa[16], Xb[16];
+    read_planes<GLOG>(Xa, xl, 0, g, G);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
+        uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
+        if (k + 1 < K) read_planes<GLOG>(Xn, xl, k + 1, g, G);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
+            c[j] = __builtin_popcount(select_bits(X[2 * j + 1], B[k].y, B[k].w)) + c[j];
+        }
+        cn = __builtin_popcount(B[k].z) + cn;
+        cn = __builtin_popcount(B[k].w) + cn;
+        asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
+                     "+v"(c[7]), "+v"(cn)::"memory");
+    }
+    int32_t acc = (int32_t)cn;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
+    acc -= (int32_t)(c[7] << 7);
+    return acc;
 }
 
 static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }

@@ -35,10 +35,12 @@ __device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0,
     const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
     uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
     const int b = p >> 2, qq = p & 3;
+    uint32_t pl[8];
+    piece_planes(v.x, v.y, v.z, v.w, pl);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const int w = 2 * j + (qq >> 1);
-        xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)piece_plane(v, j);
+        xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)pl[j];
     }
 }
 
@@ -53,73 +55,6 @@ __device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0,
 // 64/G rows), holding only those K beats in registers. Each wave keeps its next row-group's loads in
 // flight while it reduces the current one. Loads past the matrix use an offset that the buffer range
 // check answers with zeros, which also covers the partial last row-group.
-
-// Beats b = bbase + k*G of one row: zeros past bpr, past the matrix, or for a row-group that does
-// not exist (live == false), all through offsets the buffer range check turns into zeros. The loads
-// are issued on every path, so the compiler can count them and wait for exactly the older ones.
-// NB > 0 is bpr known at compile time, which removes the bound checks that cannot fail.
-template <int K, int NB>
-__device__ __forceinline__ void issue_row(u32x4 (&B)[K], __amdgpu_buffer_rsrc_t wr, uint32_t row, bool live, int bbase,
-                                          int G, int bpr) {
-    const uint32_t rowoff = row * (uint32_t)bpr;
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        const int b = bbase + k * G;
-        const bool in = NB > 0 ? (b < NB) : (b < bpr);
-        const uint32_t off = (live && in) ? (rowoff + (uint32_t)b) * 16u : kOutOfRange;
-        B[k] = load_beat(wr, off);
-    }
-}
-
-// The 16 plane words of block g + k*G (the block beat k of lane g covers). The index stays below
-// K * G <= kXPassBlocks, inside the LDS copy, even past the pass or past bpr: there the beat is zero
-// and the select yields zero whatever the words hold. When G is a multiple of 8 every block a lane
-// reads has the rotation of block g, so the addresses are one base plus constant offsets.
-template <int GLOG>
-__device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, int k, int g, int G) {
-    const int b = g + k * G;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 w = GLOG >= 3 ? xl[g * 4 + k * (4 << GLOG) + ((i + (g >> 1)) & 3)] : xl[xq_slot(b, i)];
-        X[4 * i + 0] = w.x;
-        X[4 * i + 1] = w.y;
-        X[4 * i + 2] = w.z;
-        X[4 * i + 3] = w.w;
-    }
-}
-
-// Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
-//   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
-// The planes of beat k+1 are read while beat k is reduced; the empty asm statements keep the
-// compiler from hoisting every beat's reads (16 registers per beat, and the occupancy this kernel
-// relies on).
-template <int K, int GLOG>
-__device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)[K], int g, int G) {
-    uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    uint32_t cn = 0;
-    uint32_t Xa[16], Xb[16];
-    read_planes<GLOG>(Xa, xl, 0, g, G);
-#pragma unroll
-    for (int k = 0; k < K; ++k) {
-        uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
-        uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
-        if (k + 1 < K) read_planes<GLOG>(Xn, xl, k + 1, g, G);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
-            c[j] = __builtin_popcount(select_bits(X[2 * j + 1], B[k].y, B[k].w)) + c[j];
-        }
-        cn = __builtin_popcount(B[k].z) + cn;
-        cn = __builtin_popcount(B[k].w) + cn;
-        asm volatile("" : "+v"(c[0]), "+v"(c[1]), "+v"(c[2]), "+v"(c[3]), "+v"(c[4]), "+v"(c[5]), "+v"(c[6]),
-                     "+v"(c[7]), "+v"(cn)::"memory");
-    }
-    int32_t acc = (int32_t)cn;
-#pragma unroll
-    for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
-    acc -= (int32_t)(c[7] << 7);
-    return acc;
-}
 
 // Next row-group for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
 __device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {

@@ -682,14 +682,9 @@ bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, vo
     return st;
 }
 
-size_t bpw_gemm_small_batch_workspace_bytes(const bpw_dev_mat *m, int32_t batch) {
-    if (!m || batch <= 0) return 0;
-    return align_up((size_t)batch * (size_t)m->bpr * 64);
-}
-
 bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
                                 const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
-                                void *d_ws, size_t ws_len, void *stream) {
+                                void *stream) {
     bpw_status st = check_dev_mat(m, "small batch");
     if (st) return st;
     if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL)
@@ -698,40 +693,47 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
     if (!d_X || !x_scales || !d_out_i32) return fail(BPW_E_INVAL, "small batch: NULL argument");
     if (ldx < m->bpr * 64)
         return fail(BPW_E_INVAL, "ldx %lld < bpr * 64 = %lld", (long long)ldx, (long long)(m->bpr * 64));
+    if ((ldx % 16) != 0 || ((uintptr_t)d_X & 15u) != 0)
+        return fail(BPW_E_INVAL, "small batch: X rows must be 16-byte aligned (X aligned, ldx %% 16 == 0)");
     for (int32_t t = 0; t < batch; ++t)
         if (!std::isfinite(x_scales[t])) return fail(BPW_E_INVAL, "x_scales[%d] is not finite", (int)t);
-    const size_t need = bpw_gemm_small_batch_workspace_bytes(m, batch);
-    if (ws_len < need) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, need);
-    if (need && (!d_ws || ((uintptr_t)d_ws & (kAlign - 1)) != 0))
-        return fail(BPW_E_INVAL, "d_ws must be non-NULL and 256-byte aligned");
-    if (need > 160u * 1024u)
-        return fail(BPW_E_UNSUPPORTED, "batch * bpr * 64 = %zu bytes of activation planes exceed the 160 KiB LDS",
-                    need);
-    const Geometry g = geometry_for(m->bpr, false);
-    if ((uint64_t)(m->rows + g.tile_rows) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
+    const Geometry g = geometry_for(m->bpr, true);
+    if ((uint64_t)(m->rows + 64) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
         return fail(BPW_E_UNSUPPORTED, "plane bytes exceed the 32-bit offsets of one matrix");
     st = check_device();
     if (st) return st;
     if (m->rows == 0) return BPW_OK;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        return fail(BPW_E_HIP, "small batch: could not read the compute-unit count");
+    // Grid: kPWaves row-groups per workgroup; tokens split into groups only as far as needed to give
+    // every compute unit a workgroup (each group re-reads the weights, from the cache after the
+    // first), and into groups of at most kSBMaxTokens (their planes sit in LDS).
+    const int64_t rgs = units_of(m->rows, g);
+    const int64_t row_wgs = (rgs + bpw::kPWaves - 1) / bpw::kPWaves;
+    int64_t groups = std::max<int64_t>((batch + bpw::kSBMaxTokens - 1) / bpw::kSBMaxTokens, (cus + row_wgs - 1) / row_wgs);
+    groups = std::min<int64_t>(groups, batch);
+    const int64_t tg = (batch + groups - 1) / groups;
+    groups = (batch + tg - 1) / tg;
     bpw::SmallBatchArgs a{};
     a.planes = static_cast<const uint8_t *>(m->d_planes);
-    a.xplanes = static_cast<const uint32_t *>(d_ws);
+    a.X = d_X;
     a.out_i32 = d_out_i32;
     a.out_f32 = d_out_f32;
+    a.ldx = ldx;
+    a.plane_bytes = (uint32_t)((uint64_t)m->rows * (uint64_t)m->bpr * 16u);
     a.rows = (int32_t)m->rows;
     a.bpr = (int32_t)m->bpr;
     a.batch = batch;
     a.glog = g.glog;
     a.kblk = g.kblk;
     a.nchunk = g.nchunk;
-    a.tile_rows = g.tile_rows;
+    a.tg = (int32_t)tg;
     a.w_scale = m->w_scale;
     for (int32_t t = 0; t < batch; ++t) a.x_scales[t] = x_scales[t];
-    st = hip_status(bpw::launch_stage_batch(d_X, ldx, static_cast<uint32_t *>(d_ws), (int32_t)m->bpr, batch, stream),
-                    "stage launch");
-    if (st) return st;
-    const int32_t tiles = (int32_t)((m->rows + g.tile_rows - 1) / g.tile_rows);
-    return hip_status(bpw::launch_gemm_small_batch(a, tiles, stream), "small batch launch");
+    if (row_wgs > (int64_t)INT32_MAX) return fail(BPW_E_UNSUPPORTED, "small batch: too many rows for one launch");
+    return hip_status(bpw::launch_gemm_small_batch(a, (int32_t)row_wgs, (int32_t)groups, stream), "small batch launch");
 }
 
 bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t cols, const uint16_t *d_x_bf16,

@@ -53,14 +53,18 @@ struct DevTile {
     int32_t row0;
 };
 
-// Small-batch arguments (passed by value; <= 64 tokens).
+// Small-batch arguments (passed by value; <= kMaxBatch tokens).
 constexpr int kMaxBatch = 64;
+constexpr int kSBMaxTokens = 16;  // tokens whose planes one small-batch workgroup holds in LDS (128 KiB)
 struct SmallBatchArgs {
     const uint8_t *planes;
-    const uint32_t *xplanes;  // [batch][bpr][16]
+    const int8_t *X;          // [batch][ldx] int8 codes, 16-byte aligned rows
     int32_t *out_i32;         // [batch][rows]
     float *out_f32;           // [batch][rows] or null
-    int32_t rows, bpr, batch, glog, kblk, nchunk, tile_rows, pad;
+    int64_t ldx;
+    uint32_t plane_bytes;     // rows * bpr * 16 (the buffer range of the weight loads)
+    int32_t rows, bpr, batch, glog, kblk, nchunk;
+    int32_t tg;               // tokens per workgroup (<= kSBMaxTokens)
     float w_scale;
     float x_scales[kMaxBatch];
 };
@@ -73,8 +77,7 @@ int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_
 // Workgroups of the persistent bit-serial kernel that are resident at once on the current device
 // (CUs x occupancy); 0 on error.
 int32_t persistent_workgroups();
-int launch_stage_batch(const int8_t *X, int64_t ldx, uint32_t *xplanes, int32_t bpr, int32_t batch, void *stream);
-int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t n_tiles, void *stream);
+int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);
 int launch_flush(void *buf, size_t len, void *stream);

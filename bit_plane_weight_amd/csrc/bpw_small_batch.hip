@@ -1,158 +1,121 @@
-// bpw_small_batch.hip - small-batch ternary GEMM: each beat read once and applied to every token.
+// bpw_small_batch.hip - small-batch ternary GEMM on gfx950: out[t][r] = sum_c W[r][c] * X[t][c].
 //
-// Written for CDNA4 (wave64); launched only by bpw_host.cpp after its argument and architecture
-// checks.
+// The batch-1 select-accumulate (Tritium paper, introduction, Equations 2-3) applied to a few
+// tokens at once. A wave loads its row-group's beats once and reuses them for every token of its
+// token group, so the weights stream from HBM once per call whatever the batch. Written for CDNA4
+// (wave64, 160 KB LDS); launched only by bpw_host.cpp after its argument and architecture checks.
+//
+// Grid: blockIdx.x picks kPWaves consecutive row-groups (one per wave), blockIdx.y a group of up to
+// A.tg tokens. The workgroup builds its tokens' activation planes in LDS straight from X (token t of
+// the group at xl + t * kXPassBlocks * 4, the batch-1 word order and block rotation), so a call is a
+// single launch.
 #include "bpw_device.h"
 
 namespace bpw {
 
-// Small-batch activation planes: a token-major batch X [batch][ldx] -> [batch][bpr][16] words, word
-// 2j + h of a block holding bit j of its columns 32h .. 32h+31 (the batch-1 GEMV's order), one wave
-// per 64-column block (eight ballots give the eight planes).
-__global__ __launch_bounds__(kThreads) void stage_batch_kernel(const int8_t *__restrict__ X, int64_t ldx,
-                                                               uint32_t *__restrict__ xplanes, int32_t bpr,
-                                                               int32_t batch) {
-    const int item = blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (item >= bpr * batch) return;
-    const int lane = threadIdx.x & 63;
-    const int t = item / bpr, b = item - t * bpr;
-    const uint32_t xv = (uint8_t)X[(int64_t)t * ldx + (int64_t)b * 64 + lane];
-    uint32_t word = 0;
+// Planes of tokens [t0, t0 + nt), blocks [b0, b0 + nb) of X into LDS, all threads of the workgroup;
+// one 16-byte piece per lane per round. Each lane uses its load inside the branch that issued it.
+__device__ __forceinline__ void stage_tokens(u32x4 *xl, const int8_t *X, int64_t ldx, int t0, int nt, int b0,
+                                             int nb) {
+    const int per_token = nb * 4;
+    const int total = nt * per_token;
+    uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
+    for (int base = 0; base < total; base += kPThreads) {
+        const int p = base + (int)threadIdx.x;
+        if (p < total) {
+            const int t = p / per_token, pp = p - t * per_token;
+            const u32x4 v =
+                *reinterpret_cast<const u32x4 *>(X + (int64_t)(t0 + t) * ldx + (int64_t)b0 * 64 + (int64_t)pp * 16);
+            uint32_t pl[8];
+            piece_planes(v.x, v.y, v.z, v.w, pl);
+            const int b = pp >> 2, qq = pp & 3;
+            const int tbase = t * kXPassBlocks * 4;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint64_t m = __ballot((xv >> j) & 1u);
-        if ((lane >> 1) == j) word = (lane & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+            for (int j = 0; j < 8; ++j) {
+                const int w = 2 * j + (qq >> 1);
+                xh[((tbase + xq_slot(b, w >> 2)) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)pl[j];
+            }
+        }
     }
-    if (lane < 16) xplanes[((int64_t)t * bpr + b) * 16 + lane] = word;
 }
 
-// ------------------------------------------------------------------------------------------
-// Small-batch GEMM, bit-serial: each beat is loaded once and applied to every token. The batch's
-// activation planes sit in LDS ([batch][bpr][16] words); lanes of one row group read the same
-// block addresses, so reads across row groups of a wave are broadcasts.
-
-template <int K>
-__device__ __forceinline__ void gemm_sb_tile(const SmallBatchArgs &A, const uint32_t *lds, int row0, int lane,
-                                             int wave) {
-    const int glog = A.glog;
+// One wave's row-group rg for tokens [t0, t0 + nt). Rows past the matrix read zeros and store
+// nothing. Wide rows (several passes) add each pass into the output the same lane wrote before.
+template <int K, int GLOG, int NB>
+__device__ __forceinline__ void sb_rowgroup(const SmallBatchArgs &A, u32x4 *xl, int rg, int t0, int nt, int lane) {
+    const int glog = GLOG >= 0 ? GLOG : A.glog;
     const int G = 1 << glog;
     const int g = lane & (G - 1);
     const int q = lane >> glog;
     const int rpi = 64 >> glog;
-    const int bpr = A.bpr;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, (uint32_t)((uint64_t)A.rows * bpr * 16));
-    const u32x4 *lx = reinterpret_cast<const u32x4 *>(lds);
-
-    for (int it = 0; it < kIters; ++it) {
-        const int row = row0 + (it * kWaves + wave) * rpi + q;
-        for (int ch = 0; ch < A.nchunk; ++ch) {
-            const int bbase = ch * K * G + g;
-            u32x4 v[K];
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                const int b = bbase + k * G;
-                const uint32_t off = (b < bpr) ? (uint32_t)(((uint32_t)row * (uint32_t)bpr + (uint32_t)b) * 16u)
-                                               : kOutOfRange;
-                v[k] = load_beat(wr, off);
-            }
-            uint32_t cn = 0;
-#pragma unroll
-            for (int k = 0; k < K; ++k) {
-                cn = __builtin_popcount(v[k].z) + cn;
-                cn = __builtin_popcount(v[k].w) + cn;
-            }
-            for (int t = 0; t < A.batch; ++t) {
-                uint32_t c[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-                for (int k = 0; k < K; ++k) {
-                    const int b = bbase + k * G;
-                    const int bb = b < bpr ? b : 0;  // v[k] is zero past bpr, any planes give 0
-                    uint32_t X[16];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const u32x4 w = lx[((t * bpr) + bb) * 4 + i];
-                        X[4 * i + 0] = w.x;
-                        X[4 * i + 1] = w.y;
-                        X[4 * i + 2] = w.z;
-                        X[4 * i + 3] = w.w;
-                    }
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        c[j] = __builtin_popcount(select_bits(X[2 * j], v[k].x, v[k].z)) + c[j];
-                        c[j] = __builtin_popcount(select_bits(X[2 * j + 1], v[k].y, v[k].w)) + c[j];
-                    }
-                }
-                int32_t acc = (int32_t)cn;
-#pragma unroll
-                for (int j = 0; j < 7; ++j) acc += (int32_t)(c[j] << j);
-                acc -= (int32_t)(c[7] << 7);
-                const int32_t tot = group_sum(acc, glog);
-                if (g == 0 && row < A.rows) {
-                    int32_t *o = A.out_i32 + (int64_t)t * A.rows + row;
-                    const int32_t prev = (ch == 0) ? 0 : *o;
-                    const int32_t val = prev + tot;
-                    *o = val;
-                    if (ch + 1 == A.nchunk && A.out_f32) {
-                        float f = (float)val * A.x_scales[t];
-                        A.out_f32[(int64_t)t * A.rows + row] = f * A.w_scale;
-                    }
+    const int bpr = NB > 0 ? NB : A.bpr;
+    const int pass_blocks = K * G;
+    const int nchunk = NB > 0 ? 1 : A.nchunk;
+    const int row = rg * rpi + q;
+    const bool live = row < A.rows;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
+    for (int ch = 0; ch < nchunk; ++ch) {
+        const int b0 = ch * pass_blocks;
+        const int nb = min(pass_blocks, bpr - b0);
+        u32x4 B[K];
+        issue_row<K, NB>(B, wr, (uint32_t)row, live, b0 + g, G, bpr);
+        __syncthreads();  // the previous pass's planes are no longer read
+        stage_tokens(xl, A.X, A.ldx, t0, nt, b0, nb);
+        __syncthreads();
+        for (int t = 0; t < nt; ++t) {
+            const int32_t tot = group_sum(row_partial<K, GLOG>(xl + t * kXPassBlocks * 4, B, g, G), glog);
+            if (live && g == 0) {
+                const int64_t idx = (int64_t)(t0 + t) * A.rows + row;
+                const int32_t val = ch == 0 ? tot : A.out_i32[idx] + tot;
+                A.out_i32[idx] = val;
+                if (ch + 1 == nchunk && A.out_f32) {
+                    const float f = (float)val * A.x_scales[t0 + t];  // exact integer times the token's scale
+                    A.out_f32[idx] = f * A.w_scale;                  // then the weight scale
                 }
             }
         }
     }
 }
 
-__global__ __launch_bounds__(kThreads) void gemm_small_batch_kernel(SmallBatchArgs A) {
-    extern __shared__ uint32_t lds[];
-    const int words = A.batch * A.bpr * 16;
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(A.xplanes);
-    u32x4 *dst = reinterpret_cast<u32x4 *>(lds);
-    for (int i = threadIdx.x; i < words / 4; i += kThreads) dst[i] = src[i];
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int row0 = blockIdx.x * A.tile_rows;
-    switch (A.kblk) {
-        case 1: gemm_sb_tile<1>(A, lds, row0, lane, wave); break;
-        case 2: gemm_sb_tile<2>(A, lds, row0, lane, wave); break;
-        case 3: gemm_sb_tile<3>(A, lds, row0, lane, wave); break;
-        case 4: gemm_sb_tile<4>(A, lds, row0, lane, wave); break;
-        case 5: gemm_sb_tile<5>(A, lds, row0, lane, wave); break;
-        case 6: gemm_sb_tile<6>(A, lds, row0, lane, wave); break;
-        case 7: gemm_sb_tile<7>(A, lds, row0, lane, wave); break;
-        default: {
-            for (int it = 0; it < kIters; ++it) {
-                const int row = row0 + (it * kWaves + wave) * 64 + lane;
-                if (row < A.rows)
-                    for (int t = 0; t < A.batch; ++t) {
-                        A.out_i32[(int64_t)t * A.rows + row] = 0;
-                        if (A.out_f32) A.out_f32[(int64_t)t * A.rows + row] = 0.0f * A.x_scales[t] * A.w_scale;
-                    }
+__global__ __launch_bounds__(kPThreads) void gemm_small_batch_kernel(SmallBatchArgs A) {
+    extern __shared__ u32x4 xl[];  // A.tg tokens x kXPassBlocks blocks x 4 quarters
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rg = blockIdx.x * kPWaves + wave;
+    const int t0 = blockIdx.y * A.tg;
+    const int nt = min(A.tg, A.batch - t0);
+    if (A.bpr == 40) {  // 2560-column rows: 8 lanes x 5 beats
+        sb_rowgroup<5, 3, 40>(A, xl, rg, t0, nt, lane);
+    } else if (A.bpr == 108) {  // 6912-column rows: 32 lanes x 4 beats
+        sb_rowgroup<4, 5, 108>(A, xl, rg, t0, nt, lane);
+    } else if (A.kblk == 0) {  // no columns: every sum is empty (row-groups of 64 rows)
+        const int row = rg * 64 + lane;
+        if (row < A.rows)
+            for (int t = 0; t < nt; ++t) {
+                const int64_t idx = (int64_t)(t0 + t) * A.rows + row;
+                A.out_i32[idx] = 0;
+                if (A.out_f32) A.out_f32[idx] = (0.0f * A.x_scales[t0 + t]) * A.w_scale;
             }
-        }
+    } else if (A.kblk == 1) {
+        sb_rowgroup<1, -1, 0>(A, xl, rg, t0, nt, lane);
+    } else {
+        sb_rowgroup<2, -1, 0>(A, xl, rg, t0, nt, lane);
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Launchers.
+// Launcher.
 
-int launch_stage_batch(const int8_t *X, int64_t ldx, uint32_t *xplanes, int32_t bpr, int32_t batch, void *stream) {
-    const int64_t items = (int64_t)bpr * batch;
-    if (items <= 0) return hipSuccess;
-    const unsigned grid = (unsigned)((items + kWaves - 1) / kWaves);
-    hipLaunchKernelGGL(stage_batch_kernel, dim3(grid), dim3(kThreads), 0, as_stream(stream), X, ldx, xplanes, bpr,
-                       batch);
-    return hipGetLastError();
-}
-
-int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t n_tiles, void *stream) {
-    if (n_tiles <= 0) return hipSuccess;
-    const size_t lds = (size_t)a.batch * a.bpr * 64;
+int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream) {
+    if (row_wgs <= 0 || token_groups <= 0) return hipSuccess;
+    const size_t lds = (size_t)a.tg * kXPassBlocks * 64;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_small_batch_kernel),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(gemm_small_batch_kernel, dim3((unsigned)n_tiles), dim3(kThreads), lds, as_stream(stream), a);
+    hipLaunchKernelGGL(gemm_small_batch_kernel, dim3((unsigned)row_wgs, (unsigned)token_groups), dim3(kPThreads), lds,
+                       as_stream(stream), a);
     return hipGetLastError();
 }
 

@@ -182,17 +182,16 @@ void bpw_gemv_plan_free(bpw_gemv_plan *plan);
 
 /* ------------------------------------------------------------------------ small-batch GEMM */
 
-/* Device workspace bytes bpw_gemm_small_batch needs for this matrix and batch. */
-size_t bpw_gemm_small_batch_workspace_bytes(const bpw_dev_mat *m, int32_t batch);
-
-/* out[t][r] = sum_c W[r][c] * X[t][c] for t < batch, one pass over the weights: each beat is read
- * once and applied to every token. X is device int8, token-major, row t at d_X + t * ldx with
- * ldx >= bpr * 64. x_scales is a HOST float[batch]. d_out_i32 is device int32 [batch x rows];
- * d_out_f32 (device float [batch x rows], or NULL) gets ((float)acc * x_scales[t]) * w_scale.
- * 1 <= batch <= 64. With batch == 1 the results equal bpw_gemv's bit for bit. */
+/* out[t][r] = sum_c W[r][c] * X[t][c] for t < batch, one kernel launch: each beat is read from HBM once
+ * and applied to every token (tokens beyond a workgroup's group re-read it from the cache). X is
+ * device int8, token-major, row t at d_X + t * ldx with ldx >= bpr * 64, ldx % 16 == 0 and d_X
+ * 16-byte aligned (codes past cols are ignored). x_scales is a HOST float[batch]. d_out_i32 is device
+ * int32 [batch x rows]; d_out_f32 (device float [batch x rows], or NULL) gets
+ * ((float)acc * x_scales[t]) * w_scale. 1 <= batch <= 64. With batch == 1 the results equal
+ * bpw_gemv's bit for bit. Needs no workspace. */
 bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
                                 const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
-                                void *d_ws, size_t ws_len, void *stream);
+                                void *stream);
 
 /* ------------------------------------------------------------------------ dense head */
 

@@ -150,8 +150,7 @@ def test_small_batch(dev, shape, batch):
     Xd = torch.from_numpy(Xh).to(dev)
     oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
     of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
-    ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(u.m, batch), dtype=torch.uint8, device=dev)
-    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of, ws)
+    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of)
     torch.cuda.synchronize()
     acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), rows, cols, Xh, sc, case.w_scale, nthreads=NT)
     assert np.array_equal(oi.cpu().numpy(), acc)
@@ -163,6 +162,29 @@ def test_small_batch(dev, shape, batch):
         (g,) = run_grouped([case1], dev)
         assert np.array_equal(g.oi.cpu().numpy(), oi.cpu().numpy()[0])
         assert np.array_equal(g.of.cpu().numpy().view(np.uint32), of.cpu().numpy()[0].view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols,batch", ((1, 1, 1), (7, 65, 3), (65, 129, 17), (129, 2500, 64), (33, 8193, 5),
+                                             (1025, 448, 16), (5, 0, 4), (2560, 6912, 40)))
+def test_small_batch_ragged_and_wide(dev, rows, cols, batch):
+    """Ragged column tails, rows wider than one LDS pass, no columns, and batches split into several
+    token groups; ldx larger than the row and junk past cols."""
+    log(f"case: small batch {rows}x{cols} B={batch}")
+    case = synth.ternary_case(515, rows % 7, cols % 7, rows, cols)
+    u = Uploaded(case, dev)
+    bpr = (cols + 63) // 64
+    X, sc = synth.small_batch_x(516 + batch, batch, max(cols, 1))
+    ldx = bpr * 64 + 48
+    Xh = synth.u64(517, batch * ldx).astype(np.uint8).view(np.int8).reshape(batch, ldx).copy()
+    Xh[:, :cols] = X[:, :cols]
+    Xd = torch.from_numpy(Xh).to(dev)
+    oi = torch.full((batch, rows), -7, dtype=torch.int32, device=dev)
+    of = torch.full((batch, rows), -7.0, dtype=torch.float32, device=dev)
+    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of)
+    torch.cuda.synchronize()
+    acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), rows, cols, Xh, sc, case.w_scale, nthreads=NT)
+    assert np.array_equal(oi.cpu().numpy(), acc)
+    assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32))
 
 
 def test_dense_head_full_128256x2560(dev):
