@@ -22,39 +22,42 @@
 
 namespace bpw {
 
-// Planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks), built in LDS by the first
-// ceil(nb / 16) waves of the workgroup: a lane loads one 16-byte piece (piece p = block p / 4,
-// quarter p % 4) and stores its 16 bits of every plane as one 16-bit LDS write. Pieces of the last
-// wave past nb * 4 read zeros through the buffer range check and write zero planes into blocks no
-// beat of this pass selects from. The branch is uniform per wave and each wave consumes its load
-// inside it, so no load is left outstanding behind it.
+// Planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks), built in LDS by the workgroup's waves
+// in turn, 16 blocks per wave-round: a lane loads one 16-byte piece (piece p = block p / 4, quarter
+// p % 4) and stores its 16 bits of every plane as one 16-bit LDS write. Pieces of the last round
+// past nb * 4 read zeros through the buffer range check and write zero planes into blocks no beat
+// of this pass selects from. Each trip consumes its own load, so no load is left outstanding behind
+// the (wave-uniform) loop.
 __device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
-    if (wave >= (nb * 4 + 63) / 64) return;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
-    const int p = wave * 64 + lane;
-    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
+    const int need = (nb * 4 + 63) / 64;  // waves' worth of pieces
     uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
-    const int b = p >> 2, qq = p & 3;
-    uint32_t pl[8];
-    piece_planes(v.x, v.y, v.z, v.w, pl);
+    for (int wv = wave; wv < need; wv += kWaves) {
+        const int p = wv * 64 + lane;
+        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
+        const int b = p >> 2, qq = p & 3;
+        uint32_t pl[8];
+        piece_planes(v.x, v.y, v.z, v.w, pl);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int w = 2 * j + (qq >> 1);
-        xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)pl[j];
+        for (int j = 0; j < 8; ++j) {
+            const int w = 2 * j + (qq >> 1);
+            xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)pl[j];
+        }
     }
 }
 
 // ------------------------------------------------------------------------------------------
-// Batch-1 GEMV, bit-serial select, persistent. One workgroup of kPWaves waves per compute unit;
-// the host splits all jobs' row-groups over the workgroups by plane bytes into segments (runs of
-// consecutive row-groups of one job). Per segment the workgroup builds the job's activation planes
-// in LDS, then its waves claim row-groups from an LDS counter: the compute unit serves older waves
-// first, so a fixed share per wave would leave the younger ones finishing last, while claiming
-// keeps every wave busy until the segment runs out. A row is served by G = 2^glog consecutive
-// lanes; lane g reads beats g, g+G, ... of its row (one wave load = G*16 contiguous bytes of each of
-// 64/G rows), holding only those K beats in registers. Each wave keeps its next row-group's loads in
-// flight while it reduces the current one. Loads past the matrix use an offset that the buffer range
-// check answers with zeros, which also covers the partial last row-group.
+// Batch-1 grouped GEMV, bit-serial select. The host cuts every job's row-groups into tiles of
+// kTileUnits row-groups (one job each) and the grid has one workgroup of kWaves waves per tile; the
+// hardware dispatcher hands tiles to compute units as earlier ones finish, so every compute unit
+// streams until the whole list is done. Per tile the workgroup builds the job's activation planes
+// in LDS, then its waves claim row-groups from an LDS counter: a compute unit serves older waves
+// first, and claiming keeps the younger ones from being left with a fixed share to finish last. A
+// row is served by G = 2^glog consecutive lanes; lane g reads beats g, g+G, ... of its row (one wave
+// load = G*16 contiguous bytes of each of 64/G rows), holding only those K beats in registers. Each
+// wave keeps its next row-group's loads in flight while it reduces the current one. Loads past the
+// matrix use an offset that the buffer range check answers with zeros, which also covers the
+// partial last row-group.
 
 // Next row-group for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
 __device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
@@ -63,13 +66,13 @@ __device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
     return (int)__builtin_amdgcn_readfirstlane(v);
 }
 
-// Row sums collect in LDS (sums[], one slot per row of the segment) and leave in one coalesced pass
+// Row sums collect in LDS (sums[], one slot per row of the tile) and leave in one coalesced pass
 // at the end: a vector store inside the streaming loop would count against the same vector-memory
 // counter as the weight loads.
 // GLOG >= 0 and NB > 0 fix the geometry at compile time (one pass, NB == bpr); otherwise it is read
 // from the job.
 template <int K, int GLOG, int NB>
-__device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
+__device__ __forceinline__ void bs_tile(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
                                            int32_t *sums, uint32_t *claim) {
     const int glog = GLOG >= 0 ? GLOG : J.glog;
     const int G = 1 << glog;
@@ -88,7 +91,7 @@ __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int 
         int u = u0 + wave;  // every wave's first row-group is fixed; the rest are claimed
         issue_row<K, NB>(B0, wr, (uint32_t)(u * rpi + q), u < u1, bb, G, bpr);
         __syncthreads();  // every wave is done with the previous planes, sums and counter
-        if (threadIdx.x == 0) *claim = (uint32_t)(u0 + kPWaves);
+        if (threadIdx.x == 0) *claim = (uint32_t)(u0 + kWaves);
         stage_planes(xl, J.x, b0, nb, wave, lane);
         __syncthreads();
         // Two register sets alternate: the loads of the next row-group leave before the current one
@@ -117,62 +120,46 @@ __device__ __forceinline__ void bs_segment(const DevJob &J, int u0, int u1, int 
     }
     __syncthreads();
     const int row0 = u0 * rpi, n = (u1 - u0) * rpi;
-    for (int i = threadIdx.x; i < n; i += kPThreads)
+    for (int i = threadIdx.x; i < n; i += kThreads)
         if (row0 + i < J.rows) write_row(J, row0 + i, sums[i]);
 }
 
 // cols == 0: every row is the empty sum (row-groups of 64 rows).
-__device__ __forceinline__ void bs_segment_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
-    for (int u = u0 + wave; u < u1; u += kPWaves) {
+__device__ __forceinline__ void bs_tile_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
+    for (int u = u0 + wave; u < u1; u += kWaves) {
         const int row = u * 64 + lane;
         if (row < J.rows) write_row(J, row, 0);
     }
 }
 
-__global__ __launch_bounds__(kPThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
-                                                                   const Segment *__restrict__ segs,
-                                                                   const int32_t *__restrict__ wg_seg) {
+__global__ __launch_bounds__(kThreads) void gemv_bitserial_kernel(const DevJob *__restrict__ jobs,
+                                                                  const Tile *__restrict__ tiles) {
     __shared__ u32x4 xl[kXPassBlocks * 4];
-    __shared__ int32_t sums[kSegRows];
+    __shared__ int32_t sums[kTileRows];
     __shared__ uint32_t claim;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int s0 = wg_seg[blockIdx.x], s1 = wg_seg[blockIdx.x + 1];
-    for (int si = s0; si < s1; ++si) {
-        const Segment sg = segs[si];
-        const DevJob J = jobs[sg.job];
-        if (J.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
-            bs_segment<5, 3, 40>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
-        else if (J.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
-            bs_segment<4, 5, 108>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
-        else if (J.kblk == 0)
-            bs_segment_empty(J, sg.u0, sg.u1, wave, lane);
-        else if (J.kblk == 1)
-            bs_segment<1, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
-        else
-            bs_segment<2, -1, 0>(J, sg.u0, sg.u1, wave, lane, xl, sums, &claim);
-    }
+    const Tile t = tiles[blockIdx.x];
+    const DevJob J = jobs[t.job];
+    if (J.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
+        bs_tile<5, 3, 40>(J, t.u0, t.u1, wave, lane, xl, sums, &claim);
+    else if (J.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
+        bs_tile<4, 5, 108>(J, t.u0, t.u1, wave, lane, xl, sums, &claim);
+    else if (J.kblk == 0)
+        bs_tile_empty(J, t.u0, t.u1, wave, lane);
+    else if (J.kblk == 1)
+        bs_tile<1, -1, 0>(J, t.u0, t.u1, wave, lane, xl, sums, &claim);
+    else
+        bs_tile<2, -1, 0>(J, t.u0, t.u1, wave, lane, xl, sums, &claim);
 }
 
 // ------------------------------------------------------------------------------------------
 // Launchers.
 
-int32_t persistent_workgroups() {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(gemv_bitserial_kernel),
-                                                     kPThreads, 0) != hipSuccess)
-        return 0;
-    if (cus <= 0 || per_cu <= 0) return 0;
-    return cus * per_cu;
-}
-
-int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
-                           void *stream) {
-    if (n_wg <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_wg), dim3(kPThreads), 0, as_stream(stream), jobs, segs,
-                       wg_seg);
+int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream) {
+    if (n_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemv_bitserial_kernel, dim3((unsigned)n_tiles), dim3(kThreads), 0, as_stream(stream), jobs,
+                       tiles);
     return hipGetLastError();
 }
 

@@ -241,30 +241,30 @@ struct Geometry {
 // Lanes per row G = 2^glog and beats per lane K.
 // Tiled (byte-lane) kernel: the smallest power-of-two G with ceil(bpr / G) <= kKMax, capped at a
 // full wave; wider rows take passes of G * kKMax blocks.
-// Persistent (bit-serial) kernel: the two row widths of the model have compiled-in geometry
-// (2560 columns: 8 lanes x 5 beats; 6912 columns: 32 lanes x 4 beats). Other widths take the same
-// rule as above with K <= kKMaxPersistent for rows of up to kXPassBlocks blocks (one LDS pass);
-// wider rows take passes of kXPassBlocks = 64 lanes x kKMaxPersistent beats.
-Geometry geometry_for(int64_t bpr, bool persistent) {
+// Bit-serial kernels (batch-1 and small batch): the two row widths of the model have compiled-in
+// geometry (2560 columns: 8 lanes x 5 beats; 6912 columns: 32 lanes x 4 beats). Other widths take the
+// same rule as above with K <= kKMaxBitSerial for rows of up to kXPassBlocks blocks (one LDS pass);
+// wider rows take passes of kXPassBlocks = 64 lanes x kKMaxBitSerial beats.
+Geometry geometry_for(int64_t bpr, bool bitserial) {
     Geometry g{0, 0, 0, 0};
     if (bpr == 0) {
         g.tile_rows = bpw::kWaves * bpw::kIters * 64;
         return g;
     }
-    if (persistent && (bpr == 40 || bpr == 108)) {
+    if (bitserial && (bpr == 40 || bpr == 108)) {
         g.glog = bpr == 40 ? 3 : 5;
         g.kblk = bpr == 40 ? 5 : 4;
         g.nchunk = 1;
         g.tile_rows = bpw::kWaves * bpw::kIters * (int32_t)(64 >> g.glog);
         return g;
     }
-    const int kmax = persistent ? bpw::kKMaxPersistent : bpw::kKMax;
+    const int kmax = bitserial ? bpw::kKMaxBitSerial : bpw::kKMax;
     int glog = 0;
     while (glog < 6 && ((bpr + (1 << glog) - 1) >> glog) > kmax) ++glog;
     int64_t G = (int64_t)1 << glog;
     int64_t k = (bpr + G - 1) / G;
     int64_t nchunk = 1;
-    if (persistent && bpr > bpw::kXPassBlocks) {
+    if (bitserial && bpr > bpw::kXPassBlocks) {
         glog = 6;
         G = 64;
         k = bpw::kXPassBlocks / G;
@@ -280,95 +280,42 @@ Geometry geometry_for(int64_t bpr, bool persistent) {
     return g;
 }
 
-// The persistent kernel's workgroup count is bounded so workspace sizes do not depend on the device.
-constexpr int32_t kMaxPersistentWG = 8192;
-
 struct Layout {
-    size_t jobs_off, work_off, wg_off, total;
-    int64_t n_work;  // tiles (byte-lane) or segment capacity (bit-serial)
+    size_t jobs_off, work_off, total;
+    int64_t n_work;  // tiles of the selected kernel
 };
 
-// Row-groups of one job for the persistent kernel: 64/G rows each (64 rows when cols == 0).
+// Row-groups of one job for the bit-serial kernels: 64/G rows each (64 rows when cols == 0).
 inline int64_t units_of(int64_t rows, const Geometry &g) {
     const int64_t rpi = 64 >> g.glog;
     return (rows + rpi - 1) / rpi;
 }
 
+// Row-groups in one bit-serial tile of a job: kTileUnits, or fewer where kTileRows caps the rows.
+inline int64_t tile_units(const Geometry &g) {
+    return std::min<int64_t>(bpw::kTileUnits, bpw::kTileRows / (64 >> g.glog));
+}
+
+int64_t bitserial_tiles(const bpw_gemv_job &j) {
+    const Geometry g = geometry_for(j.m.bpr, true);
+    const int64_t tu = tile_units(g);
+    return (units_of(j.m.rows, g) + tu - 1) / tu;
+}
+
+int64_t bytelane_tiles(const bpw_gemv_job &j) {
+    const Geometry g = geometry_for(j.m.bpr, false);
+    return (j.m.rows + g.tile_rows - 1) / g.tile_rows;
+}
+
 Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial) {
     Layout L{};
     L.jobs_off = 0;
-    int64_t tiles = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        const Geometry g = geometry_for(jobs[i].m.bpr, false);
-        tiles += (jobs[i].m.rows + g.tile_rows - 1) / g.tile_rows;
-    }
-    // segments: one per (workgroup, job) overlap, plus one per kSegRows rows of each job
-    int64_t seg_cap = (int64_t)n + kMaxPersistentWG;
-    for (int32_t i = 0; i < n; ++i) seg_cap += jobs[i].m.rows / bpw::kSegRows + 1;
-    L.n_work = bitserial ? seg_cap : tiles;
+    L.n_work = 0;
+    for (int32_t i = 0; i < n; ++i) L.n_work += bitserial ? bitserial_tiles(jobs[i]) : bytelane_tiles(jobs[i]);
     L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
-    const size_t work_bytes =
-        bitserial ? sizeof(bpw::Segment) * (size_t)L.n_work : sizeof(bpw::DevTile) * (size_t)tiles;
-    L.wg_off = align_up(L.work_off + work_bytes);
-    L.total = align_up(L.wg_off + (bitserial ? sizeof(int32_t) * (size_t)(kMaxPersistentWG + 1) : 0));
+    const size_t tile_bytes = bitserial ? sizeof(bpw::Tile) : sizeof(bpw::DevTile);
+    L.total = align_up(L.work_off + tile_bytes * (size_t)L.n_work);
     return L;
-}
-
-// Split all jobs' row-groups over `nwg` workgroups so each streams about the same number of plane
-// bytes: workgroup w owns the row-groups whose first byte falls in [w * total / nwg,
-// (w+1) * total / nwg). Jobs with no columns (nothing to stream) go to workgroup 0.
-bool partition_units(const bpw_gemv_job *jobs, int32_t n, int64_t nwg, std::vector<bpw::Segment> &segs,
-                     std::vector<int32_t> &wg_seg) {
-    segs.clear();
-    wg_seg.assign((size_t)nwg + 1, 0);
-    int64_t total = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        const Geometry g = geometry_for(jobs[i].m.bpr, true);
-        const int64_t U = units_of(jobs[i].m.rows, g);
-        if (jobs[i].m.bpr == 0) {
-            if (U > 0) segs.push_back(bpw::Segment{i, 0, (int32_t)U, 0});
-            continue;
-        }
-        total += U * (int64_t)(64 >> g.glog) * jobs[i].m.bpr * 16;
-    }
-    int64_t w = 0, base = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        if (jobs[i].m.bpr == 0) continue;
-        const Geometry g = geometry_for(jobs[i].m.bpr, true);
-        const int64_t U = units_of(jobs[i].m.rows, g);
-        const int64_t ub = (int64_t)(64 >> g.glog) * jobs[i].m.bpr * 16;
-        int64_t u = 0;
-        while (u < U) {
-            const int64_t end_byte = (w + 1 >= nwg) ? total : (total * (w + 1)) / nwg;
-            int64_t uend = end_byte <= base ? u : std::min(U, (end_byte - base + ub - 1) / ub);
-            if (uend < u) uend = u;
-            // a segment holds at most kSegRows rows (the kernel keeps its sums in LDS)
-            const int64_t max_units = bpw::kSegRows / (64 >> g.glog);
-            while (uend > u) {
-                const int64_t e = std::min(uend, u + max_units);
-                segs.push_back(bpw::Segment{i, (int32_t)u, (int32_t)e, 0});
-                u = e;
-            }
-            if (u < U) {
-                ++w;
-                wg_seg[(size_t)w] = (int32_t)segs.size();
-            }
-        }
-        base += U * ub;
-    }
-    while (w < nwg) {
-        ++w;
-        wg_seg[(size_t)w] = (int32_t)segs.size();
-    }
-    // every job's row-groups are covered exactly once, in order
-    std::vector<int64_t> next((size_t)n, 0);
-    for (const auto &sg : segs) {
-        if (sg.u0 != next[(size_t)sg.job] || sg.u1 <= sg.u0) return false;
-        next[(size_t)sg.job] = sg.u1;
-    }
-    for (int32_t i = 0; i < n; ++i)
-        if (next[(size_t)i] != units_of(jobs[i].m.rows, geometry_for(jobs[i].m.bpr, true))) return false;
-    return wg_seg[(size_t)nwg] == (int32_t)segs.size();
 }
 
 bpw_status check_dev_mat(const bpw_dev_mat *m, const char *who) {
@@ -405,11 +352,8 @@ struct bpw_gemv_plan {
     int device;
     int32_t kernel;
     const bpw::DevJob *jobs;
-    const bpw::DevTile *tiles;     // byte-lane
-    const bpw::Segment *segs;      // bit-serial: segments, grouped by workgroup
-    const int32_t *wg_seg;         // bit-serial: per-workgroup segment offsets
+    const void *tiles;             // bpw::Tile (bit-serial) or bpw::DevTile (byte-lane), one per workgroup
     int64_t n_tiles;
-    int32_t n_wg;                  // bit-serial persistent workgroups
     int32_t has_work;
 };
 
@@ -554,7 +498,7 @@ bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *st
 
 size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs) {
     if (!jobs || n_jobs <= 0) return 0;
-    return layout_for(jobs, n_jobs, true).total;  // the bit-serial layout is the larger one
+    return std::max(layout_for(jobs, n_jobs, true).total, layout_for(jobs, n_jobs, false).total);
 }
 
 bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
@@ -581,27 +525,14 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     int dev = 0;
     (void)hipGetDevice(&dev);
 
-    int32_t n_wg = 0;
-    std::vector<bpw::Segment> segs;
-    std::vector<int32_t> wg_seg;
-    if (bitserial && n_jobs > 0) {
-        n_wg = std::min(bpw::persistent_workgroups(), kMaxPersistentWG);
-        if (n_wg <= 0) return fail(BPW_E_HIP, "could not size the persistent grid (occupancy query failed)");
-        if (!partition_units(jobs, n_jobs, n_wg, segs, wg_seg) || (int64_t)segs.size() > L.n_work)
-            return fail(BPW_E_UNSUPPORTED, "internal: row-group partition failed (%zu segments)", segs.size());
-    }
-
     auto *plan = new (std::nothrow) bpw_gemv_plan;
     if (!plan) return fail(BPW_E_INVAL, "out of host memory");
     uint8_t *ws = static_cast<uint8_t *>(d_ws);
     plan->device = dev;
     plan->kernel = kernel;
     plan->jobs = reinterpret_cast<const bpw::DevJob *>(ws + L.jobs_off);
-    plan->tiles = reinterpret_cast<const bpw::DevTile *>(ws + L.work_off);
-    plan->segs = reinterpret_cast<const bpw::Segment *>(ws + L.work_off);
-    plan->wg_seg = reinterpret_cast<const int32_t *>(ws + L.wg_off);
-    plan->n_tiles = bitserial ? 0 : L.n_work;
-    plan->n_wg = n_wg;
+    plan->tiles = ws + L.work_off;
+    plan->n_tiles = L.n_work;
     plan->has_work = 0;
     if (n_jobs == 0) {
         *out = plan;
@@ -612,6 +543,7 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     std::vector<uint8_t> host(table_bytes, 0);
     auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
     auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
+    auto *hb = reinterpret_cast<bpw::Tile *>(host.data() + L.work_off);
     int64_t t = 0;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const bpw_gemv_job &j = jobs[i];
@@ -631,13 +563,18 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         d.tile_rows = g.tile_rows;
         d.plane_bytes = (uint32_t)((uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u);
         hj[i] = d;
-        if (!bitserial)
+        if (!bitserial) {
             for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
+        } else {
+            // tiles of one job in row order; jobs in the order given
+            const int64_t U = units_of(j.m.rows, g), tu = tile_units(g);
+            for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
+        }
         if (j.m.rows > 0) plan->has_work = 1;
     }
-    if (bitserial) {
-        std::memcpy(host.data() + L.work_off, segs.data(), segs.size() * sizeof(bpw::Segment));
-        std::memcpy(host.data() + L.wg_off, wg_seg.data(), wg_seg.size() * sizeof(int32_t));
+    if (t != L.n_work) {
+        delete plan;
+        return fail(BPW_E_UNSUPPORTED, "internal: %lld tiles written, %lld expected", (long long)t, (long long)L.n_work);
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
@@ -663,9 +600,11 @@ bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream) {
     if (st) return st;
     if (!plan->has_work) return BPW_OK;
     if (plan->kernel == BPW_KERNEL_BYTELANE)
-        return hip_status(bpw::launch_gemv_tiles(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
+        return hip_status(bpw::launch_gemv_tiles(plan->jobs, static_cast<const bpw::DevTile *>(plan->tiles),
+                                                 (int32_t)plan->n_tiles, stream),
                           "gemv launch");
-    return hip_status(bpw::launch_gemv_persistent(plan->jobs, plan->segs, plan->wg_seg, plan->n_wg, stream),
+    return hip_status(bpw::launch_gemv_bitserial(plan->jobs, static_cast<const bpw::Tile *>(plan->tiles),
+                                                 (int32_t)plan->n_tiles, stream),
                       "gemv launch");
 }
 
@@ -707,11 +646,11 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         cus <= 0)
         return fail(BPW_E_HIP, "small batch: could not read the compute-unit count");
-    // Grid: kPWaves row-groups per workgroup; tokens split into groups only as far as needed to give
+    // Grid: kSBWaves row-groups per workgroup; tokens split into groups only as far as needed to give
     // every compute unit a workgroup (each group re-reads the weights, from the cache after the
     // first), and into groups of at most kSBMaxTokens (their planes sit in LDS).
     const int64_t rgs = units_of(m->rows, g);
-    const int64_t row_wgs = (rgs + bpw::kPWaves - 1) / bpw::kPWaves;
+    const int64_t row_wgs = (rgs + bpw::kSBWaves - 1) / bpw::kSBWaves;
     int64_t groups = std::max<int64_t>((batch + bpw::kSBMaxTokens - 1) / bpw::kSBMaxTokens, (cus + row_wgs - 1) / row_wgs);
     groups = std::min<int64_t>(groups, batch);
     const int64_t tg = (batch + groups - 1) / groups;

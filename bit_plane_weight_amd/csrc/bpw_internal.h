@@ -11,14 +11,14 @@ namespace bpw {
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // wave64
 constexpr int kKMax = 7;                  // 64-column blocks one lane handles per pass (tiled byte-lane kernel)
-constexpr int kKMaxPersistent = 2;        // beats one lane holds per row-group (persistent bit-serial kernel,
+constexpr int kKMaxBitSerial = 2;         // beats one lane holds per row-group (bit-serial kernels,
                                           // shapes other than 2560 and 6912 columns)
-constexpr int kPWaves = 16;               // waves of the persistent GEMV workgroup (one workgroup per CU)
-constexpr int kPThreads = 64 * kPWaves;
+constexpr int kSBWaves = 16;              // waves of a small-batch workgroup (one row-group each)
+constexpr int kSBThreads = 64 * kSBWaves;
 constexpr int kXPassBlocks = 128;         // activation-plane blocks held in LDS per pass (8 KiB)
-static_assert(kXPassBlocks == 64 * kKMaxPersistent, "a wide row's pass is one full wave of lanes x kKMaxPersistent");
-static_assert(kXPassBlocks * 4 <= kPThreads, "one lane per 16-byte piece stages a whole pass");
-constexpr int kSegRows = 4096;            // rows of one persistent-kernel segment (its sums sit in LDS)
+static_assert(kXPassBlocks == 64 * kKMaxBitSerial, "a wide row's pass is one full wave of lanes x kKMaxBitSerial");
+constexpr int kTileRows = 1024;           // most rows of one bit-serial GEMV tile (its sums sit in LDS)
+constexpr int kTileUnits = 16;            // row-groups of one bit-serial GEMV tile (fewer at a job's end)
 constexpr int kIters = 4;                 // row-iterations per wave per tile
 
 // One GEMV of a grouped launch, as the kernels read it (lives in the caller's workspace).
@@ -39,9 +39,9 @@ struct DevJob {
     int32_t pad;
 };
 
-// A run of consecutive row-groups ("units" of 64 / G rows) of one job, run by one workgroup of the
-// persistent bit-serial kernel. Units [u0, u1), at most kSegRows rows.
-struct Segment {
+// A tile of the bit-serial GEMV: consecutive row-groups ("units" of 64 / G rows) [u0, u1) of one
+// job, at most kTileRows rows, run by one workgroup.
+struct Tile {
     int32_t job;
     int32_t u0;
     int32_t u1;
@@ -71,12 +71,8 @@ struct SmallBatchArgs {
 
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
-// bit-serial: workgroup w runs segments [wg_seg[w], wg_seg[w + 1]) in order
-int launch_gemv_persistent(const DevJob *jobs, const Segment *segs, const int32_t *wg_seg, int32_t n_wg,
-                           void *stream);
-// Workgroups of the persistent bit-serial kernel that are resident at once on the current device
-// (CUs x occupancy); 0 on error.
-int32_t persistent_workgroups();
+// bit-serial: workgroup w runs tiles[w]
+int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);

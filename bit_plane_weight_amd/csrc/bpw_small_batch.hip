@@ -5,7 +5,7 @@
 // token group, so the weights stream from HBM once per call whatever the batch. Written for CDNA4
 // (wave64, 160 KB LDS); launched only by bpw_host.cpp after its argument and architecture checks.
 //
-// Grid: blockIdx.x picks kPWaves consecutive row-groups (one per wave), blockIdx.y a group of up to
+// Grid: blockIdx.x picks kSBWaves consecutive row-groups (one per wave), blockIdx.y a group of up to
 // A.tg tokens. The workgroup builds its tokens' activation planes in LDS straight from X (token t of
 // the group at xl + t * kXPassBlocks * 4, the batch-1 word order and block rotation), so a call is a
 // single launch.
@@ -20,7 +20,7 @@ __device__ __forceinline__ void stage_tokens(u32x4 *xl, const int8_t *X, int64_t
     const int per_token = nb * 4;
     const int total = nt * per_token;
     uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
-    for (int base = 0; base < total; base += kPThreads) {
+    for (int base = 0; base < total; base += kSBThreads) {
         const int p = base + (int)threadIdx.x;
         if (p < total) {
             const int t = p / per_token, pp = p - t * per_token;
@@ -77,11 +77,11 @@ __device__ __forceinline__ void sb_rowgroup(const SmallBatchArgs &A, u32x4 *xl, 
     }
 }
 
-__global__ __launch_bounds__(kPThreads) void gemm_small_batch_kernel(SmallBatchArgs A) {
+__global__ __launch_bounds__(kSBThreads) void gemm_small_batch_kernel(SmallBatchArgs A) {
     extern __shared__ u32x4 xl[];  // A.tg tokens x kXPassBlocks blocks x 4 quarters
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int rg = blockIdx.x * kPWaves + wave;
+    const int rg = blockIdx.x * kSBWaves + wave;
     const int t0 = blockIdx.y * A.tg;
     const int nt = min(A.tg, A.batch - t0);
     if (A.bpr == 40) {  // 2560-column rows: 8 lanes x 5 beats
@@ -114,7 +114,7 @@ int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t to
                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(gemm_small_batch_kernel, dim3((unsigned)row_wgs, (unsigned)token_groups), dim3(kPThreads), lds,
+    hipLaunchKernelGGL(gemm_small_batch_kernel, dim3((unsigned)row_wgs, (unsigned)token_groups), dim3(kSBThreads), lds,
                        as_stream(stream), a);
     return hipGetLastError();
 }
