@@ -158,7 +158,7 @@ def head_measure(bpw, torch, synth, dev, reps: int = 20) -> dict:
             "pct_hbm_peak": 100.0 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
-def small_batch_measure(bpw, torch, synth, dev, reps: int = 64) -> list[dict]:
+def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0) -> list[dict]:
     """Small-batch GEMM at gate/up (6912x2560) and down (2560x6912), B in 1..16; 64 rotating HBM
     copies of the matrix (283 MB) so weights come from HBM. One call is a few microseconds, less
     than the host needs to issue it, so `reps` calls (one per copy) are captured in a HIP graph and
@@ -181,12 +181,12 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64) -> list[dict]:
             oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
             of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
             for i in range(3):
-                bpw.bpw_gemm_small_batch(mats[i], Xd, sc, oi, of)
+                bpw.bpw_gemm_small_batch(mats[i], Xd, sc, oi, of, kernel)
             torch.cuda.synchronize()
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 for i in range(reps):
-                    bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of)
+                    bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of, kernel)
             graph.replay()
             torch.cuda.synchronize()
             times = []
@@ -391,7 +391,8 @@ def main() -> int:
         log("zero-density sweep")
         result["z_sweep"] = z_sweep_measure(bpw, torch, synth, dev)
         log("small batch")
-        result["small_batch"] = small_batch_measure(bpw, torch, synth, dev)
+        result["small_batch"] = small_batch_measure(bpw, torch, synth, dev)  # auto: the matrix-core kernel
+        result["small_batch_bitserial"] = small_batch_measure(bpw, torch, synth, dev, kernel=bpw.KERNEL_BITSERIAL)
 
     print(json.dumps(result), flush=True)
     return 0

@@ -13,10 +13,10 @@ import numpy as np
 
 from . import _lib
 from ._lib import (BpwDevMat, BpwError, BpwGemvJob, KERNEL_AUTO, KERNEL_BITSERIAL,  # noqa: F401
-                   KERNEL_BYTELANE)
+                   KERNEL_BYTELANE, KERNEL_MFMA)
 
 __all__ = [
-    "BpwError", "KERNEL_AUTO", "KERNEL_BITSERIAL", "KERNEL_BYTELANE",
+    "BpwError", "KERNEL_AUTO", "KERNEL_BITSERIAL", "KERNEL_BYTELANE", "KERNEL_MFMA",
     "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",

@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(_HERE, "libbpw.so")
 # bpw_status
 OK, E_INVAL, E_SIZE, E_P1_BOTH_BITS, E_P2_PADDING, E_NOT_VALIDATED, E_ARCH, E_HIP, E_UNSUPPORTED = range(9)
 # bpw_kernel
-KERNEL_AUTO, KERNEL_BITSERIAL, KERNEL_BYTELANE = 0, 1, 2
+KERNEL_AUTO, KERNEL_BITSERIAL, KERNEL_BYTELANE, KERNEL_MFMA = 0, 1, 2, 3
 ABI_VERSION = 1
 
 

@@ -63,6 +63,7 @@ struct SmallBatchArgs {
     float *out_f32;           // [batch][rows] or null
     int64_t ldx;
     uint32_t plane_bytes;     // rows * bpr * 16 (the buffer range of the weight loads)
+    uint32_t x_bytes;         // batch * ldx (the buffer range of the activation loads)
     int32_t rows, bpr, batch, glog, kblk, nchunk;
     int32_t tg;               // tokens per workgroup (<= kSBMaxTokens)
     float w_scale;
@@ -74,6 +75,7 @@ int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles,
 // bit-serial: workgroup w runs tiles[w]
 int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
+int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);
 int launch_flush(void *buf, size_t len, void *stream);

@@ -104,7 +104,140 @@ __global__ __launch_bounds__(kSBThreads) void gemm_small_batch_kernel(SmallBatch
 }
 
 // ------------------------------------------------------------------------------------------
+// Small batch on the matrix cores: v_mfma_i32_16x16x64_i8 multiplies 16 rows x 64 columns of int8
+// weights by 64 columns x 16 tokens of int8 activations into 16 x 16 int32 sums. The planes are
+// decoded to int8 weights once per beat, whatever the batch. Decoding goes through a 256-entry LDS
+// table: entry (p | n << 4) holds the four weights of a nibble pair of the planes (byte k = +1 if
+// bit k of p, -1 if bit k of n, else 0; P1 rules out both).
+//
+// A workgroup owns 16 rows x up to 16 tokens; its waves (4, or 8 for rows of more than 64 blocks)
+// split the row's beats (iteration i covers blocks 4i .. 4i+3, wave w takes i = w, w + waves, ...),
+// and the partial sums meet in LDS. In one iteration lane l holds the beat of row l % 16, block 4i + l / 16, and for each
+// quarter m of that block the 16 activation bytes of token l % 16 at the same columns: the
+// instruction pairs byte j of lane l's weights with byte j of the activations of lanes with the
+// same l / 16, so both operands only have to agree on the column order, which they do. Result lane
+// l, register r holds row 4 * (l / 16) + r, token l % 16.
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRows = 16;    // rows per workgroup
+constexpr int kMfmaTokens = 16;  // tokens per workgroup
+
+__device__ __forceinline__ uint32_t lut_entry(uint32_t idx) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if ((idx >> k) & 1u)
+            w |= 0x01u << (8 * k);
+        else if ((idx >> (4 + k)) & 1u)
+            w |= 0xFFu << (8 * k);
+    }
+    return w;
+}
+
+// Weights of columns 16m .. 16m+15 of a beat as the 16 int8 bytes of one operand. e and o hold the
+// table indices of the even and odd nibbles of the beat's 32-bit half that contains them.
+__device__ __forceinline__ v4i decode_quarter(const uint32_t *lut, uint32_t e, uint32_t o, int m) {
+    const int sh = 16 * (m & 1);
+    v4i a;
+    a.x = (int)lut[(e >> sh) & 0xFFu];        // columns 16m + 0..3
+    a.y = (int)lut[(o >> sh) & 0xFFu];        // 4..7
+    a.z = (int)lut[(e >> (sh + 8)) & 0xFFu];  // 8..11
+    a.w = (int)lut[(o >> (sh + 8)) & 0xFFu];  // 12..15
+    return a;
+}
+
+// Loads of one iteration: the beat of (row, block b) and the four 16-byte activation pieces of
+// token tok at block b. Past the matrix, past bpr or past the batch they read zeros through the
+// buffer range checks; they are issued on every path so the compiler counts them exactly.
+__device__ __forceinline__ void mfma_issue(u32x4 &beat, u32x4 (&xv)[4], __amdgpu_buffer_rsrc_t wr,
+                                           __amdgpu_buffer_rsrc_t xr, uint32_t row, uint32_t tok, int b, int bpr,
+                                           int64_t ldx, bool live) {
+    const bool in = live && b < bpr;
+    beat = load_beat(wr, in ? (row * (uint32_t)bpr + (uint32_t)b) * 16u : kOutOfRange);
+    const uint32_t xo = (uint32_t)((int64_t)tok * ldx + (int64_t)b * 64);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        xv[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? xo + 16u * m : kOutOfRange, 0, 0));
+}
+
+// One iteration's four products: the beat's nibble-pair table indices (e: even nibbles, o: odd
+// nibbles of each 32-bit half, byte k = p nibble | n nibble << 4), then one instruction per quarter.
+__device__ __forceinline__ v4i mfma_beat(const uint32_t *lut, const u32x4 &beat, const u32x4 (&xv)[4], v4i acc) {
+    const uint32_t elo = (beat.x & 0x0F0F0F0Fu) | ((beat.z << 4) & 0xF0F0F0F0u);
+    const uint32_t olo = ((beat.x >> 4) & 0x0F0F0F0Fu) | (beat.z & 0xF0F0F0F0u);
+    const uint32_t ehi = (beat.y & 0x0F0F0F0Fu) | ((beat.w << 4) & 0xF0F0F0F0u);
+    const uint32_t ohi = ((beat.y >> 4) & 0x0F0F0F0Fu) | (beat.w & 0xF0F0F0F0u);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_quarter(lut, m < 2 ? elo : ehi, m < 2 ? olo : ohi, m),
+                                                    __builtin_bit_cast(v4i, xv[m]), acc, 0, 0, 0);
+    return acc;
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(SmallBatchArgs A) {
+    static_assert(64 * WAVES >= 256, "every thread of the first four waves fills one table entry");
+    __shared__ uint32_t lut[256];
+    __shared__ v4i part[WAVES][64];
+    if (threadIdx.x < 256) lut[threadIdx.x] = lut_entry(threadIdx.x);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t row = blockIdx.x * kMfmaRows + (lane & 15);
+    const uint32_t tok = blockIdx.y * kMfmaTokens + (lane & 15);
+    const int bq = lane >> 4;  // which block of the iteration's four this lane holds
+    const int bpr = A.bpr;
+    const int n_it = (bpr + 3) / 4;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(A.X, A.x_bytes);
+    __syncthreads();  // the table is complete
+    v4i acc = {0, 0, 0, 0};
+    u32x4 beat0, beat1, x0[4], x1[4];
+    int it = wave;
+    mfma_issue(beat0, x0, wr, xr, row, tok, 4 * it + bq, bpr, A.ldx, it < n_it);
+    // Two load sets alternate, as in the batch-1 kernel: iteration it + WAVES is in flight while
+    // iteration it is multiplied; one trip covers two iterations with no exit in between.
+    for (; it < n_it; it += 2 * WAVES) {
+        mfma_issue(beat1, x1, wr, xr, row, tok, 4 * (it + WAVES) + bq, bpr, A.ldx, it + WAVES < n_it);
+        asm volatile("" ::: "memory");
+        acc = mfma_beat(lut, beat0, x0, acc);
+        mfma_issue(beat0, x0, wr, xr, row, tok, 4 * (it + 2 * WAVES) + bq, bpr, A.ldx, it + 2 * WAVES < n_it);
+        asm volatile("" ::: "memory");
+        acc = mfma_beat(lut, beat1, x1, acc);
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (threadIdx.x >= 256) return;
+    // thread t < 256 sums register t / 64 of lane t % 64 over the waves (exact) and stores it
+    const int l = threadIdx.x & 63, r = threadIdx.x >> 6;
+    int32_t sum = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += part[w][l][r];
+    const int orow = blockIdx.x * kMfmaRows + 4 * (l >> 4) + r;
+    const int otok = blockIdx.y * kMfmaTokens + (l & 15);
+    if (orow < A.rows && otok < A.batch) {
+        const int64_t idx = (int64_t)otok * A.rows + orow;
+        A.out_i32[idx] = sum;
+        if (A.out_f32) {
+            const float f = (float)sum * A.x_scales[otok];  // exact integer times the token's scale
+            A.out_f32[idx] = f * A.w_scale;                  // then the weight scale
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Launcher.
+
+int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream) {
+    const unsigned row_wgs = (unsigned)((a.rows + kMfmaRows - 1) / kMfmaRows);
+    const unsigned groups = (unsigned)((a.batch + kMfmaTokens - 1) / kMfmaTokens);
+    if (row_wgs == 0 || groups == 0) return hipSuccess;
+    if (a.bpr > 64)
+        hipLaunchKernelGGL(gemm_small_batch_mfma_kernel<8>, dim3(row_wgs, groups), dim3(512), 0, as_stream(stream), a);
+    else
+        hipLaunchKernelGGL(gemm_small_batch_mfma_kernel<4>, dim3(row_wgs, groups), dim3(256), 0, as_stream(stream), a);
+    return hipGetLastError();
+}
 
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream) {
     if (row_wgs <= 0 || token_groups <= 0) return hipSuccess;

@@ -98,8 +98,10 @@ typedef enum bpw_kernel {
     BPW_KERNEL_AUTO = 0,      /* the fastest measured formulation (bit-serial) */
     BPW_KERNEL_BITSERIAL = 1, /* x split into bit planes; per plane one 3-input bit select + popcount
                                  (Tritium paper, "On popcount": the adder-tree formulation) */
-    BPW_KERNEL_BYTELANE = 2   /* each 4-bit mask group widened to byte lanes, then 4-way int8 dot
+    BPW_KERNEL_BYTELANE = 2,  /* each 4-bit mask group widened to byte lanes, then 4-way int8 dot
                                  products (the masked-byte formulation of format page section 1) */
+    BPW_KERNEL_MFMA = 3       /* small batch only: planes decoded to int8 weights once per beat, then
+                                 16 rows x 64 columns x 16 tokens per v_mfma_i32_16x16x64_i8 */
 } bpw_kernel;
 
 /* ------------------------------------------------------------------------ library */
@@ -185,10 +187,12 @@ void bpw_gemv_plan_free(bpw_gemv_plan *plan);
 /* out[t][r] = sum_c W[r][c] * X[t][c] for t < batch, one kernel launch: each beat is read from HBM once
  * and applied to every token (tokens beyond a workgroup's group re-read it from the cache). X is
  * device int8, token-major, row t at d_X + t * ldx with ldx >= bpr * 64, ldx % 16 == 0 and d_X
- * 16-byte aligned (codes past cols are ignored). x_scales is a HOST float[batch]. d_out_i32 is device
- * int32 [batch x rows]; d_out_f32 (device float [batch x rows], or NULL) gets
- * ((float)acc * x_scales[t]) * w_scale. 1 <= batch <= 64. With batch == 1 the results equal
- * bpw_gemv's bit for bit. Needs no workspace. */
+ * 16-byte aligned (codes past cols are ignored); (batch + 16) * ldx must stay below 2^32 bytes.
+ * x_scales is a HOST float[batch]. d_out_i32 is device int32 [batch x rows]; d_out_f32 (device float
+ * [batch x rows], or NULL) gets ((float)acc * x_scales[t]) * w_scale. 1 <= batch <= 64. kernel:
+ * BPW_KERNEL_BITSERIAL (select per token), BPW_KERNEL_MFMA (int8 matrix cores), or BPW_KERNEL_AUTO
+ * (the faster measured one for the batch); BPW_KERNEL_BYTELANE is refused. Every kernel gives the
+ * same integers; with batch == 1 they equal bpw_gemv's bit for bit. Needs no workspace. */
 bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
                                 const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
                                 void *stream);

@@ -135,11 +135,15 @@ def test_zero_density_sweep_layer(dev, z):
         check_case(u, oracle_ref(u.case), f"{u.case.name} z={z}")
 
 
+SB_KERNELS = (bpw.KERNEL_BITSERIAL, bpw.KERNEL_MFMA)
+
+
+@pytest.mark.parametrize("kernel", SB_KERNELS)
 @pytest.mark.parametrize("batch", (1, 2, 3, 4, 8, 16))
 @pytest.mark.parametrize("shape", ((6912, 2560), (2560, 6912)))
-def test_small_batch(dev, shape, batch):
+def test_small_batch(dev, shape, batch, kernel):
     rows, cols = shape
-    log(f"case: small batch {rows}x{cols} B={batch}")
+    log(f"case: small batch {rows}x{cols} B={batch} kernel={kernel}")
     case = synth.ternary_case(505, 0, 4 if rows == 6912 else 6, rows, cols)
     u = Uploaded(case, dev)
     bpr = (cols + 63) // 64
@@ -150,7 +154,7 @@ def test_small_batch(dev, shape, batch):
     Xd = torch.from_numpy(Xh).to(dev)
     oi = torch.empty((batch, rows), dtype=torch.int32, device=dev)
     of = torch.empty((batch, rows), dtype=torch.float32, device=dev)
-    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of)
+    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of, kernel)
     torch.cuda.synchronize()
     acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), rows, cols, Xh, sc, case.w_scale, nthreads=NT)
     assert np.array_equal(oi.cpu().numpy(), acc)
@@ -164,12 +168,13 @@ def test_small_batch(dev, shape, batch):
         assert np.array_equal(g.of.cpu().numpy().view(np.uint32), of.cpu().numpy()[0].view(np.uint32))
 
 
+@pytest.mark.parametrize("kernel", SB_KERNELS + (bpw.KERNEL_AUTO,))
 @pytest.mark.parametrize("rows,cols,batch", ((1, 1, 1), (7, 65, 3), (65, 129, 17), (129, 2500, 64), (33, 8193, 5),
-                                             (1025, 448, 16), (5, 0, 4), (2560, 6912, 40)))
-def test_small_batch_ragged_and_wide(dev, rows, cols, batch):
+                                             (1025, 448, 16), (5, 0, 4), (2560, 6912, 40), (17, 320, 33)))
+def test_small_batch_ragged_and_wide(dev, rows, cols, batch, kernel):
     """Ragged column tails, rows wider than one LDS pass, no columns, and batches split into several
     token groups; ldx larger than the row and junk past cols."""
-    log(f"case: small batch {rows}x{cols} B={batch}")
+    log(f"case: small batch {rows}x{cols} B={batch} kernel={kernel}")
     case = synth.ternary_case(515, rows % 7, cols % 7, rows, cols)
     u = Uploaded(case, dev)
     bpr = (cols + 63) // 64
@@ -180,7 +185,7 @@ def test_small_batch_ragged_and_wide(dev, rows, cols, batch):
     Xd = torch.from_numpy(Xh).to(dev)
     oi = torch.full((batch, rows), -7, dtype=torch.int32, device=dev)
     of = torch.full((batch, rows), -7.0, dtype=torch.float32, device=dev)
-    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of)
+    bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi, of, kernel)
     torch.cuda.synchronize()
     acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), rows, cols, Xh, sc, case.w_scale, nthreads=NT)
     assert np.array_equal(oi.cpu().numpy(), acc)
