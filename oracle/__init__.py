@@ -40,7 +40,7 @@ def build(force: bool = True) -> str:
         tmp = _SO + ".tmp"
         subprocess.run(
             ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-             "-fno-fast-math", "-o", tmp, _SRC],
+             "-fno-fast-math", "-o", tmp, _SRC, "-lm"],
             check=True,
         )
         os.replace(tmp, _SO)
@@ -71,8 +71,9 @@ def _load():
         lib.oracle_gemv_bitserial.argtypes = [vp, i64, i64, i64, vp, i64, vp, ci, ep]
         lib.oracle_gemm_small_batch.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, f32, vp, vp, vp, ci, ep]
         lib.oracle_dense_head.argtypes = [vp, i64, i64, vp, vp, vp, ci]
+        lib.oracle_quantize.argtypes = [vp, vp, i64, f32, ci, vp, vp]
         for f in ("oracle_pack", "oracle_validate", "oracle_unpack", "oracle_gemv",
-                  "oracle_gemv_bitserial", "oracle_gemm_small_batch", "oracle_dense_head"):
+                  "oracle_gemv_bitserial", "oracle_gemm_small_batch", "oracle_dense_head", "oracle_quantize"):
             getattr(lib, f).restype = ci
         _lib = lib
     return _lib
@@ -177,3 +178,17 @@ def dense_head(w_bf16: np.ndarray, x_bf16: np.ndarray, nthreads=1):
     if rc != OK:
         raise OracleError(rc, -1, -1, -1)
     return y, s
+
+
+def quantize(h: np.ndarray, g: np.ndarray, eps: float, folded: bool) -> tuple[np.ndarray, float]:
+    """Activation codes and scale of the Reference (folded=False) or Folded (folded=True) mode:
+    int8[n] codes and the float32 scale (see oracle_quantize in oracle.c)."""
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    g = np.ascontiguousarray(g, dtype=np.float32)
+    assert h.shape == g.shape and h.ndim == 1
+    q = np.empty(h.size, dtype=np.int8)
+    s = np.zeros(1, dtype=np.float32)
+    rc = _load().oracle_quantize(_p(h), _p(g), h.size, float(eps), int(bool(folded)), _p(q), _p(s))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    return q, float(s[0])

@@ -32,6 +32,7 @@
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+#include <math.h>
 
 enum {
     OR_OK = 0,
@@ -324,5 +325,59 @@ int oracle_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint1
         y[v] = acc;
         if (s) s[v] = mag;
     }
+    return OR_OK;
+}
+
+/*
+ * Activation quantisation in front of a matvec ([TP] "Numerics": the Reference and Folded modes).
+ * h is the float32 residual stream [n], g the float32 RMS-norm gain [n]; eps the norm's epsilon
+ * (the pages give none; callers pass it).
+ *
+ *   rms = sqrt(sum_i h_i^2 / n + eps), the sum and the root in float64 over i in order.
+ *
+ * Reference (folded == 0): the norm is materialised, y_i = (h_i / (float)rms) * g_i in float32;
+ *   then the absmax code of y: m = max_i |y_i|, q_i = rint((127 * y_i) / m) (float32, ties to even),
+ *   scale = m / 127 (float32).
+ * Folded (folded == 1): the per-element divide leaves. Absmax codes do not change when every input
+ *   is scaled by one positive number, and y = u / rms with u_i = h_i * g_i, so the codes are taken
+ *   from u directly and the rms survives only in the per-token scale:
+ *   m = max_i |u_i|, q_i = rint((127 * u_i) / m) (float32), scale = (float)((m / 127) / rms) in float64.
+ * m == 0 gives all-zero codes and scale 0. In exact arithmetic the two modes give the same codes
+ * and scales; in floating point a code may differ by one where the value sits at a rounding tie.
+ */
+static double oracle_rms(const float *h, int64_t n, float eps) {
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; ++i) ss += (double)h[i] * (double)h[i];
+    return sqrt(ss / (double)n + (double)eps);
+}
+
+static int8_t oracle_code(float v, float m) {
+    float t = (127.0f * v) / m;
+    float r = rintf(t);
+    if (r > 127.0f) r = 127.0f;
+    if (r < -127.0f) r = -127.0f;
+    return (int8_t)r;
+}
+
+int oracle_quantize(const float *h, const float *g, int64_t n, float eps, int folded, int8_t *q, float *scale) {
+    if (n <= 0 || !h || !g || !q || !scale || !(eps >= 0.0f)) return OR_E_INVAL;
+    const double rms = oracle_rms(h, n, eps);
+    float *v = (float *)malloc((size_t)n * sizeof(float));
+    if (!v) return OR_E_INVAL;
+    const float rms32 = (float)rms;
+    for (int64_t i = 0; i < n; ++i) v[i] = folded ? h[i] * g[i] : (h[i] / rms32) * g[i];
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > m) m = a;
+    }
+    if (m == 0.0f) {
+        memset(q, 0, (size_t)n);
+        *scale = 0.0f;
+    } else {
+        for (int64_t i = 0; i < n; ++i) q[i] = oracle_code(v[i], m);
+        *scale = folded ? (float)(((double)m / 127.0) / rms) : m / 127.0f;
+    }
+    free(v);
     return OR_OK;
 }

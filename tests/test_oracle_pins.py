@@ -335,3 +335,82 @@ def test_dequant_applies_scales_in_turn():
     t = (acc.astype(np.float64) * np.float64(np.float32(case.x_scale))).astype(np.float32)
     y = (t.astype(np.float64) * np.float64(np.float32(case.w_scale))).astype(np.float32)
     assert np.array_equal(y32, y)
+
+
+# ----------------------------------------------------------------------------- activation quantisation
+# [TP] "Numerics": Folded mode takes absmax codes from h * g and moves 1/rms into the per-token scale.
+
+
+def _residual(seed, n, spread=3.0):
+    h = synth.normal_f32(seed, n) * np.float32(spread)
+    g = (np.float32(0.5) + synth.uniform(seed + 1, n).astype(np.float32))
+    return h.astype(np.float32), g.astype(np.float32)
+
+
+@pytest.mark.parametrize("n", (1, 7, 64, 2560, 6912, 8193))
+def test_folded_codes_equal_reference_codes_up_to_ties(n):
+    """In exact arithmetic both modes give the same codes (absmax codes are invariant under the
+    uniform positive scale 1/rms) and the same scale; in float32 a code may move by one at a tie."""
+    total = mismatched = 0
+    for seed in range(20):
+        h, g = _residual(9000 + 17 * seed + n, n, spread=10.0 ** ((seed % 7) - 3))
+        qr, sr = oracle.quantize(h, g, 1e-5, folded=False)
+        qf, sf = oracle.quantize(h, g, 1e-5, folded=True)
+        d = qr.astype(np.int32) - qf.astype(np.int32)
+        assert np.all(np.abs(d) <= 1)
+        total += n
+        mismatched += int(np.count_nonzero(d))
+        assert abs(sr - sf) <= 4e-7 * abs(sf)
+    assert mismatched <= max(1, total // 500)
+
+
+@pytest.mark.parametrize("k", (-12, -3, 1, 5, 20))
+def test_quantize_power_of_two_scaling(k):
+    """Scaling h by 2^k (eps = 0) changes nothing; scaling g by 2^k scales the Folded scale by 2^k.
+    Power-of-two factors commute with every rounding involved, so the equalities are exact."""
+    h, g = _residual(77, 2560)
+    f = np.float32(2.0 ** k)
+    for folded in (False, True):
+        q0, s0 = oracle.quantize(h, g, 0.0, folded)
+        q1, s1 = oracle.quantize(h * f, g, 0.0, folded)
+        assert np.array_equal(q0, q1) and s0 == s1
+    q0, s0 = oracle.quantize(h, g, 0.0, True)
+    q2, s2 = oracle.quantize(h, g * f, 0.0, True)
+    assert np.array_equal(q0, q2) and s2 == np.float32(s0 * f)
+
+
+def test_quantize_closed_forms():
+    n = 2560
+    # one non-zero entry: code +-127 there, 0 elsewhere; Folded scale (|c|/127)/(|c|/sqrt(n)) = sqrt(n)/127
+    for c in (3.5, -0.25, 1e-3):
+        h = np.zeros(n, np.float32)
+        h[123] = c
+        g = np.ones(n, np.float32)
+        q, s = oracle.quantize(h, g, 0.0, True)
+        assert q[123] == (127 if c > 0 else -127) and np.count_nonzero(q) == 1
+        assert s == np.float32(np.sqrt(n) / 127.0)
+    # constant input: every code 127 * sign(c); Folded scale 1/127
+    for c in (2.0, -5.0):
+        q, s = oracle.quantize(np.full(n, c, np.float32), np.ones(n, np.float32), 0.0, True)
+        assert np.all(q == (127 if c > 0 else -127)) and s == np.float32(1.0 / 127.0)
+    # a negative gain flips every code; zeros give zero codes and scale
+    h, g = _residual(5, n)
+    qa, sa = oracle.quantize(h, g, 1e-5, True)
+    qb, sb = oracle.quantize(h, -g, 1e-5, True)
+    assert np.array_equal(qa, -qb) and sa == sb
+    q, s = oracle.quantize(np.zeros(n, np.float32), g, 1e-5, True)
+    assert not q.any() and s == 0.0
+
+
+def test_quantize_codes_against_exact_rationals():
+    """Each Folded code is the float32 rounding of 127 u / m; checked against the exact rational
+    value: the code is within 1/2 + (float32 error) of it, and equals it at exactly representable
+    ratios."""
+    from fractions import Fraction
+    h, g = _residual(31, 300)
+    q, s = oracle.quantize(h, g, 1e-5, True)
+    u = [Fraction(float(np.float32(a) * np.float32(b))) for a, b in zip(h, g)]
+    m = max(abs(x) for x in u)
+    for code, x in zip(q.tolist(), u):
+        exact = 127 * x / m
+        assert abs(Fraction(code) - exact) <= Fraction(1, 2) + Fraction(1, 1 << 16)
