@@ -12,7 +12,7 @@ import ctypes
 import numpy as np
 
 from . import _lib
-from ._lib import (BpwDevMat, BpwError, BpwGemvJob, KERNEL_AUTO, KERNEL_BITSERIAL,  # noqa: F401
+from ._lib import (BpwDevMat, BpwError, BpwGemvJob, BpwQuantJob, KERNEL_AUTO, KERNEL_BITSERIAL,  # noqa: F401
                    KERNEL_BYTELANE, KERNEL_MFMA)
 
 __all__ = [
@@ -20,7 +20,7 @@ __all__ = [
     "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
-    "bpw_gemm_small_batch",
+    "bpw_gemm_small_batch", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
 ]
 
@@ -153,8 +153,9 @@ def bpw_upload(m: HostMat, d_buf, stream=None) -> DevMat:
 # ------------------------------------------------------------------------------ batch-1 GEMV
 
 
-def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None) -> BpwGemvJob:
-    """One bpw_gemv_job: x int8 GPU tensor (>= bpr * 64 bytes), outputs int32 / float32 [rows]."""
+def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None, x_scale_dev=None) -> BpwGemvJob:
+    """One bpw_gemv_job: x int8 GPU tensor (>= bpr * 64 bytes), outputs int32 / float32 [rows].
+    x_scale_dev (a float32 GPU tensor of one element) makes the kernel read the scale there."""
     j = BpwGemvJob()
     j.m = m.desc
     j.d_x = _dptr(x)
@@ -162,6 +163,7 @@ def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None) -> BpwGemvJob:
     j.x_scale = float(x_scale)
     j.d_out_i32 = _dptr(out_i32)
     j.d_out_f32 = _dptr(out_f32)
+    j.d_x_scale = _dptr(x_scale_dev)
     return j
 
 
@@ -198,6 +200,62 @@ class GemvPlan:
     def free(self) -> None:
         if self._h:
             _lib.lib().bpw_gemv_plan_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------ quantiser
+
+
+def quant_job(h, g, q, scale, eps: float) -> BpwQuantJob:
+    """One bpw_quant_job: h, g float32 GPU tensors [n]; q int8 GPU tensor (>= n); scale float32 [1]."""
+    j = BpwQuantJob()
+    j.d_h, j.d_g = _dptr(h), _dptr(g)
+    j.n = h.numel()
+    if g.numel() != j.n:
+        raise ValueError("h and g must have the same length")
+    j.d_q, j.q_len = _dptr(q), q.numel()
+    j.d_scale = _dptr(scale)
+    j.eps = float(eps)
+    return j
+
+
+def _quant_array(jobs):
+    arr = (BpwQuantJob * max(1, len(jobs)))(*jobs)
+    return arr, len(jobs)
+
+
+def bpw_quantize_workspace_bytes(n_jobs: int) -> int:
+    return _lib.lib().bpw_quantize_workspace_bytes(n_jobs)
+
+
+def bpw_quantize(jobs, d_ws, stream=None) -> None:
+    arr, n = _quant_array(jobs)
+    ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+    _lib.check(_lib.lib().bpw_quantize(arr, n, _dptr(d_ws), ws_len, _stream(stream)))
+
+
+class QuantPlan:
+    """bpw_quant_plan: the quantiser's job table written once into d_ws; run() queues one launch."""
+
+    def __init__(self, jobs, d_ws, stream=None):
+        arr, n = _quant_array(jobs)
+        ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().bpw_quant_plan_create(arr, n, _dptr(d_ws), ws_len, _stream(stream), ctypes.byref(h)))
+        self._h, self._keep = h, (jobs, d_ws)
+
+    def run(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_quant_plan_run(self._h, _stream(stream)))
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_quant_plan_free(self._h)
             self._h = ctypes.c_void_p(None)
 
     def __del__(self):

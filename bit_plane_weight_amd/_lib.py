@@ -29,7 +29,13 @@ class BpwDevMat(ctypes.Structure):
 class BpwGemvJob(ctypes.Structure):
     _fields_ = [("m", BpwDevMat), ("d_x", ctypes.c_void_p), ("x_len", ctypes.c_int64),
                 ("x_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
-                ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p)]
+                ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p), ("d_x_scale", ctypes.c_void_p)]
+
+
+class BpwQuantJob(ctypes.Structure):
+    _fields_ = [("d_h", ctypes.c_void_p), ("d_g", ctypes.c_void_p), ("n", ctypes.c_int64),
+                ("d_q", ctypes.c_void_p), ("q_len", ctypes.c_int64), ("d_scale", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("reserved", ctypes.c_uint32)]
 
 
 class BpwError(RuntimeError):
@@ -61,6 +67,7 @@ def lib():
     E = ctypes.POINTER(BpwErr)
     M = ctypes.POINTER(BpwDevMat)
     J = ctypes.POINTER(BpwGemvJob)
+    Q = ctypes.POINTER(BpwQuantJob)
     sig = {
         "bpw_abi_version": (i32, []),
         "bpw_status_string": (ctypes.c_char_p, [i32]),
@@ -78,6 +85,11 @@ def lib():
         "bpw_gemv_plan_run": (i32, [vp, vp]),
         "bpw_gemv_plan_free": (None, [vp]),
         "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp]),
+        "bpw_quantize_workspace_bytes": (sz, [i32]),
+        "bpw_quantize": (i32, [Q, i32, vp, sz, vp]),
+        "bpw_quant_plan_create": (i32, [Q, i32, vp, sz, vp, ctypes.POINTER(vp)]),
+        "bpw_quant_plan_run": (i32, [vp, vp]),
+        "bpw_quant_plan_free": (None, [vp]),
         "bpw_dense_head_gemv": (i32, [vp, i64, i64, vp, vp, vp]),
         "bpw_stream_read_probe": (i32, [vp, sz, vp, vp]),
         "bpw_cache_flush": (i32, [vp, sz, vp]),

@@ -73,13 +73,13 @@ __device__ __forceinline__ void gemv_bytelane_tile(const DevJob &J, int row0, in
             const int32_t tot = group_sum(s[it], glog);
             if (g == 0 && row < J.rows) {
                 if (J.nchunk == 1) {
-                    write_row(J, row, tot);
+                    write_row(J, job_x_scale(J), row, tot);
                 } else {
                     const int32_t prev = (ch == 0) ? 0 : J.out_i32[row];
                     if (ch + 1 < J.nchunk)
                         J.out_i32[row] = prev + tot;
                     else
-                        write_row(J, row, prev + tot);
+                        write_row(J, job_x_scale(J), row, prev + tot);
                 }
             }
         }
@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bytelane_kernel(const DevJob *_
         default: {
             for (int it = 0; it < kIters; ++it) {
                 const int row = tile.row0 + (it * kWaves + wave) * 64 + lane;
-                if (row < J.rows) write_row(J, row, 0);
+                if (row < J.rows) write_row(J, job_x_scale(J), row, 0);
             }
         }
     }

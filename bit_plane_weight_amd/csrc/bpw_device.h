@@ -38,13 +38,16 @@ __device__ __forceinline__ int32_t group_sum(int32_t s, int glog) {
     return s;
 }
 
-__device__ __forceinline__ void write_row(const DevJob &J, int row, int32_t s) {
+__device__ __forceinline__ void write_row(const DevJob &J, float x_scale, int row, int32_t s) {
     J.out_i32[row] = s;
     if (J.out_f32) {
-        float t = (float)s * J.x_scale;  // exact integer (|s| < 2^24) times the activation scale
+        float t = (float)s * x_scale;   // exact integer (|s| < 2^24) times the activation scale
         J.out_f32[row] = t * J.w_scale;  // then the weight scale, each product rounded on its own
     }
 }
+
+// The job's activation scale: from device memory when the job names a location, else the table.
+__device__ __forceinline__ float job_x_scale(const DevJob &J) { return J.x_scale_ptr ? *J.x_scale_ptr : J.x_scale; }
 
 // ------------------------------------------------------------------------------------------
 // Activation bit planes. Block b of x (64 int8 codes) becomes 16 words: word 2j + h holds bit j of

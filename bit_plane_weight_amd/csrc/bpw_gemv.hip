@@ -119,16 +119,17 @@ __device__ __forceinline__ void bs_tile(const DevJob &J, int u0, int u1, int wav
         }
     }
     __syncthreads();
+    const float xs = job_x_scale(J);
     const int row0 = u0 * rpi, n = (u1 - u0) * rpi;
     for (int i = threadIdx.x; i < n; i += kThreads)
-        if (row0 + i < J.rows) write_row(J, row0 + i, sums[i]);
+        if (row0 + i < J.rows) write_row(J, xs, row0 + i, sums[i]);
 }
 
 // cols == 0: every row is the empty sum (row-groups of 64 rows).
 __device__ __forceinline__ void bs_tile_empty(const DevJob &J, int u0, int u1, int wave, int lane) {
     for (int u = u0 + wave; u < u1; u += kWaves) {
         const int row = u * 64 + lane;
-        if (row < J.rows) write_row(J, row, 0);
+        if (row < J.rows) write_row(J, job_x_scale(J), row, 0);
     }
 }
 

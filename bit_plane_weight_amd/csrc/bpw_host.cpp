@@ -556,6 +556,7 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
         d.rows = (int32_t)j.m.rows;
         d.bpr = (int32_t)j.m.bpr;
         d.x_scale = j.x_scale;
+        d.x_scale_ptr = j.d_x_scale;
         d.w_scale = j.m.w_scale;
         d.glog = g.glog;
         d.kblk = g.kblk;
@@ -618,6 +619,77 @@ bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, vo
     if (st) return st;
     st = bpw_gemv_plan_run(plan, stream);
     bpw_gemv_plan_free(plan);
+    return st;
+}
+
+struct bpw_quant_plan {
+    int device;
+    const bpw::QuantJob *jobs;
+    int32_t n_jobs;
+};
+
+size_t bpw_quantize_workspace_bytes(int32_t n_jobs) {
+    return n_jobs > 0 ? align_up(sizeof(bpw::QuantJob) * (size_t)n_jobs) : 0;
+}
+
+bpw_status bpw_quant_plan_create(const bpw_quant_job *jobs, int32_t n_jobs, void *d_ws, size_t ws_len, void *stream,
+                                 bpw_quant_plan **out) {
+    if (!out) return fail(BPW_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad quantiser job list");
+    std::vector<bpw::QuantJob> table((size_t)n_jobs);
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        const bpw_quant_job &j = jobs[i];
+        if (!j.d_h || !j.d_g || !j.d_q || !j.d_scale)
+            return fail(BPW_E_INVAL, "quantiser job %d: NULL pointer", (int)i);
+        if (j.n < 1 || j.q_len < j.n) return fail(BPW_E_INVAL, "quantiser job %d: need 1 <= n <= q_len", (int)i);
+        if (!std::isfinite(j.eps) || j.eps < 0.0f)
+            return fail(BPW_E_INVAL, "quantiser job %d: eps must be finite and >= 0", (int)i);
+        table[(size_t)i] = bpw::QuantJob{j.d_h, j.d_g, j.d_q, j.d_scale, j.n, j.q_len, j.eps, 0};
+    }
+    const size_t need = bpw_quantize_workspace_bytes(n_jobs);
+    if (ws_len < need) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, need);
+    if (need && (!d_ws || ((uintptr_t)d_ws & (kAlign - 1)) != 0))
+        return fail(BPW_E_INVAL, "d_ws must be non-NULL and 256-byte aligned");
+    bpw_status st = check_device();
+    if (st) return st;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (need) {
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        st = hip_status(hipMemcpyAsync(d_ws, table.data(), sizeof(bpw::QuantJob) * table.size(), hipMemcpyHostToDevice, s),
+                        "hipMemcpyAsync");
+        if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
+        if (st) return st;
+    }
+    auto *plan = new (std::nothrow) bpw_quant_plan;
+    if (!plan) return fail(BPW_E_INVAL, "out of host memory");
+    plan->device = dev;
+    plan->jobs = static_cast<const bpw::QuantJob *>(d_ws);
+    plan->n_jobs = n_jobs;
+    *out = plan;
+    return BPW_OK;
+}
+
+bpw_status bpw_quant_plan_run(const bpw_quant_plan *plan, void *stream) {
+    if (!plan) return fail(BPW_E_INVAL, "plan is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+        return fail(BPW_E_INVAL, "plan was created on device %d, current device is %d", plan->device, dev);
+    bpw_status st = check_device();
+    if (st) return st;
+    return hip_status(bpw::launch_quantize(plan->jobs, plan->n_jobs, stream), "quantiser launch");
+}
+
+void bpw_quant_plan_free(bpw_quant_plan *plan) { delete plan; }
+
+bpw_status bpw_quantize(const bpw_quant_job *jobs, int32_t n_jobs, void *d_ws, size_t ws_len, void *stream) {
+    if (n_jobs == 0) return BPW_OK;
+    bpw_quant_plan *plan = nullptr;
+    bpw_status st = bpw_quant_plan_create(jobs, n_jobs, d_ws, ws_len, stream, &plan);
+    if (st) return st;
+    st = bpw_quant_plan_run(plan, stream);
+    bpw_quant_plan_free(plan);
     return st;
 }
 

@@ -31,6 +31,7 @@ struct DevJob {
     int32_t bpr;
     float x_scale;
     float w_scale;
+    const float *x_scale_ptr;  // if set, the activation scale is read from here (x_scale ignored)
     int32_t glog;           // log2 of lanes per row (G)
     int32_t kblk;           // blocks per lane per pass (<= kKMax; 0 when cols == 0)
     int32_t nchunk;         // passes over the row: bpr <= G * kblk * nchunk
@@ -70,6 +71,18 @@ struct SmallBatchArgs {
     float x_scales[kMaxBatch];
 };
 
+// One activation of the Folded quantiser (lives in the caller's workspace).
+struct QuantJob {
+    const float *h;
+    const float *g;
+    int8_t *q;
+    float *scale;
+    int64_t n;
+    int64_t q_len;
+    float eps;
+    int32_t pad;
+};
+
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
 // bit-serial: workgroup w runs tiles[w]
@@ -77,6 +90,7 @@ int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
+int launch_quantize(const QuantJob *jobs, int32_t n_jobs, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);
 int launch_flush(void *buf, size_t len, void *stream);
 

@@ -91,6 +91,8 @@ typedef struct bpw_gemv_job {
     uint32_t reserved;
     int32_t *d_out_i32;   /* device int32 [rows]: exact sums */
     float *d_out_f32;     /* device float [rows]: ((float)acc * x_scale) * w_scale, or NULL */
+    const float *d_x_scale; /* device float [1] or NULL: if set, the scale is read from here when the
+                               kernel runs (for example written by bpw_quantize) and x_scale is ignored */
 } bpw_gemv_job;
 
 /* Inner-loop formulation, pinned by name; a pinned kernel that cannot serve the call errors. */
@@ -181,6 +183,42 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
 bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream);
 
 void bpw_gemv_plan_free(bpw_gemv_plan *plan);
+
+/* ------------------------------------------------------------------------ activation quantiser */
+
+/* One activation to quantise in the Folded mode ("Tritium ...", "Numerics"): int8 codes are taken
+ * from u = h * g (the residual stream times the RMS-norm gain) and 1/rms moves into the scale:
+ *   m = max |u_i|, q_i = rint((127 * u_i) / m) in float32 (ties to even),
+ *   scale = (float)((m / 127) / sqrt(sum_i h_i^2 / n + eps)) with the sum and root in float64.
+ * In exact arithmetic these are the codes and scale of quantising the materialised norm
+ * (h / rms) * g; the scale is what a GEMV epilogue multiplies by (bpw_gemv_job.d_x_scale). */
+typedef struct bpw_quant_job {
+    const float *d_h;     /* device float [n]: residual stream */
+    const float *d_g;     /* device float [n]: RMS-norm gain */
+    int64_t n;            /* elements, >= 1 */
+    int8_t *d_q;          /* device int8 [q_len]: codes; bytes n .. q_len-1 are written 0 */
+    int64_t q_len;        /* >= n */
+    float *d_scale;       /* device float [1]: the scale */
+    float eps;            /* the norm's epsilon, finite and >= 0 */
+    uint32_t reserved;
+} bpw_quant_job;
+
+/* Device workspace bytes bpw_quantize / bpw_quant_plan_create need for n_jobs jobs. */
+size_t bpw_quantize_workspace_bytes(int32_t n_jobs);
+
+/* Quantise n_jobs activations, one launch on `stream`. The job table is copied into d_ws
+ * (256-byte aligned, ws_len >= bpw_quantize_workspace_bytes); the call waits for that copy.
+ * n_jobs == 0 does nothing. Jobs must not write overlapping outputs. */
+bpw_status bpw_quantize(const bpw_quant_job *jobs, int32_t n_jobs, void *d_ws, size_t ws_len, void *stream);
+
+typedef struct bpw_quant_plan bpw_quant_plan;
+
+/* The job table written once into d_ws (which, with the jobs' buffers, must outlive the plan);
+ * each run is one launch that reads the inputs as they are when it executes. */
+bpw_status bpw_quant_plan_create(const bpw_quant_job *jobs, int32_t n_jobs, void *d_ws, size_t ws_len,
+                                 void *stream, bpw_quant_plan **out);
+bpw_status bpw_quant_plan_run(const bpw_quant_plan *plan, void *stream);
+void bpw_quant_plan_free(bpw_quant_plan *plan);
 
 /* ------------------------------------------------------------------------ small-batch GEMM */
 

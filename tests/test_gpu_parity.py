@@ -355,3 +355,95 @@ def test_probe_and_flush_run(dev):
     torch.cuda.synchronize()
     assert int(sink.item()) == 0
     assert int(buf.sum().item()) == 0
+
+
+# ----------------------------------------------------------------------------- Folded quantiser
+
+
+def _hg(seed, n, spread):
+    h = (synth.normal_f32(seed, n) * np.float32(spread)).astype(np.float32)
+    g = (np.float32(0.5) + synth.uniform(seed + 1, n).astype(np.float32)).astype(np.float32)
+    return h, g
+
+
+@pytest.mark.parametrize("n,spread", ((1, 1.0), (7, 1e-3), (64, 10.0), (2560, 1.0), (2560, 1e4), (6912, 0.5),
+                                      (8193, 3.0), (100000, 1.0)))
+def test_quantize_folded_parity(dev, n, spread):
+    log(f"case: quantiser n={n} spread={spread}")
+    h, g = _hg(3131 + n, n, spread)
+    q_len = ((n + 63) // 64) * 64 + 64
+    hd, gd = torch.from_numpy(h).to(dev), torch.from_numpy(g).to(dev)
+    qd = torch.full((q_len,), 55, dtype=torch.int8, device=dev)
+    sd = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(bpw.bpw_quantize_workspace_bytes(1), 1), dtype=torch.uint8, device=dev)
+    bpw.bpw_quantize([bpw.quant_job(hd, gd, qd, sd, 1e-5)], ws)
+    torch.cuda.synchronize()
+    q, s = oracle.quantize(h, g, 1e-5, folded=True)
+    got = qd.cpu().numpy()
+    assert np.array_equal(got[:n], q)
+    assert not got[n:].any()
+    gs = float(sd.item())
+    assert abs(gs - s) <= abs(s) * 2.0 ** -23  # the float64 sum of squares may differ in its last bits
+
+
+def test_quantize_zero_and_errors(dev):
+    log("case: quantiser zeros and argument errors")
+    n = 300
+    hd = torch.zeros(n, dtype=torch.float32, device=dev)
+    gd = torch.ones(n, dtype=torch.float32, device=dev)
+    qd = torch.full((n,), 9, dtype=torch.int8, device=dev)
+    sd = torch.full((1,), 1.0, dtype=torch.float32, device=dev)
+    ws = torch.empty(bpw.bpw_quantize_workspace_bytes(1), dtype=torch.uint8, device=dev)
+    bpw.bpw_quantize([bpw.quant_job(hd, gd, qd, sd, 1e-5)], ws)
+    torch.cuda.synchronize()
+    assert not qd.cpu().numpy().any() and float(sd.item()) == 0.0
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_quantize([bpw.quant_job(hd, gd, qd[:10], sd, 1e-5)], ws)
+    assert ei.value.status == _lib.E_INVAL
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_quantize([bpw.quant_job(hd, gd, qd, sd, float("nan"))], ws)
+    assert ei.value.status == _lib.E_INVAL
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.bpw_quantize([bpw.quant_job(hd, gd, qd, sd, 1e-5)], ws[:8])
+    assert ei.value.status == _lib.E_SIZE
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_quantise_then_gemv_layer(dev, kernel):
+    """A layer's seven projections fed by the Folded quantiser: codes and scales stay on the device
+    (the GEMV reads each scale when it runs); two runs of the plans with new residuals."""
+    log(f"case: quantiser -> grouped GEMV, kernel={kernel}")
+    cases = synth.layer_cases(4242, 0)
+    ups, qjobs, keep = [], [], []
+    for i, c in enumerate(cases):
+        u = Uploaded(c, dev)
+        sd = torch.zeros(1, dtype=torch.float32, device=dev)
+        hd = torch.empty(c.cols, dtype=torch.float32, device=dev)
+        gd = torch.empty(c.cols, dtype=torch.float32, device=dev)
+        u.sd, u.hd, u.gd = sd, hd, gd
+        qjobs.append(bpw.quant_job(hd, gd, u.x, sd, 1e-5))
+        ups.append(u)
+    qws = torch.empty(bpw.bpw_quantize_workspace_bytes(len(qjobs)), dtype=torch.uint8, device=dev)
+    qplan = bpw.QuantPlan(qjobs, qws)
+    jobs = [bpw.gemv_job(u.m, u.x, 0.0, u.oi, u.of, x_scale_dev=u.sd) for u in ups]
+    ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+    plan = bpw.GemvPlan(jobs, ws, kernel)
+    for rep in range(2):
+        hs = []
+        for i, u in enumerate(ups):
+            h, g = _hg(5000 + 10 * rep + i, u.case.cols, 2.0 + rep)
+            u.hd.copy_(torch.from_numpy(h))
+            u.gd.copy_(torch.from_numpy(g))
+            hs.append((h, g))
+        qplan.run()
+        plan.run()
+        torch.cuda.synchronize()
+        for u, (h, g) in zip(ups, hs):
+            q, s = oracle.quantize(h, g, 1e-5, folded=True)
+            acc, y32, y64 = oracle.gemv(oracle.pack(u.case.w), u.case.rows, u.case.cols, q, s, u.case.w_scale,
+                                        nthreads=NT)
+            assert np.array_equal(u.oi.cpu().numpy(), acc)
+            gf = u.of.cpu().numpy().astype(np.float64)
+            assert np.all(np.abs(gf - y64) <= 1e-6 * np.abs(y64))
+    plan.free()
+    qplan.free()
