@@ -91,6 +91,7 @@ class DecodeSet:
             jobs = [bpw.gemv_job(m, x, s, oi, of) for m, (x, s), (oi, of) in zip(mats, xs, outs)]
             ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
             self.copies.append((bpw.GemvPlan(jobs, ws), mats, ws))
+        self.shapes = shapes
         for hm in host_mats:
             hm.free()
         self.xs, self.outs = xs, outs
@@ -113,6 +114,51 @@ def time_steps(torch, dset, steps: int) -> tuple[float, float]:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return a.elapsed_time(b) / steps, wall * 1e3 / steps
+
+
+def prologue_measure(bpw, torch, synth, dev, ds, steps: int = 100) -> dict:
+    """The decode step with its activation prep: the Folded quantiser turns each job's float32
+    residual h and gain g (seeded: h ~ N(0, 1), g ~ U(0.5, 1.5)) into the job's int8 codes and a
+    device-resident scale, then the grouped GEMV reads both. One quantiser launch (210 jobs) plus one
+    GEMV launch per step, timed back to back between HIP events."""
+    import numpy as np
+    qjobs, scales, keep = [], [], []
+    for i, ((layer, proj, name, rows, cols), (x, _)) in enumerate(zip(ds.shapes, ds.xs)):
+        h = torch.from_numpy(synth.normal_f32(BASE_SEED + 31 * i + 1, cols)).to(dev)
+        g = torch.from_numpy((np.float32(0.5) + synth.uniform(BASE_SEED + 31 * i + 2, cols)).astype(np.float32)).to(dev)
+        sd = torch.zeros(1, dtype=torch.float32, device=dev)
+        qjobs.append(bpw.quant_job(h, g, x, sd, 1e-5))
+        scales.append(sd)
+        keep += [h, g]
+    qws = torch.empty(bpw.bpw_quantize_workspace_bytes(len(qjobs)), dtype=torch.uint8, device=dev)
+    qplan = bpw.QuantPlan(qjobs, qws)
+    plans = []
+    for plan, mats, _ in ds.copies:
+        jobs = [bpw.gemv_job(m, x, 0.0, oi, of, x_scale_dev=sd)
+                for m, (x, _), (oi, of), sd in zip(mats, ds.xs, ds.outs, scales)]
+        ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+        plans.append((bpw.GemvPlan(jobs, ws), ws))
+    for i in range(5):
+        qplan.run()
+        plans[i % len(plans)][0].run()
+    torch.cuda.synchronize()
+    a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    a.record()
+    for i in range(steps):
+        qplan.run()
+    b.record()
+    for i in range(steps):
+        qplan.run()
+        plans[i % len(plans)][0].run()
+    c.record()
+    torch.cuda.synchronize()
+    q_us = a.elapsed_time(b) / steps * 1e3
+    step_us = b.elapsed_time(c) / steps * 1e3
+    for p, _ in plans:
+        p.free()
+    qplan.free()
+    return {"quantise_us": round(q_us, 2), "decode_step_with_quantise_us": round(step_us, 2),
+            "quantised_values": int(sum(c[4] for c in ds.shapes))}
 
 
 def probe_gbs(bpw, torch, dev) -> float:
@@ -377,6 +423,8 @@ def main() -> int:
 
     # ---------------------------------------------------------------- companion measurements
     if not args.no_extras:
+        log("quantiser prologue")
+        result["prologue"] = prologue_measure(bpw, torch, synth, dev, ds)
         del ds
         torch.cuda.empty_cache()
         log("probe")
