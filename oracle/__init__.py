@@ -72,8 +72,10 @@ def _load():
         lib.oracle_gemm_small_batch.argtypes = [vp, i64, i64, i64, vp, i64, i64, vp, f32, vp, vp, vp, ci, ep]
         lib.oracle_dense_head.argtypes = [vp, i64, i64, vp, vp, vp, ci]
         lib.oracle_quantize.argtypes = [vp, vp, i64, f32, ci, vp, vp]
+        lib.oracle_intmlp.argtypes = [vp, vp, i64, i64, i64, vp, i64, f32, f32, f32, vp, vp, vp, vp, ci, ep]
         for f in ("oracle_pack", "oracle_validate", "oracle_unpack", "oracle_gemv",
-                  "oracle_gemv_bitserial", "oracle_gemm_small_batch", "oracle_dense_head", "oracle_quantize"):
+                  "oracle_gemv_bitserial", "oracle_gemm_small_batch", "oracle_dense_head", "oracle_quantize",
+                  "oracle_intmlp"):
             getattr(lib, f).restype = ci
         _lib = lib
     return _lib
@@ -192,3 +194,22 @@ def quantize(h: np.ndarray, g: np.ndarray, eps: float, folded: bool) -> tuple[np
     if rc != OK:
         raise OracleError(rc, -1, -1, -1)
     return q, float(s[0])
+
+
+def intmlp(gate_planes, up_planes, rows, cols, x, x_scale, w_gate, w_up, nthreads=1):
+    """IntMlp epilogue of a gate/up pair sharing x (see oracle_intmlp in oracle.c): returns
+    (t int64[rows] = relu(a_g)^2 * a_u, K float64 = S_g^2 * S_u, a_g int32[rows], a_u int32[rows])."""
+    g = np.ascontiguousarray(gate_planes, dtype=np.uint8)
+    u = np.ascontiguousarray(up_planes, dtype=np.uint8)
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    if g.size != u.size:
+        raise OracleError(E_SIZE, -1, -1, -1)
+    t = np.empty(max(rows, 1), dtype=np.int64)[:rows]
+    k = np.zeros(1, dtype=np.float64)
+    ag = np.empty(max(rows, 1), dtype=np.int32)[:rows]
+    au = np.empty(max(rows, 1), dtype=np.int32)[:rows]
+    err = _Err()
+    rc = _load().oracle_intmlp(_p(g), _p(u), g.size, rows, cols, _p(x), x.size, float(x_scale), float(w_gate),
+                               float(w_up), _p(t), _p(k), _p(ag), _p(au), int(nthreads), ctypes.byref(err))
+    _check(rc, err)
+    return t, float(k[0]), ag, au

@@ -10,7 +10,8 @@
  *   [TP] "Tritium: One Weight Format for Ternary Inference on Commodity CPUs and
  *        Multiplier-Free Hardware" - sections "Background / The model", "The .trit v1
  *        layout" (Equations 2-3 in the introduction), "Invariants", "On popcount",
- *        "The hardware core", "Verification".
+ *        "The hardware core", "Verification", "Numerics" (the Reference, Folded and IntMlp
+ *        modes around the matvec).
  *   [TF] "The .trit format, version 1" - section 1 "Why bit planes", 2.3 "Ternary
  *        payload", 2.4 "Dense payload", 3 "A complete file", 4 "Validation".
  *
@@ -24,6 +25,8 @@
  *     at its lowest offending bit; within one beat P1 is checked before P2.
  *   - The dense head is y = W x over bfloat16 inputs; the oracle accumulates in float64
  *     and also returns sum |w * x| for the tolerance.
+ *   - IntMlp: gate and up share the activation (and so its scale); K = S_g^2 S_u is one
+ *     float64 number, (S_g * S_g) * S_u with S = (double)x_scale * (double)w_scale.
  *
  * Parity pins live in the test suite (worked example bytes of [TF] section 3, brute force
  * against a dense integer product, closed-form invariants, the -128 extremes case).
@@ -380,4 +383,51 @@ int oracle_quantize(const float *h, const float *g, int64_t n, float eps, int fo
     }
     free(v);
     return OR_OK;
+}
+
+/*
+ * IntMlp ([TP] "Numerics", the third mode): the squared-ReLU stage of the MLP in exact integers.
+ * The gate and up projections of one token share the activation x; their exact row sums are a_g and
+ * a_u, and their dequantisation scales S_g = x_scale * w_g and S_u = x_scale * w_u are uniform and
+ * positive, so
+ *   relu(a_g S_g)^2 (a_u S_u) = t K,   t = relu(a_g)^2 a_u (an integer),   K = S_g^2 S_u.
+ * t is formed in 64-bit integers (checked in 128 bits: |a| <= 128 cols, so t fits whenever
+ * 128 cols < 2^21, and |t| < 2^55 at 2560 columns as the pages state). K is one float64 number:
+ * S_g and S_u are exact float64 products of two floats; K = (S_g * S_g) * S_u, two roundings.
+ * a_g and a_u come from oracle_gemv. gate_i32 / up_i32 may be NULL.
+ */
+int oracle_intmlp(const uint8_t *gate, const uint8_t *up, int64_t len, int64_t rows, int64_t cols,
+                  const int8_t *x, int64_t x_len, float x_scale, float w_gate, float w_up, int64_t *t,
+                  double *k, int32_t *gate_i32, int32_t *up_i32, int nthreads, or_err *e) {
+    if (rows < 0 || !t || !k) return set_err(e, OR_E_INVAL, -1, -1, -1);
+    int32_t *ag = (int32_t *)malloc((size_t)(rows > 0 ? rows : 1) * sizeof(int32_t));
+    int32_t *au = (int32_t *)malloc((size_t)(rows > 0 ? rows : 1) * sizeof(int32_t));
+    if (!ag || !au) {
+        free(ag);
+        free(au);
+        return set_err(e, OR_E_INVAL, -1, -1, -1);
+    }
+    int rc = oracle_gemv(gate, len, rows, cols, x, x_len, x_scale, w_gate, ag, NULL, NULL, nthreads, e);
+    if (!rc) rc = oracle_gemv(up, len, rows, cols, x, x_len, x_scale, w_up, au, NULL, NULL, nthreads, e);
+    if (!rc) {
+        for (int64_t r = 0; r < rows; ++r) {
+            const __int128 g = ag[r] > 0 ? (__int128)ag[r] : 0;
+            const __int128 v = g * g * (__int128)au[r];
+            if (v > (__int128)INT64_MAX || v < -(__int128)INT64_MAX) {
+                rc = set_err(e, OR_E_RANGE, r, -1, -1);
+                break;
+            }
+            t[r] = (int64_t)v;
+            if (gate_i32) gate_i32[r] = ag[r];
+            if (up_i32) up_i32[r] = au[r];
+        }
+    }
+    if (!rc) {
+        const double sg = (double)x_scale * (double)w_gate;
+        const double su = (double)x_scale * (double)w_up;
+        *k = (sg * sg) * su;
+    }
+    free(ag);
+    free(au);
+    return rc;
 }

@@ -414,3 +414,93 @@ def test_quantize_codes_against_exact_rationals():
     for code, x in zip(q.tolist(), u):
         exact = 127 * x / m
         assert abs(Fraction(code) - exact) <= Fraction(1, 2) + Fraction(1, 1 << 16)
+
+
+# ----------------------------------------------------------------------------- IntMlp epilogue
+# [TP] "Numerics", IntMlp: with gate g = a_g S_g and up u = a_u S_u (uniform positive scales), the
+# squared-ReLU stage relu(g)^2 u equals t K for the integer t = relu(a_g)^2 a_u and K = S_g^2 S_u.
+
+
+def _pair(seed, rows, cols, p_zero=synth.P_ZERO_2B4T):
+    wg = synth.trits(seed, rows, cols, p_zero)
+    wu = synth.trits(seed + 1, rows, cols, p_zero)
+    x, xs = synth.activation(seed + 2, cols)
+    return wg, wu, x, xs, synth.weight_scale(seed + 3), synth.weight_scale(seed + 4)
+
+
+@pytest.mark.parametrize("rows,cols", ((1, 1), (5, 63), (9, 64), (17, 200), (33, 2560), (3, 6912)))
+def test_intmlp_equals_squared_relu_of_dequantised_projections(rows, cols):
+    """relu(g)^2 * u evaluated in exact rationals from the dequantised projections (dense numpy
+    product, relu taken of the real value g) equals t * S_g^2 * S_u exactly; K is the float64
+    rounding of S_g^2 * S_u (two roundings: within 2^-52 relative)."""
+    wg, wu, x, xs, sg32, su32 = _pair(700 + rows + cols, rows, cols)
+    t, k, ag, au = oracle.intmlp(np_pack(wg), np_pack(wu), rows, cols, x, xs, sg32, su32)
+    dg, du = dense_acc(wg, x), dense_acc(wu, x)
+    assert np.array_equal(ag, dg) and np.array_equal(au, du)
+    Sg = Fraction(float(np.float32(xs))) * Fraction(float(np.float32(sg32)))
+    Su = Fraction(float(np.float32(xs))) * Fraction(float(np.float32(su32)))
+    Kx = Sg * Sg * Su
+    for r in range(rows):
+        g = int(dg[r]) * Sg
+        u = int(du[r]) * Su
+        assert max(g, Fraction(0)) ** 2 * u == int(t[r]) * Kx
+    assert abs(Fraction(k) - Kx) <= Kx * Fraction(1, 1 << 52)
+
+
+def test_intmlp_tiny_exhaustive():
+    """Every pair of ternary rows over 3 columns, x over {-128, -1, 0, 1, 127}^3, against Python's
+    unbounded integers applied to the dense sums."""
+    rows = np.array(list(itertools.product((-1, 0, 1), repeat=3)), dtype=np.int8)  # 27 rows
+    for xv in itertools.product((-128, -1, 0, 1, 127), repeat=3):
+        x = np.array(xv, dtype=np.int8)
+        for shift in (0, 5, 11):
+            wg = rows
+            wu = np.roll(rows, shift, axis=0)
+            t, k, _, _ = oracle.intmlp(np_pack(wg), np_pack(wu), 27, 3, x, 1.0, 1.0, 1.0)
+            for r in range(27):
+                a = sum(int(wg[r, c]) * int(x[c]) for c in range(3))
+                b = sum(int(wu[r, c]) * int(x[c]) for c in range(3))
+                assert int(t[r]) == (a if a > 0 else 0) * (a if a > 0 else 0) * b
+            assert k == 1.0
+
+
+def test_intmlp_special_cases():
+    rows, cols = 40, 2560
+    wg, wu, x, xs, sg, su = _pair(91, rows, cols)
+    pg, pu = np_pack(wg), np_pack(wu)
+    t, k, ag, au = oracle.intmlp(pg, pu, rows, cols, x, xs, sg, su)
+    assert np.all(t[ag <= 0] == 0)                       # relu kills non-positive gate rows
+    assert np.all(np.sign(t[ag > 0]) == np.sign(au[ag > 0]))
+    t2, k2, _, _ = oracle.intmlp(pg, swap_planes(pu), rows, cols, x, xs, sg, su)
+    assert np.array_equal(t2, -t) and k2 == k           # negated up weights negate t
+    t3, _, a3, _ = oracle.intmlp(pg, pg, rows, cols, x, xs, sg, sg)
+    assert np.array_equal(t3, np.where(a3 > 0, a3.astype(np.int64) ** 3, 0))  # gate == up: relu(a)^3
+    t4, k4, _, _ = oracle.intmlp(pg, pu, rows, cols, x, xs, np.float32(2 * sg), su)
+    assert np.array_equal(t4, t) and k4 == 4 * k        # a power-of-two weight scale only moves K
+
+
+@pytest.mark.parametrize("cols", (2560, 16383))
+def test_intmlp_bound_extremes(cols):
+    """x = -128 everywhere, gate all -1 and up all +1: a_g = 128 cols, a_u = -128 cols, the largest
+    |t| any pair of this width can give. At 2560 columns |t| < 2^55 (the pages' bound); up to
+    16383 columns it still fits int64 exactly."""
+    x = np.full(cols, -128, dtype=np.int8)
+    wg = np.full((2, cols), -1, dtype=np.int8)
+    wu = np.full((2, cols), 1, dtype=np.int8)
+    t, _, ag, au = oracle.intmlp(np_pack(wg), np_pack(wu), 2, cols, x, 1.0, 1.0, 1.0)
+    want = -((128 * cols) ** 3)
+    assert int(ag[0]) == 128 * cols and int(au[0]) == -128 * cols
+    assert [int(v) for v in t] == [want, want]
+    if cols == 2560:
+        assert abs(want) < 2 ** 55
+
+
+def test_intmlp_range_error_past_int64():
+    """At 16384 columns the extreme pair reaches 2^63, which int64 cannot hold: the oracle refuses."""
+    cols = 16384
+    x = np.full(cols, -128, dtype=np.int8)
+    wg = np.full((1, cols), -1, dtype=np.int8)
+    wu = np.full((1, cols), -1, dtype=np.int8)
+    with pytest.raises(oracle.OracleError) as ei:
+        oracle.intmlp(np_pack(wg), np_pack(wu), 1, cols, x, 1.0, 1.0, 1.0)
+    assert ei.value.code == oracle.E_RANGE
