@@ -161,6 +161,44 @@ def prologue_measure(bpw, torch, synth, dev, ds, steps: int = 100) -> dict:
             "quantised_values": int(sum(c[4] for c in ds.shapes))}
 
 
+def intmlp_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
+    """The decode step with the MLP's squared-ReLU stage fused into gate/up: per layer q, k, v, o and
+    down stay plain GEMVs and gate/up become one IntMlp pair reading the gate's activation, writing
+    t = relu(a_g)^2 * a_u (int64) and K instead of the two projections' outputs. Same 521 MB of
+    planes, one launch per step, the HBM copies in rotation, timed between HIP events."""
+    ts, ks, plans = {}, {}, []
+    for _, mats, _ in ds.copies:
+        jobs, pairs = [], []
+        for i, (layer, proj, name, rows, cols) in enumerate(ds.shapes):
+            if proj == 5:
+                continue
+            x, s = ds.xs[i]
+            if proj == 4:
+                if layer not in ts:
+                    ts[layer] = torch.empty(rows, dtype=torch.int64, device=dev)
+                    ks[layer] = torch.empty(1, dtype=torch.float64, device=dev)
+                pairs.append(bpw.intmlp_job(mats[i], mats[i + 1], x, s, ts[layer], ks[layer]))
+            else:
+                oi, of = ds.outs[i]
+                jobs.append(bpw.gemv_job(mats[i], x, s, oi, of))
+        ws = torch.empty(bpw.bpw_gemv_intmlp_workspace_bytes(jobs, pairs), dtype=torch.uint8, device=dev)
+        plans.append((bpw.GemvPlan(jobs, ws, mlp=pairs), ws))
+    for i in range(10):
+        plans[i % len(plans)][0].run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        plans[i % len(plans)][0].run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    for p, _ in plans:
+        p.free()
+    return {"decode_step_intmlp_us": round(us, 2), "weight_gbs": round(ds.plane_bytes / (us * 1e-6) / 1e9, 1),
+            "pairs": len(ts), "plain_jobs": len(ds.shapes) - 2 * len(ts)}
+
+
 def probe_gbs(bpw, torch, dev) -> float:
     """Streaming-read probe: best of 5 passes over 4 GiB (the pages' measured-roofline method)."""
     n = 4 << 30
@@ -425,6 +463,8 @@ def main() -> int:
     if not args.no_extras:
         log("quantiser prologue")
         result["prologue"] = prologue_measure(bpw, torch, synth, dev, ds)
+        log("IntMlp pairs")
+        result["intmlp"] = intmlp_measure(bpw, torch, dev, ds)
         del ds
         torch.cuda.empty_cache()
         log("probe")

@@ -20,6 +20,7 @@ __all__ = [
     "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
+    "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
     "bpw_gemm_small_batch", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
 ]
@@ -177,6 +178,36 @@ def bpw_gemv_workspace_bytes(jobs) -> int:
     return _lib.lib().bpw_gemv_workspace_bytes(arr, n)
 
 
+def intmlp_job(gate: DevMat, up: DevMat, x, x_scale: float, t_out, k_out, gate_i32=None, up_i32=None,
+               x_scale_dev=None) -> _lib.BpwIntMlpJob:
+    """One bpw_intmlp_job: gate and up (same shape) read the int8 GPU tensor x; t_out int64 [rows]
+    receives relu(a_g)^2 * a_u, k_out float64 [1] receives K; gate_i32 / up_i32 optional int32 [rows]."""
+    j = _lib.BpwIntMlpJob()
+    j.gate = gate.desc
+    j.up = up.desc
+    j.d_x = _dptr(x)
+    j.x_len = x.numel() * x.element_size()
+    j.x_scale = float(x_scale)
+    j.d_x_scale = _dptr(x_scale_dev)
+    j.d_t = _dptr(t_out)
+    j.d_k = _dptr(k_out)
+    j.d_gate_i32 = _dptr(gate_i32)
+    j.d_up_i32 = _dptr(up_i32)
+    return j
+
+
+def _mlp_array(mlp):
+    mlp = list(mlp or [])
+    arr = (_lib.BpwIntMlpJob * max(1, len(mlp)))(*mlp)
+    return arr, len(mlp)
+
+
+def bpw_gemv_intmlp_workspace_bytes(jobs, mlp) -> int:
+    arr, n = _jobs_array(jobs)
+    marr, nm = _mlp_array(mlp)
+    return _lib.lib().bpw_gemv_intmlp_workspace_bytes(arr, n, marr, nm)
+
+
 def bpw_gemv(jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None) -> None:
     arr, n = _jobs_array(jobs)
     ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
@@ -184,15 +215,21 @@ def bpw_gemv(jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None) -> None:
 
 
 class GemvPlan:
-    """bpw_gemv_plan: the job table written once into d_ws; run() queues the one launch."""
+    """bpw_gemv_plan: the job table written once into d_ws; run() queues the one launch. With mlp
+    (a list of intmlp_job) the plan is made by bpw_gemv_intmlp_plan_create."""
 
-    def __init__(self, jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None):
+    def __init__(self, jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None, mlp=None):
         arr, n = _jobs_array(jobs)
         ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
         h = ctypes.c_void_p()
-        _lib.check(_lib.lib().bpw_gemv_plan_create(arr, n, kernel, _dptr(d_ws), ws_len, _stream(stream),
-                                                   ctypes.byref(h)))
-        self._h, self._keep = h, (jobs, d_ws)
+        if mlp is None:
+            _lib.check(_lib.lib().bpw_gemv_plan_create(arr, n, kernel, _dptr(d_ws), ws_len, _stream(stream),
+                                                       ctypes.byref(h)))
+        else:
+            marr, nm = _mlp_array(mlp)
+            _lib.check(_lib.lib().bpw_gemv_intmlp_plan_create(arr, n, marr, nm, kernel, _dptr(d_ws), ws_len,
+                                                              _stream(stream), ctypes.byref(h)))
+        self._h, self._keep = h, (jobs, mlp, d_ws)
 
     def run(self, stream=None) -> None:
         _lib.check(_lib.lib().bpw_gemv_plan_run(self._h, _stream(stream)))

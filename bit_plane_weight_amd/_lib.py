@@ -32,6 +32,13 @@ class BpwGemvJob(ctypes.Structure):
                 ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p), ("d_x_scale", ctypes.c_void_p)]
 
 
+class BpwIntMlpJob(ctypes.Structure):
+    _fields_ = [("gate", BpwDevMat), ("up", BpwDevMat), ("d_x", ctypes.c_void_p), ("x_len", ctypes.c_int64),
+                ("x_scale", ctypes.c_float), ("reserved", ctypes.c_uint32), ("d_x_scale", ctypes.c_void_p),
+                ("d_t", ctypes.c_void_p), ("d_k", ctypes.c_void_p), ("d_gate_i32", ctypes.c_void_p),
+                ("d_up_i32", ctypes.c_void_p)]
+
+
 class BpwQuantJob(ctypes.Structure):
     _fields_ = [("d_h", ctypes.c_void_p), ("d_g", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("d_q", ctypes.c_void_p), ("q_len", ctypes.c_int64), ("d_scale", ctypes.c_void_p),
@@ -82,6 +89,9 @@ def lib():
         "bpw_gemv_workspace_bytes": (sz, [J, i32]),
         "bpw_gemv": (i32, [J, i32, i32, vp, sz, vp]),
         "bpw_gemv_plan_create": (i32, [J, i32, i32, vp, sz, vp, ctypes.POINTER(vp)]),
+        "bpw_gemv_intmlp_workspace_bytes": (sz, [J, i32, ctypes.POINTER(BpwIntMlpJob), i32]),
+        "bpw_gemv_intmlp_plan_create": (i32, [J, i32, ctypes.POINTER(BpwIntMlpJob), i32, i32, vp, sz, vp,
+                                              ctypes.POINTER(vp)]),
         "bpw_gemv_plan_run": (i32, [vp, vp]),
         "bpw_gemv_plan_free": (None, [vp]),
         "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp]),

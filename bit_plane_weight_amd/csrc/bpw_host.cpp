@@ -307,12 +307,22 @@ int64_t bytelane_tiles(const bpw_gemv_job &j) {
     return (j.m.rows + g.tile_rows - 1) / g.tile_rows;
 }
 
-Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial) {
+// An IntMlp pair's tiles: kPairTileUnits row-groups of each matrix (so as many beats as a plain
+// tile of kTileUnits row-groups).
+int64_t pair_tiles(const bpw_intmlp_job &j) {
+    const Geometry g = geometry_for(j.gate.bpr, true);
+    const int64_t tu = tile_units(g) / 2;
+    return (units_of(j.gate.rows, g) + tu - 1) / tu;
+}
+
+Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial, const bpw_intmlp_job *mlp = nullptr,
+                  int32_t n_mlp = 0) {
     Layout L{};
     L.jobs_off = 0;
     L.n_work = 0;
     for (int32_t i = 0; i < n; ++i) L.n_work += bitserial ? bitserial_tiles(jobs[i]) : bytelane_tiles(jobs[i]);
-    L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)n);
+    for (int32_t i = 0; i < n_mlp; ++i) L.n_work += pair_tiles(mlp[i]);
+    L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)(n + n_mlp));
     const size_t tile_bytes = bitserial ? sizeof(bpw::Tile) : sizeof(bpw::DevTile);
     L.total = align_up(L.work_off + tile_bytes * (size_t)L.n_work);
     return L;
@@ -326,9 +336,9 @@ bpw_status check_dev_mat(const bpw_dev_mat *m, const char *who) {
     return BPW_OK;
 }
 
-bpw_status check_job(const bpw_gemv_job &j, int32_t i) {
+bpw_status check_job(const bpw_gemv_job &j, int32_t i, const char *kind = "job") {
     char who[48];
-    std::snprintf(who, sizeof who, "job %d", i);
+    std::snprintf(who, sizeof who, "%s %d", kind, i);
     bpw_status st = check_dev_mat(&j.m, who);
     if (st) return st;
     const uint64_t bytes = (uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u;
@@ -343,6 +353,38 @@ bpw_status check_job(const bpw_gemv_job &j, int32_t i) {
                     (long long)(j.m.bpr * 64));
     if (!j.d_out_i32) return fail(BPW_E_INVAL, "%s: d_out_i32 is NULL", who);
     if (!std::isfinite(j.x_scale)) return fail(BPW_E_INVAL, "%s: x_scale is not finite", who);
+    return BPW_OK;
+}
+
+// Widest pair whose t = relu(a_g)^2 * a_u cannot overflow int64: |a| <= 128 * cols < 2^21.
+constexpr int64_t kPairMaxCols = 16383;
+
+bpw_status check_pair(const bpw_intmlp_job &j, int32_t i) {
+    char who[48];
+    std::snprintf(who, sizeof who, "pair %d gate", i);
+    bpw_status st = check_dev_mat(&j.gate, who);
+    if (st) return st;
+    std::snprintf(who, sizeof who, "pair %d up", i);
+    st = check_dev_mat(&j.up, who);
+    if (st) return st;
+    std::snprintf(who, sizeof who, "pair %d", i);
+    if (j.gate.rows != j.up.rows || j.gate.cols != j.up.cols)
+        return fail(BPW_E_INVAL, "%s: gate is %lld x %lld, up is %lld x %lld", who, (long long)j.gate.rows,
+                    (long long)j.gate.cols, (long long)j.up.rows, (long long)j.up.cols);
+    if (j.gate.cols > kPairMaxCols)
+        return fail(BPW_E_UNSUPPORTED, "%s: %lld columns; t is exact in int64 only up to %lld", who,
+                    (long long)j.gate.cols, (long long)kPairMaxCols);
+    // the same limits as a plain job over the gate (the up matrix has the same size)
+    bpw_gemv_job g{};
+    g.m = j.gate;
+    g.d_x = j.d_x;
+    g.x_len = j.x_len;
+    g.x_scale = j.x_scale;
+    g.d_out_i32 = reinterpret_cast<int32_t *>(j.d_t);  // only checked for NULL here
+    st = check_job(g, i, "pair");
+    if (st) return st;
+    if (!j.d_t || ((uintptr_t)j.d_t & 7u)) return fail(BPW_E_INVAL, "%s: d_t is NULL or not 8-byte aligned", who);
+    if (!j.d_k || ((uintptr_t)j.d_k & 7u)) return fail(BPW_E_INVAL, "%s: d_k is NULL or not 8-byte aligned", who);
     return BPW_OK;
 }
 
@@ -501,24 +543,33 @@ size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs) {
     return std::max(layout_for(jobs, n_jobs, true).total, layout_for(jobs, n_jobs, false).total);
 }
 
-bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
-                                size_t ws_len, void *stream, bpw_gemv_plan **out) {
+static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp, int32_t n_mlp,
+                              int32_t kernel, void *d_ws, size_t ws_len, void *stream, bpw_gemv_plan **out) {
     if (!out) return fail(BPW_E_INVAL, "out is NULL");
     *out = nullptr;
     if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad job list");
+    if (n_mlp < 0 || (n_mlp > 0 && !mlp)) return fail(BPW_E_INVAL, "bad pair list");
+    if ((int64_t)n_jobs + n_mlp > INT32_MAX) return fail(BPW_E_INVAL, "too many jobs");
     if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_BYTELANE)
         return fail(BPW_E_UNSUPPORTED, "unknown kernel %d", (int)kernel);
     const bool bitserial = (kernel != BPW_KERNEL_BYTELANE);
+    if (!bitserial && n_mlp > 0)
+        return fail(BPW_E_UNSUPPORTED, "IntMlp pairs run on the bit-serial kernel only (pinned: byte-lane)");
     for (int32_t i = 0; i < n_jobs; ++i) {
         bpw_status st = check_job(jobs[i], i);
         if (st) return st;
     }
-    Layout L = layout_for(jobs, n_jobs, bitserial);
+    for (int32_t i = 0; i < n_mlp; ++i) {
+        bpw_status st = check_pair(mlp[i], i);
+        if (st) return st;
+    }
+    const int32_t n_all = n_jobs + n_mlp;
+    Layout L = layout_for(jobs, n_jobs, bitserial, mlp, n_mlp);
     if (L.n_work > (int64_t)INT32_MAX)
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
-    if (n_jobs > 0 && bpw_gemv_workspace_bytes(jobs, n_jobs) > ws_len)
-        return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, bpw_gemv_workspace_bytes(jobs, n_jobs));
-    if (n_jobs > 0 && !d_ws) return fail(BPW_E_INVAL, "d_ws is NULL");
+    const size_t need = bpw_gemv_intmlp_workspace_bytes(jobs, n_jobs, mlp, n_mlp);
+    if (n_all > 0 && need > ws_len) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, need);
+    if (n_all > 0 && !d_ws) return fail(BPW_E_INVAL, "d_ws is NULL");
     if (((uintptr_t)d_ws & (kAlign - 1)) != 0) return fail(BPW_E_INVAL, "d_ws must be 256-byte aligned");
     bpw_status st = check_device();
     if (st) return st;
@@ -534,7 +585,7 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     plan->tiles = ws + L.work_off;
     plan->n_tiles = L.n_work;
     plan->has_work = 0;
-    if (n_jobs == 0) {
+    if (n_all == 0) {
         *out = plan;
         return BPW_OK;
     }
@@ -545,33 +596,49 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
     auto *hb = reinterpret_cast<bpw::Tile *>(host.data() + L.work_off);
     int64_t t = 0;
-    for (int32_t i = 0; i < n_jobs; ++i) {
-        const bpw_gemv_job &j = jobs[i];
-        const Geometry g = geometry_for(j.m.bpr, bitserial);
+    for (int32_t i = 0; i < n_all; ++i) {
+        const bool pair = i >= n_jobs;
+        const bpw_dev_mat &m = pair ? mlp[i - n_jobs].gate : jobs[i].m;
+        const Geometry g = geometry_for(m.bpr, bitserial);
         bpw::DevJob d{};
-        d.planes = static_cast<const uint8_t *>(j.m.d_planes);
-        d.x = j.d_x;
-        d.out_i32 = j.d_out_i32;
-        d.out_f32 = j.d_out_f32;
-        d.rows = (int32_t)j.m.rows;
-        d.bpr = (int32_t)j.m.bpr;
-        d.x_scale = j.x_scale;
-        d.x_scale_ptr = j.d_x_scale;
-        d.w_scale = j.m.w_scale;
+        d.planes = static_cast<const uint8_t *>(m.d_planes);
+        d.rows = (int32_t)m.rows;
+        d.bpr = (int32_t)m.bpr;
+        d.w_scale = m.w_scale;
         d.glog = g.glog;
         d.kblk = g.kblk;
         d.nchunk = g.nchunk;
         d.tile_rows = g.tile_rows;
-        d.plane_bytes = (uint32_t)((uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u);
+        d.plane_bytes = (uint32_t)((uint64_t)m.rows * (uint64_t)m.bpr * 16u);
+        if (!pair) {
+            const bpw_gemv_job &j = jobs[i];
+            d.x = j.d_x;
+            d.out_i32 = j.d_out_i32;
+            d.out_f32 = j.d_out_f32;
+            d.x_scale = j.x_scale;
+            d.x_scale_ptr = j.d_x_scale;
+        } else {
+            const bpw_intmlp_job &j = mlp[i - n_jobs];
+            d.pair = 1;
+            d.x = j.d_x;
+            d.out_i32 = j.d_gate_i32;
+            d.x_scale = j.x_scale;
+            d.x_scale_ptr = j.d_x_scale;
+            d.planes_up = static_cast<const uint8_t *>(j.up.d_planes);
+            d.out_up_i32 = j.d_up_i32;
+            d.t_out = j.d_t;
+            d.k_out = j.d_k;
+            d.w_scale_up = j.up.w_scale;
+        }
         hj[i] = d;
         if (!bitserial) {
-            for (int64_t r0 = 0; r0 < j.m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
+            for (int64_t r0 = 0; r0 < m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
         } else {
-            // tiles of one job in row order; jobs in the order given
-            const int64_t U = units_of(j.m.rows, g), tu = tile_units(g);
+            // tiles of one job in row order; jobs in the order given, pairs after the plain jobs
+            const int64_t U = units_of(m.rows, g), tu = pair ? tile_units(g) / 2 : tile_units(g);
             for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
         }
-        if (j.m.rows > 0) plan->has_work = 1;
+        if (m.rows > 0) plan->has_work = 1;  // a job without rows has no tiles (a pair: not even K)
     }
     if (t != L.n_work) {
         delete plan;
@@ -586,6 +653,24 @@ bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_
     }
     *out = plan;
     return BPW_OK;
+}
+
+bpw_status bpw_gemv_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws,
+                                size_t ws_len, void *stream, bpw_gemv_plan **out) {
+    return create_plan(jobs, n_jobs, nullptr, 0, kernel, d_ws, ws_len, stream, out);
+}
+
+size_t bpw_gemv_intmlp_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp,
+                                       int32_t n_mlp) {
+    if (n_mlp <= 0 || !mlp) return bpw_gemv_workspace_bytes(jobs, n_jobs);
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return 0;
+    return layout_for(jobs, n_jobs, true, mlp, n_mlp).total;  // pairs need the bit-serial kernel
+}
+
+bpw_status bpw_gemv_intmlp_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp,
+                                       int32_t n_mlp, int32_t kernel, void *d_ws, size_t ws_len, void *stream,
+                                       bpw_gemv_plan **out) {
+    return create_plan(jobs, n_jobs, mlp, n_mlp, kernel, d_ws, ws_len, stream, out);
 }
 
 static bpw_status plan_ready(const bpw_gemv_plan *plan) {

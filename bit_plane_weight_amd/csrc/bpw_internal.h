@@ -37,8 +37,17 @@ struct DevJob {
     int32_t nchunk;         // passes over the row: bpr <= G * kblk * nchunk
     int32_t tile_rows;      // rows per workgroup tile = kWaves * kIters * (64 / G) (tiled kernels)
     uint32_t plane_bytes;   // rows * bpr * 16 (the buffer range of the weight loads)
+    int32_t pair;           // 1: an IntMlp gate/up pair (planes = gate, out_i32 = gate sums or null)
+    // IntMlp pairs only:
+    const uint8_t *planes_up;  // up projection, same shape as the gate
+    int32_t *out_up_i32;       // up sums or null
+    int64_t *t_out;            // relu(a_g)^2 * a_u
+    double *k_out;             // (S_g * S_g) * S_u
+    float w_scale_up;
     int32_t pad;
 };
+
+constexpr int kPairTileUnits = kTileUnits / 2;  // row-groups of each matrix in one IntMlp pair tile
 
 // A tile of the bit-serial GEMV: consecutive row-groups ("units" of 64 / G rows) [u0, u1) of one
 // job, at most kTileRows rows, run by one workgroup.

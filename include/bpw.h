@@ -184,6 +184,45 @@ bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream);
 
 void bpw_gemv_plan_free(bpw_gemv_plan *plan);
 
+/* ------------------------------------------------------------------------ IntMlp gate/up pairs */
+
+/* The gate and up projections of one MLP with the IntMlp epilogue fused in ("Tritium ...",
+ * "Numerics", IntMlp): the squared-ReLU stage never becomes floating point. Both projections read
+ * the same activation codes x (so they share its scale); with exact row sums a_g, a_u and the
+ * uniform positive scales S_g = x_scale * gate.w_scale, S_u = x_scale * up.w_scale,
+ *   relu(a_g S_g)^2 (a_u S_u) = t K,   t = relu(a_g)^2 * a_u (int64),   K = S_g^2 * S_u,
+ * K computed once in float64 as (S_g * S_g) * S_u with S = (double)x_scale * (double)w_scale.
+ * |a| <= 128 * cols, so t is exact in int64 for cols <= 16383 (|t| < 2^55 at 2560 columns); wider
+ * pairs are refused with BPW_E_UNSUPPORTED. Outputs must not overlap those of other jobs. */
+typedef struct bpw_intmlp_job {
+    bpw_dev_mat gate;       /* gate projection */
+    bpw_dev_mat up;         /* up projection: same rows and cols as gate */
+    const int8_t *d_x;      /* device int8 codes both projections read, 16-byte aligned */
+    int64_t x_len;          /* bytes readable at d_x; >= bpr * 64 */
+    float x_scale;          /* activation scale (ignored if d_x_scale is set) */
+    uint32_t reserved;
+    const float *d_x_scale; /* device float [1] or NULL, as in bpw_gemv_job */
+    int64_t *d_t;           /* device int64 [rows], 8-byte aligned: t */
+    double *d_k;            /* device double [1], 8-byte aligned: K */
+    int32_t *d_gate_i32;    /* device int32 [rows] or NULL: a_g */
+    int32_t *d_up_i32;      /* device int32 [rows] or NULL: a_u */
+} bpw_intmlp_job;
+
+/* Device workspace bytes for a plan over n_jobs plain GEMVs and n_mlp gate/up pairs. */
+size_t bpw_gemv_intmlp_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp,
+                                       int32_t n_mlp);
+
+/* As bpw_gemv_plan_create, with gate/up pairs beside the plain jobs: bpw_gemv_plan_run then runs
+ * all of them in one kernel launch. Each pair is one job of the launch whose tiles stream the same
+ * rows of both matrices and write t (and K, once) instead of the two projections' outputs; a pair
+ * with no rows writes nothing, K included. Pairs
+ * need the bit-serial kernel (AUTO or BPW_KERNEL_BITSERIAL); BPW_KERNEL_BYTELANE with n_mlp > 0 is
+ * BPW_E_UNSUPPORTED. Errors as bpw_gemv_plan_create, plus BPW_E_INVAL for a pair whose matrices
+ * differ in shape or whose d_t / d_k is NULL or misaligned. */
+bpw_status bpw_gemv_intmlp_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp,
+                                       int32_t n_mlp, int32_t kernel, void *d_ws, size_t ws_len, void *stream,
+                                       bpw_gemv_plan **out);
+
 /* ------------------------------------------------------------------------ activation quantiser */
 
 /* One activation to quantise in the Folded mode ("Tritium ...", "Numerics"): int8 codes are taken

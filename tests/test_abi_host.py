@@ -31,7 +31,8 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     names = declared_functions()
     assert set(names) >= {"bpw_pack_i8", "bpw_validate", "bpw_load", "bpw_upload", "bpw_gemv", "bpw_gemv_plan_create",
-                          "bpw_gemv_plan_run", "bpw_gemm_small_batch", "bpw_dense_head_gemv"}, names
+                          "bpw_gemv_plan_run", "bpw_gemm_small_batch", "bpw_dense_head_gemv",
+                          "bpw_quantize", "bpw_gemv_intmlp_plan_create"}, names
     missing = [n for n in names if not hasattr(L, n)]
     assert not missing, missing
     assert L.bpw_abi_version() == _lib.ABI_VERSION
@@ -141,6 +142,30 @@ def test_forged_descriptor_is_refused_before_any_device_work():
     st = L.bpw_gemm_small_batch(ctypes.byref(d), ctypes.c_void_p(0x20000), 2, 64,
                                 (ctypes.c_float * 2)(1, 1), ctypes.c_void_p(0x30000), None, 0, None)
     assert st == _lib.E_NOT_VALIDATED
+
+
+def test_forged_intmlp_pair_is_refused_and_bytelane_cannot_serve_pairs():
+    L = _lib.lib()
+    d = _lib.BpwDevMat()
+    d.d_planes = 0x10000
+    d.rows, d.cols, d.bpr, d.w_scale = 4, 64, 1, 1.0
+    d.seal = 0x1234
+    p = _lib.BpwIntMlpJob()
+    p.gate = d
+    p.up = d
+    p.d_x = 0x20000
+    p.x_len = 64
+    p.d_t = 0x30000
+    p.d_k = 0x38000
+    arr = (_lib.BpwIntMlpJob * 1)(p)
+    h = ctypes.c_void_p()
+    assert L.bpw_gemv_intmlp_plan_create(None, 0, arr, 1, 0, ctypes.c_void_p(0x40000), 1 << 20, None,
+                                         ctypes.byref(h)) == _lib.E_NOT_VALIDATED
+    assert "pair 0 gate" in bpw.bpw_last_error()
+    assert L.bpw_gemv_intmlp_plan_create(None, 0, arr, 1, 2, ctypes.c_void_p(0x40000), 1 << 20, None,
+                                         ctypes.byref(h)) == _lib.E_UNSUPPORTED
+    assert L.bpw_gemv_intmlp_plan_create(None, 0, None, 1, 0, None, 0, None, ctypes.byref(h)) == _lib.E_INVAL
+    assert L.bpw_gemv_intmlp_workspace_bytes(None, 0, None, 0) == 0
 
 
 def test_empty_and_bad_arguments():

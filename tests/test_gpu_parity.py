@@ -447,3 +447,179 @@ def test_quantise_then_gemv_layer(dev, kernel):
             assert np.all(np.abs(gf - y64) <= 1e-6 * np.abs(y64))
     plan.free()
     qplan.free()
+
+
+# ----------------------------------------------------------------------------- IntMlp gate/up pairs
+
+
+class UploadedPair:
+    """A gate/up pair sharing one activation, resident on the GPU, with sentinel-filled outputs."""
+
+    def __init__(self, wg, wu, x, x_scale, sg, su, dev, want_i32=True):
+        self.wg, self.wu, self.x_np, self.xs, self.sg, self.su = wg, wu, x, x_scale, sg, su
+        rows, cols = wg.shape
+        self.rows, self.cols = rows, cols
+        self.bufs = []
+        self.g = self._up(wg, sg, dev)
+        self.u = self._up(wu, su, dev)
+        bpr = (cols + 63) // 64
+        xh = np.zeros(max(bpr * 64, 16), np.int8)
+        xh[:cols] = x
+        self.x = torch.from_numpy(xh).to(dev)
+        n = max(rows, 1)
+        self.t = torch.full((n,), 0x5A5A5A5A5A5A5A5A, dtype=torch.int64, device=dev)
+        self.k = torch.full((1,), float("nan"), dtype=torch.float64, device=dev)
+        self.gi = torch.full((n,), 0x7EADBEEF, dtype=torch.int32, device=dev) if want_i32 else None
+        self.ui = torch.full((n,), 0x7EADBEEF, dtype=torch.int32, device=dev) if want_i32 else None
+
+    def _up(self, w, s, dev):
+        hm = bpw.bpw_load(bpw.bpw_pack_i8(w), w.shape[0], w.shape[1], s)
+        buf = torch.empty(max(hm.nbytes, 1), dtype=torch.uint8, device=dev)
+        m = bpw.bpw_upload(hm, buf)
+        hm.free()
+        self.bufs.append(buf)
+        return m
+
+    def job(self, x_scale_dev=None):
+        return bpw.intmlp_job(self.g, self.u, self.x, self.xs, self.t, self.k, self.gi, self.ui,
+                              x_scale_dev=x_scale_dev)
+
+    def check(self, what, x_scale=None):
+        xs = self.xs if x_scale is None else x_scale
+        t, k, ag, au = oracle.intmlp(oracle.pack(self.wg), oracle.pack(self.wu), self.rows, self.cols, self.x_np,
+                                     xs, self.sg, self.su, nthreads=NT)
+        gt = self.t.cpu().numpy()[: self.rows]
+        bad = np.nonzero(gt != t)[0]
+        assert bad.size == 0, f"{what}: t differs at rows {bad[:8].tolist()} (got {gt[bad[:4]]}, want {t[bad[:4]]})"
+        gk = float(self.k.item())
+        assert np.float64(gk).view(np.uint64) == np.float64(k).view(np.uint64), f"{what}: K {gk!r} != {k!r}"
+        if self.gi is not None:
+            assert np.array_equal(self.gi.cpu().numpy()[: self.rows], ag), f"{what}: gate sums"
+            assert np.array_equal(self.ui.cpu().numpy()[: self.rows], au), f"{what}: up sums"
+
+
+def _pair_inputs(seed, rows, cols):
+    wg = synth.trits(seed, rows, cols)
+    wu = synth.trits(seed + 1, rows, cols)
+    x, xs = synth.activation(seed + 2, cols)
+    return wg, wu, x, xs, synth.weight_scale(seed + 3), synth.weight_scale(seed + 4)
+
+
+def _run_plan(jobs, pairs, dev, kernel=bpw.KERNEL_AUTO, reps=1):
+    ws = torch.empty(max(bpw.bpw_gemv_intmlp_workspace_bytes(jobs, pairs), 256), dtype=torch.uint8, device=dev)
+    plan = bpw.GemvPlan(jobs, ws, kernel, mlp=pairs)
+    for _ in range(reps):
+        plan.run()
+    torch.cuda.synchronize()
+    plan.free()
+
+
+@pytest.mark.parametrize("kernel", (bpw.KERNEL_AUTO, bpw.KERNEL_BITSERIAL))
+@pytest.mark.parametrize("want_i32", (True, False))
+def test_intmlp_gate_up_6912x2560(dev, kernel, want_i32):
+    log(f"case: IntMlp pair 6912x2560 kernel={kernel} i32={want_i32}")
+    p = UploadedPair(*_pair_inputs(8801, 6912, 2560), dev, want_i32=want_i32)
+    _run_plan([], [p.job()], dev, kernel, reps=2)
+    p.check("gate/up 6912x2560")
+
+
+@pytest.mark.parametrize("rows", (1, 7, 65, 129, 1025))
+def test_intmlp_ragged_pairs_beside_plain_jobs(dev, rows):
+    """Pairs of every column geometry (generic K = 1 and 2, one and several LDS passes, both model
+    widths) in one launch with plain jobs; every output checked."""
+    colss = (1, 63, 64, 65, 127, 129, 448, 2500, 2560, 6912, 8193, 16383)
+    log(f"case: IntMlp ragged pairs rows={rows} cols={colss}")
+    pairs = [UploadedPair(*_pair_inputs(9000 + 37 * rows + c, rows, c), dev) for c in colss]
+    plain = [Uploaded(synth.ternary_case(9100 + rows, 0, i, rows, c), dev) for i, c in enumerate((65, 2560, 6912))]
+    _run_plan([u.job() for u in plain], [p.job() for p in pairs], dev)
+    for p in pairs:
+        p.check(f"pair {rows}x{p.cols}")
+    for u in plain:
+        check_case(u, oracle_ref(u.case), f"plain {rows}x{u.case.cols} beside pairs")
+
+
+@pytest.mark.parametrize("cols", (2560, 16383))
+def test_intmlp_extremes(dev, cols):
+    """x = -128, gate all -1, up all +1: t = -(128 cols)^3, the largest |t| of the width."""
+    log(f"case: IntMlp extremes cols={cols}")
+    rows = 70
+    x = np.full(cols, -128, np.int8)
+    p = UploadedPair(np.full((rows, cols), -1, np.int8), np.full((rows, cols), 1, np.int8), x, 0.25, 1.0, 1.0, dev)
+    _run_plan([], [p.job()], dev)
+    p.check(f"extremes {cols}")
+    assert int(p.t[0].item()) == -((128 * cols) ** 3)
+
+
+def test_intmlp_empty_pairs(dev):
+    log("case: IntMlp pairs with no columns / no rows")
+    p0 = UploadedPair(np.zeros((70, 0), np.int8), np.zeros((70, 0), np.int8), np.zeros(0, np.int8), 0.5, 1.5, 2.0, dev)
+    pr = UploadedPair(np.zeros((0, 64), np.int8), np.zeros((0, 64), np.int8), np.zeros(64, np.int8), 0.5, 1.5, 2.0, dev)
+    _run_plan([], [p0.job(), pr.job()], dev)
+    p0.check("no columns")
+    assert not p0.t.cpu().numpy().any()
+    assert np.isnan(pr.k.item()) and int(pr.t[0].item()) == 0x5A5A5A5A5A5A5A5A  # no rows: nothing written
+
+
+def test_intmlp_scale_from_quantiser(dev):
+    """Folded quantiser -> IntMlp pair: the codes and the device-resident scale feed both projections."""
+    log("case: quantiser -> IntMlp pair 6912x2560")
+    wg, wu, _, _, sg, su = _pair_inputs(8901, 6912, 2560)
+    h, g = _hg(8902, 2560, 3.0)
+    q, s = oracle.quantize(h, g, 1e-5, folded=True)
+    p = UploadedPair(wg, wu, q, 0.0, sg, su, dev)
+    sd = torch.zeros(1, dtype=torch.float32, device=dev)
+    hd, gd = torch.from_numpy(h).to(dev), torch.from_numpy(g).to(dev)
+    qws = torch.empty(bpw.bpw_quantize_workspace_bytes(1), dtype=torch.uint8, device=dev)
+    p.x.fill_(99)  # overwritten by the quantiser (codes, then zeros up to the buffer's end)
+    bpw.bpw_quantize([bpw.quant_job(hd, gd, p.x, sd, 1e-5)], qws)
+    _run_plan([], [p.job(x_scale_dev=sd)], dev)
+    assert float(sd.item()) == s
+    p.check("quantiser -> pair", x_scale=s)
+
+
+def test_decode_step_with_intmlp_pairs(dev):
+    """A decode step with the MLP's squared-ReLU stage fused: per layer q, k, v, o, down as plain
+    jobs and gate/up as one pair sharing x, all 30 layers in one launch, run twice."""
+    log("case: decode step, 150 plain jobs + 30 IntMlp pairs")
+    plain, pairs = [], []
+    for layer in range(30):
+        cs = synth.layer_cases(777, layer)
+        for i in (0, 1, 2, 3, 6):
+            plain.append(Uploaded(cs[i], dev))
+        gc, uc = cs[4], cs[5]
+        pairs.append(UploadedPair(gc.w, uc.w, gc.x, gc.x_scale, gc.w_scale, uc.w_scale, dev, want_i32=(layer % 2 == 0)))
+    _run_plan([u.job() for u in plain], [p.job() for p in pairs], dev, reps=2)
+    for p in pairs:
+        p.check("decode-step pair")
+    for u in plain:
+        check_case(u, oracle_ref(u.case), u.case.name)
+
+
+def test_intmlp_argument_errors(dev):
+    log("case: IntMlp argument errors")
+    wg, wu, x, xs, sg, su = _pair_inputs(8701, 64, 128)
+    p = UploadedPair(wg, wu, x, xs, sg, su, dev)
+    q = UploadedPair(wg[:32], wu[:32], x, xs, sg, su, dev)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    bad = bpw.intmlp_job(p.g, q.u, p.x, xs, p.t, p.k)  # shapes differ
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.GemvPlan([], ws, mlp=[bad])
+    assert ei.value.status == _lib.E_INVAL
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.GemvPlan([], ws, bpw.KERNEL_BYTELANE, mlp=[p.job()])
+    assert ei.value.status == _lib.E_UNSUPPORTED
+    j = p.job()
+    j.d_t += 4  # misaligned
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.GemvPlan([], ws, mlp=[j])
+    assert ei.value.status == _lib.E_INVAL
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.GemvPlan([], ws[:64], mlp=[p.job()])
+    assert ei.value.status == _lib.E_SIZE
+    wide = UploadedPair(np.zeros((2, 16384), np.int8), np.zeros((2, 16384), np.int8), np.zeros(16384, np.int8),
+                        1.0, 1.0, 1.0, dev)
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.GemvPlan([], ws, mlp=[wide.job()])
+    assert ei.value.status == _lib.E_UNSUPPORTED
+    _run_plan([], [p.job()], dev)  # and a good pair still runs
+    p.check("after errors")

@@ -1,0 +1,50 @@
+"""The batch-1 GEMV's streaming loops keep their loads in flight: compiled for gfx950 (hipcc on the
+host, no GPU), each loop that holds the weight loads must wait only for the older register set
+(s_waitcnt vmcnt(N) with N > 0), never for every load in flight. A vmcnt(0) there halves the loads
+the kernel keeps in flight; it appeared once when a second copy of the loops was added to the kernel."""
+import collections
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from conftest import ROOT
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SRC = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_gemv.hip")
+
+
+def loop_bodies(asm: str) -> dict:
+    cur, blocks = None, collections.defaultdict(list)
+    for line in asm.split("\n"):
+        m = re.match(r"^(\.LBB\d+_\d+|; %bb\.\d+):(.*)$", line)
+        if m:
+            c = m.group(2)
+            h = re.search(r"Header=BB(\d+_\d+)", c)
+            if "Loop Header" in c and m.group(1).startswith(".LBB"):
+                cur = "BB" + m.group(1).split("LBB")[1]
+            elif h:
+                cur = "BB" + h.group(1)
+            else:
+                cur = None
+            continue
+        if cur and line.startswith("\t") and not line.strip().startswith(";"):
+            blocks[cur].append(line.strip())
+    return blocks
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
+def test_streaming_loops_wait_only_for_the_older_loads(tmp_path):
+    out = tmp_path / "gemv.s"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
+                    SRC, "-o", str(out)], check=True, capture_output=True)
+    loops = {k: b for k, b in loop_bodies(out.read_text()).items()
+             if sum("buffer_load_dwordx4" in x for x in b) >= 4}
+    # the 2560-column loop (2 x 5 beat loads), the 6912-column loop (2 x 4) and the generic K = 2 one
+    assert sorted(sum("buffer_load_dwordx4" in x for x in b) for b in loops.values()) == [4, 8, 10], loops.keys()
+    for name, body in loops.items():
+        waits = [int(m.group(1)) for x in body if (m := re.search(r"vmcnt\((\d+)\)", x))]
+        assert waits and min(waits) > 0, f"loop {name}: vmcnt waits {waits}"
