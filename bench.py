@@ -100,6 +100,17 @@ class DecodeSet:
         return self.copies[i % len(self.copies)][0]
 
 
+def settle(torch, fn, min_ms: float = 40.0) -> None:
+    """Run fn (a few launches) until min_ms of wall time has passed. Under sustained load the GPU's
+    clocks take about 20 ms to ramp up (measured: 50-step blocks of the decode step at 103, 90, 84,
+    82 us, then 81.5 us; again after 2 s idle), so every measurement that follows host work or idle
+    time runs this first."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < min_ms:
+        fn()
+        torch.cuda.synchronize()
+
+
 def time_steps(torch, dset, steps: int) -> tuple[float, float]:
     """Run `steps` decode steps back to back (one GEMV launch each, plans in rotation) between two
     HIP events on the launch stream. Returns (GPU ms per step from the events, wall ms per step);
@@ -138,10 +149,11 @@ def prologue_measure(bpw, torch, synth, dev, ds, steps: int = 100) -> dict:
                 for m, (x, _), (oi, of), sd in zip(mats, ds.xs, ds.outs, scales)]
         ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
         plans.append((bpw.GemvPlan(jobs, ws), ws))
-    for i in range(5):
-        qplan.run()
-        plans[i % len(plans)][0].run()
-    torch.cuda.synchronize()
+    def some():
+        for i in range(10):
+            qplan.run()
+            plans[i % len(plans)][0].run()
+    settle(torch, some)
     a, b, c = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     a.record()
     for i in range(steps):
@@ -183,9 +195,10 @@ def intmlp_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
                 jobs.append(bpw.gemv_job(mats[i], x, s, oi, of))
         ws = torch.empty(bpw.bpw_gemv_intmlp_workspace_bytes(jobs, pairs), dtype=torch.uint8, device=dev)
         plans.append((bpw.GemvPlan(jobs, ws, mlp=pairs), ws))
-    for i in range(10):
-        plans[i % len(plans)][0].run()
-    torch.cuda.synchronize()
+    def some():
+        for i in range(10):
+            plans[i % len(plans)][0].run()
+    settle(torch, some)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for i in range(steps):
@@ -204,8 +217,7 @@ def probe_gbs(bpw, torch, dev) -> float:
     n = 4 << 30
     buf = torch.zeros(n, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    bpw.bpw_stream_read_probe(buf, sink)
-    torch.cuda.synchronize()
+    settle(torch, lambda: bpw.bpw_stream_read_probe(buf, sink))
     best = 0.0
     for _ in range(5):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -227,9 +239,7 @@ def head_measure(bpw, torch, synth, dev, reps: int = 20) -> dict:
     wd = [torch.from_numpy(w.view(np.int16)).to(dev) for _ in range(2)]
     xd = torch.from_numpy(x.view(np.int16)).to(dev)
     y = torch.empty(rows, dtype=torch.float32, device=dev)
-    for i in range(3):
-        bpw.bpw_dense_head_gemv(wd[i % 2], xd, y)
-    torch.cuda.synchronize()
+    settle(torch, lambda: [bpw.bpw_dense_head_gemv(wd[i % 2], xd, y) for i in range(4)])
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for i in range(reps):
         ev[i][0].record()
@@ -271,8 +281,7 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0)
             with torch.cuda.graph(graph):
                 for i in range(reps):
                     bpw.bpw_gemm_small_batch(mats[i % 64], Xd, sc, oi, of, kernel)
-            graph.replay()
-            torch.cuda.synchronize()
+            settle(torch, graph.replay, 20.0)
             times = []
             for _ in range(5):
                 a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -297,9 +306,7 @@ def z_sweep_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
     out = []
     for z in synth.P_ZERO_SWEEP:
         ds = DecodeSet(bpw, torch, synth, dev, copies=2, p_zero=z, base=BASE_SEED + 13, layers=lambda l: 0)
-        for i in range(4):
-            ds.plan(i).run()
-        torch.cuda.synchronize()
+        settle(torch, lambda: [ds.plan(i).run() for i in range(10)])
         ms = statistics.median(time_steps(torch, ds, reps)[0] for _ in range(3))
         out.append({"p_zero": z, "gemv_us": round(ms * 1e3, 2),
                     "weight_gbs": round(ds.plane_bytes / (ms * 1e-3) / 1e9, 1)})
@@ -348,7 +355,8 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=500,
+                    help="untimed steps first (the clocks need about 250 decode steps, ~20 ms, to ramp up)")
     ap.add_argument("--copies", type=int, default=3, help="HBM copies of the weight set used in rotation")
     ap.add_argument("--kernel", choices=("auto", "bitserial", "bytelane"), default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -291,9 +291,12 @@ inline int64_t units_of(int64_t rows, const Geometry &g) {
     return (rows + rpi - 1) / rpi;
 }
 
-// Row-groups in one bit-serial tile of a job: kTileUnits, or fewer where kTileRows caps the rows.
+// Row-groups in one bit-serial tile of a job: 16, or fewer where kTileRows caps the rows; a pair's
+// tile holds half as many of each matrix. (Measured on the decode step: 16 beat 12 and 24, and 24
+// for the 6912-column rows alone was 1 us slower.)
+constexpr int64_t kTileUnits = 16;
 inline int64_t tile_units(const Geometry &g) {
-    return std::min<int64_t>(bpw::kTileUnits, bpw::kTileRows / (64 >> g.glog));
+    return std::min<int64_t>(kTileUnits, bpw::kTileRows / (64 >> g.glog));
 }
 
 int64_t bitserial_tiles(const bpw_gemv_job &j) {
@@ -354,6 +357,20 @@ bpw_status check_job(const bpw_gemv_job &j, int32_t i, const char *kind = "job")
     if (!j.d_out_i32) return fail(BPW_E_INVAL, "%s: d_out_i32 is NULL", who);
     if (!std::isfinite(j.x_scale)) return fail(BPW_E_INVAL, "%s: x_scale is not finite", who);
     return BPW_OK;
+}
+
+// The dispatcher hands workgroup b of a launch to XCD b mod X in turn, and each XCD has its own L2
+// and address-translation caches. Permuting the tile table so that XCD x runs one contiguous run of
+// it (instead of every X-th tile) keeps the tiles an XCD streams at the same time on nearby
+// addresses, and its activation vectors in its own L2. Measured on the decode-step set: 83.6 us with
+// every X-th tile per XCD, 82.0 us with contiguous runs (a seeded shuffle of the tiles: 87.2 us).
+template <class T>
+void xcd_contiguous(T *tiles, int64_t n, int X) {
+    if (X <= 1 || n <= X) return;
+    std::vector<T> src(tiles, tiles + n);
+    std::vector<int64_t> start(X + 1, 0);
+    for (int x = 0; x < X; ++x) start[x + 1] = start[x] + (n - x + X - 1) / X;  // blocks b with b % X == x
+    for (int64_t b = 0; b < n; ++b) tiles[b] = src[start[b % X] + b / X];
 }
 
 // Widest pair whose t = relu(a_g)^2 * a_u cannot overflow int64: |a| <= 128 * cols < 2^21.
@@ -595,8 +612,30 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
     auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
     auto *hb = reinterpret_cast<bpw::Tile *>(host.data() + L.work_off);
+    // Tile-table order: the plain jobs in the order given, with the pairs merged in where their
+    // share of the pairs' bytes matches the plain jobs' share so far (for a decode step: each layer's
+    // pair beside its other projections). With the table laid out per XCD below, this gives every
+    // XCD the same mix of shapes.
+    std::vector<int32_t> order;
+    order.reserve(n_all);
+    {
+        double tot_j = 0, tot_p = 0, done_j = 0, done_p = 0;
+        for (int32_t i = 0; i < n_jobs; ++i) tot_j += (double)jobs[i].m.rows * (double)jobs[i].m.bpr;
+        for (int32_t i = 0; i < n_mlp; ++i) tot_p += 2.0 * (double)mlp[i].gate.rows * (double)mlp[i].gate.bpr;
+        int32_t a = 0, b = 0;
+        while (a < n_jobs || b < n_mlp) {
+            const bool take_pair = b < n_mlp && (a >= n_jobs || done_p * tot_j <= done_j * tot_p);
+            if (take_pair) {
+                done_p += 2.0 * (double)mlp[b].gate.rows * (double)mlp[b].gate.bpr;
+                order.push_back(n_jobs + b++);
+            } else {
+                done_j += (double)jobs[a].m.rows * (double)jobs[a].m.bpr;
+                order.push_back(a++);
+            }
+        }
+    }
     int64_t t = 0;
-    for (int32_t i = 0; i < n_all; ++i) {
+    for (const int32_t i : order) {
         const bool pair = i >= n_jobs;
         const bpw_dev_mat &m = pair ? mlp[i - n_jobs].gate : jobs[i].m;
         const Geometry g = geometry_for(m.bpr, bitserial);
@@ -634,7 +673,8 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         if (!bitserial) {
             for (int64_t r0 = 0; r0 < m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
         } else {
-            // tiles of one job in row order; jobs in the order given, pairs after the plain jobs
+            // tiles of one job in row order; jobs in the order given, pairs after the plain jobs (the
+            // whole table is then laid out per XCD, below)
             const int64_t U = units_of(m.rows, g), tu = pair ? tile_units(g) / 2 : tile_units(g);
             for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
         }
@@ -644,6 +684,12 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         delete plan;
         return fail(BPW_E_UNSUPPORTED, "internal: %lld tiles written, %lld expected", (long long)t, (long long)L.n_work);
     }
+    int xccs = 1;
+    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs < 1) xccs = 1;
+    if (bitserial)
+        xcd_contiguous(hb, t, xccs);
+    else
+        xcd_contiguous(ht, t, xccs);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");

@@ -18,7 +18,6 @@ constexpr int kSBThreads = 64 * kSBWaves;
 constexpr int kXPassBlocks = 128;         // activation-plane blocks held in LDS per pass (8 KiB)
 static_assert(kXPassBlocks == 64 * kKMaxBitSerial, "a wide row's pass is one full wave of lanes x kKMaxBitSerial");
 constexpr int kTileRows = 1024;           // most rows of one bit-serial GEMV tile (its sums sit in LDS)
-constexpr int kTileUnits = 16;            // row-groups of one bit-serial GEMV tile (fewer at a job's end)
 constexpr int kIters = 4;                 // row-iterations per wave per tile
 
 // One GEMV of a grouped launch, as the kernels read it (lives in the caller's workspace).
@@ -46,8 +45,6 @@ struct DevJob {
     float w_scale_up;
     int32_t pad;
 };
-
-constexpr int kPairTileUnits = kTileUnits / 2;  // row-groups of each matrix in one IntMlp pair tile
 
 // A tile of the bit-serial GEMV: consecutive row-groups ("units" of 64 / G rows) [u0, u1) of one
 // job, at most kTileRows rows, run by one workgroup.
