@@ -128,6 +128,23 @@ bpw_status check_device() {
     return BPW_OK;
 }
 
+// XCDs of the current device (hipDeviceAttributeNumberOfXccs; 1 if the runtime cannot say), cached
+// per device. Workgroup b of a launch runs on XCD b mod this count.
+std::atomic<int> g_xcds[64];
+int device_xcds() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    const int slot = dev >= 0 && dev < 64 ? dev : -1;
+    if (slot >= 0) {
+        const int v = g_xcds[slot].load(std::memory_order_acquire);
+        if (v > 0) return v;
+    }
+    int n = 1;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || n < 1) n = 1;
+    if (slot >= 0) g_xcds[slot].store(n, std::memory_order_release);
+    return n;
+}
+
 bpw_status hip_status(int e, const char *what) {
     if (e == hipSuccess) return BPW_OK;
     return fail(BPW_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
@@ -684,8 +701,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         delete plan;
         return fail(BPW_E_UNSUPPORTED, "internal: %lld tiles written, %lld expected", (long long)t, (long long)L.n_work);
     }
-    int xccs = 1;
-    if (hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess || xccs < 1) xccs = 1;
+    const int xccs = device_xcds();
     if (bitserial)
         xcd_contiguous(hb, t, xccs);
     else
@@ -896,8 +912,6 @@ bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t c
     if (cols % 8 != 0) return fail(BPW_E_UNSUPPORTED, "dense head: cols %lld is not a multiple of 8", (long long)cols);
     if (((uintptr_t)d_w_bf16 & 15u) || ((uintptr_t)d_x_bf16 & 15u))
         return fail(BPW_E_INVAL, "dense head: W and x must be 16-byte aligned");
-    if (cols * 2 > 64 * 1024)
-        return fail(BPW_E_UNSUPPORTED, "dense head: cols %lld exceed the 32768 staged in LDS", (long long)cols);
     bpw_status st = check_device();
     if (st) return st;
     return hip_status(bpw::launch_dense_head(d_w_bf16, rows, cols, d_x_bf16, d_y, stream), "dense head launch");

@@ -205,7 +205,8 @@ def test_dense_head_full_128256x2560(dev):
     assert np.all(err <= 1e-3 * rs + 1e-5), f"max err/bound {np.max(err / (1e-3 * rs + 1e-5))}"
 
 
-@pytest.mark.parametrize("rows,cols", ((1, 8), (3, 64), (17, 136), (1000, 2560), (129, 32768), (64, 1024)))
+@pytest.mark.parametrize("rows,cols", ((1, 8), (3, 64), (17, 136), (1000, 2560), (9, 2560), (129, 32768), (64, 1024),
+                                       (5, 40008)))
 def test_dense_head_shapes(dev, rows, cols):
     log(f"case: dense head {rows}x{cols}")
     w, x = synth.head_case(rows * 7 + cols, rows=rows, cols=cols)
