@@ -21,7 +21,7 @@ __all__ = [
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
     "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
-    "bpw_gemm_small_batch", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
+    "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
 ]
 
@@ -313,6 +313,69 @@ def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, kernel: int =
         raise ValueError(f"x_scales must hold {batch} values")
     _lib.check(_lib.lib().bpw_gemm_small_batch(ctypes.byref(m.desc), _dptr(X), batch, ldx, xs.ctypes.data,
                                                _dptr(out_i32), _dptr(out_f32), kernel, _stream(stream)))
+
+
+class _SbJob:
+    """One grouped small-batch job; keeps its host scales alive until the plan has copied them."""
+
+    def __init__(self, m: DevMat, X, x_scales, out_i32, out_f32=None):
+        batch, ldx = X.shape
+        self.batch = batch
+        self.scales = np.ascontiguousarray(np.asarray(x_scales, dtype=np.float32))
+        if self.scales.shape != (batch,):
+            raise ValueError(f"x_scales must hold {batch} values")
+        j = _lib.BpwSbJob()
+        j.m = m.desc
+        j.d_X = _dptr(X)
+        j.ldx = ldx
+        j.x_scales = self.scales.ctypes.data
+        j.d_out_i32 = _dptr(out_i32)
+        j.d_out_f32 = _dptr(out_f32)
+        self.c = j
+
+
+def sb_job(m: DevMat, X, x_scales, out_i32, out_f32=None) -> _SbJob:
+    """One job of a grouped small-batch plan: X int8 GPU tensor [batch, ldx], x_scales host [batch],
+    outputs [batch, rows]."""
+    return _SbJob(m, X, x_scales, out_i32, out_f32)
+
+
+def _sb_array(jobs):
+    arr = (_lib.BpwSbJob * max(1, len(jobs)))(*[j.c for j in jobs])
+    return arr, len(jobs)
+
+
+def bpw_gemm_small_batch_workspace_bytes(jobs, batch: int) -> int:
+    arr, n = _sb_array(jobs)
+    return _lib.lib().bpw_gemm_small_batch_workspace_bytes(arr, n, batch)
+
+
+class SmallBatchPlan:
+    """bpw_sb_plan: several small-batch calls with one batch size, one launch per run()."""
+
+    def __init__(self, jobs, batch: int, d_ws, kernel: int = KERNEL_AUTO, stream=None):
+        if any(j.batch != batch for j in jobs):
+            raise ValueError(f"every job's X must hold batch = {batch} rows")
+        arr, n = _sb_array(jobs)
+        ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().bpw_gemm_small_batch_plan_create(arr, n, batch, kernel, _dptr(d_ws), ws_len,
+                                                               _stream(stream), ctypes.byref(h)))
+        self._h, self._keep = h, (jobs, d_ws)
+
+    def run(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_gemm_small_batch_plan_run(self._h, _stream(stream)))
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_gemm_small_batch_plan_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------------------ dense head

@@ -39,6 +39,11 @@ class BpwIntMlpJob(ctypes.Structure):
                 ("d_up_i32", ctypes.c_void_p)]
 
 
+class BpwSbJob(ctypes.Structure):
+    _fields_ = [("m", BpwDevMat), ("d_X", ctypes.c_void_p), ("ldx", ctypes.c_int64), ("x_scales", ctypes.c_void_p),
+                ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p)]
+
+
 class BpwQuantJob(ctypes.Structure):
     _fields_ = [("d_h", ctypes.c_void_p), ("d_g", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("d_q", ctypes.c_void_p), ("q_len", ctypes.c_int64), ("d_scale", ctypes.c_void_p),
@@ -95,6 +100,11 @@ def lib():
         "bpw_gemv_plan_run": (i32, [vp, vp]),
         "bpw_gemv_plan_free": (None, [vp]),
         "bpw_gemm_small_batch": (i32, [M, vp, i32, i64, vp, vp, vp, i32, vp]),
+        "bpw_gemm_small_batch_workspace_bytes": (sz, [ctypes.POINTER(BpwSbJob), i32, i32]),
+        "bpw_gemm_small_batch_plan_create": (i32, [ctypes.POINTER(BpwSbJob), i32, i32, i32, vp, sz, vp,
+                                                   ctypes.POINTER(vp)]),
+        "bpw_gemm_small_batch_plan_run": (i32, [vp, vp]),
+        "bpw_gemm_small_batch_plan_free": (None, [vp]),
         "bpw_quantize_workspace_bytes": (sz, [i32]),
         "bpw_quantize": (i32, [Q, i32, vp, sz, vp]),
         "bpw_quant_plan_create": (i32, [Q, i32, vp, sz, vp, ctypes.POINTER(vp)]),

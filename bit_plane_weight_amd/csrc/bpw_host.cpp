@@ -845,26 +845,59 @@ bpw_status bpw_quantize(const bpw_quant_job *jobs, int32_t n_jobs, void *d_ws, s
 // (6.9-7.8 us against 12.3-17.9 us).
 constexpr int32_t kMfmaFromBatch = 1;
 
+// Argument checks of one small-batch call (shared by the single call and the grouped plan).
+static bpw_status check_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
+                                    const float *x_scales, const int32_t *d_out_i32, const char *who) {
+    bpw_status st = check_dev_mat(m, who);
+    if (st) return st;
+    if (batch < 1 || batch > bpw::kMaxBatch) return fail(BPW_E_INVAL, "%s: batch %d outside [1, 64]", who, (int)batch);
+    if (!d_X || !x_scales || !d_out_i32) return fail(BPW_E_INVAL, "%s: NULL argument", who);
+    if (ldx < m->bpr * 64)
+        return fail(BPW_E_INVAL, "%s: ldx %lld < bpr * 64 = %lld", who, (long long)ldx, (long long)(m->bpr * 64));
+    if ((ldx % 16) != 0 || ((uintptr_t)d_X & 15u) != 0)
+        return fail(BPW_E_INVAL, "%s: X rows must be 16-byte aligned (X aligned, ldx %% 16 == 0)", who);
+    if ((uint64_t)(batch + 16) * (uint64_t)ldx >= 0xFFFFFFF0ull)
+        return fail(BPW_E_UNSUPPORTED, "%s: (batch + 16) * ldx exceeds the 32-bit offsets of X", who);
+    for (int32_t t = 0; t < batch; ++t)
+        if (!std::isfinite(x_scales[t])) return fail(BPW_E_INVAL, "%s: x_scales[%d] is not finite", who, (int)t);
+    if ((uint64_t)(m->rows + 64) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
+        return fail(BPW_E_UNSUPPORTED, "%s: plane bytes exceed the 32-bit offsets of one matrix", who);
+    return BPW_OK;
+}
+
+static bpw::SmallBatchArgs small_batch_args(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
+                                            const float *x_scales, int32_t *d_out_i32, float *d_out_f32) {
+    const Geometry g = geometry_for(m->bpr, true);
+    bpw::SmallBatchArgs a{};
+    a.planes = static_cast<const uint8_t *>(m->d_planes);
+    a.X = d_X;
+    a.out_i32 = d_out_i32;
+    a.out_f32 = d_out_f32;
+    a.ldx = ldx;
+    a.plane_bytes = (uint32_t)((uint64_t)m->rows * (uint64_t)m->bpr * 16u);
+    a.x_bytes = (uint32_t)((uint64_t)batch * (uint64_t)ldx);
+    a.rows = (int32_t)m->rows;
+    a.bpr = (int32_t)m->bpr;
+    a.batch = batch;
+    a.glog = g.glog;
+    a.kblk = g.kblk;
+    a.nchunk = g.nchunk;
+    a.w_scale = m->w_scale;
+    for (int32_t t = 0; t < batch; ++t) a.x_scales[t] = x_scales[t];
+    return a;
+}
+
 bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
                                 const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
                                 void *stream) {
-    bpw_status st = check_dev_mat(m, "small batch");
-    if (st) return st;
-    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_MFMA)
+    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_MFMA) {
+        bpw_status st = check_dev_mat(m, "small batch");
+        if (st) return st;
         return fail(BPW_E_UNSUPPORTED, "small batch: kernel %d is not available for this entry point", (int)kernel);
-    if (batch < 1 || batch > bpw::kMaxBatch) return fail(BPW_E_INVAL, "batch %d outside [1, 64]", (int)batch);
-    if (!d_X || !x_scales || !d_out_i32) return fail(BPW_E_INVAL, "small batch: NULL argument");
-    if (ldx < m->bpr * 64)
-        return fail(BPW_E_INVAL, "ldx %lld < bpr * 64 = %lld", (long long)ldx, (long long)(m->bpr * 64));
-    if ((ldx % 16) != 0 || ((uintptr_t)d_X & 15u) != 0)
-        return fail(BPW_E_INVAL, "small batch: X rows must be 16-byte aligned (X aligned, ldx %% 16 == 0)");
-    if ((uint64_t)(batch + 16) * (uint64_t)ldx >= 0xFFFFFFF0ull)
-        return fail(BPW_E_UNSUPPORTED, "small batch: (batch + 16) * ldx exceeds the 32-bit offsets of X");
-    for (int32_t t = 0; t < batch; ++t)
-        if (!std::isfinite(x_scales[t])) return fail(BPW_E_INVAL, "x_scales[%d] is not finite", (int)t);
+    }
+    bpw_status st = check_small_batch(m, d_X, batch, ldx, x_scales, d_out_i32, "small batch");
+    if (st) return st;
     const Geometry g = geometry_for(m->bpr, true);
-    if ((uint64_t)(m->rows + 64) * (uint64_t)m->bpr * 16u >= 0xFFFFFFF0ull)
-        return fail(BPW_E_UNSUPPORTED, "plane bytes exceed the 32-bit offsets of one matrix");
     st = check_device();
     if (st) return st;
     if (m->rows == 0) return BPW_OK;
@@ -881,28 +914,116 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
     groups = std::min<int64_t>(groups, batch);
     const int64_t tg = (batch + groups - 1) / groups;
     groups = (batch + tg - 1) / tg;
-    bpw::SmallBatchArgs a{};
-    a.planes = static_cast<const uint8_t *>(m->d_planes);
-    a.X = d_X;
-    a.out_i32 = d_out_i32;
-    a.out_f32 = d_out_f32;
-    a.ldx = ldx;
-    a.plane_bytes = (uint32_t)((uint64_t)m->rows * (uint64_t)m->bpr * 16u);
-    a.x_bytes = (uint32_t)((uint64_t)batch * (uint64_t)ldx);
-    a.rows = (int32_t)m->rows;
-    a.bpr = (int32_t)m->bpr;
-    a.batch = batch;
-    a.glog = g.glog;
-    a.kblk = g.kblk;
-    a.nchunk = g.nchunk;
+    bpw::SmallBatchArgs a = small_batch_args(m, d_X, batch, ldx, x_scales, d_out_i32, d_out_f32);
     a.tg = (int32_t)tg;
-    a.w_scale = m->w_scale;
-    for (int32_t t = 0; t < batch; ++t) a.x_scales[t] = x_scales[t];
     if (row_wgs > (int64_t)INT32_MAX) return fail(BPW_E_UNSUPPORTED, "small batch: too many rows for one launch");
     const bool mfma = kernel == BPW_KERNEL_MFMA || (kernel == BPW_KERNEL_AUTO && batch >= kMfmaFromBatch);
     if (mfma) return hip_status(bpw::launch_gemm_small_batch_mfma(a, stream), "small batch launch");
     return hip_status(bpw::launch_gemm_small_batch(a, (int32_t)row_wgs, (int32_t)groups, stream), "small batch launch");
 }
+
+// ---------------------------------------------------------------- grouped small batch
+
+struct bpw_sb_plan {
+    int device;
+    const bpw::SmallBatchArgs *jobs;
+    const bpw::SBTile *tiles;
+    int64_t n_tiles;
+};
+
+namespace {
+struct SBLayout {
+    size_t jobs_off, tiles_off, total;
+    int64_t n_tiles;
+};
+
+SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
+    SBLayout L{};
+    const int64_t groups = (batch + 15) / 16;
+    for (int32_t i = 0; i < n; ++i) L.n_tiles += (jobs[i].m.rows + 15) / 16 * groups;
+    L.jobs_off = 0;
+    L.tiles_off = align_up(sizeof(bpw::SmallBatchArgs) * (size_t)n);
+    L.total = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)L.n_tiles);
+    return L;
+}
+}  // namespace
+
+size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch) {
+    if (!jobs || n_jobs <= 0 || batch < 1) return 0;
+    return sb_layout(jobs, n_jobs, batch).total;
+}
+
+bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch, int32_t kernel,
+                                            void *d_ws, size_t ws_len, void *stream, bpw_sb_plan **out) {
+    if (!out) return fail(BPW_E_INVAL, "out is NULL");
+    *out = nullptr;
+    if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad job list");
+    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_MFMA)
+        return fail(BPW_E_UNSUPPORTED, "grouped small batch runs on the matrix cores only (kernel %d)", (int)kernel);
+    if (batch < 1 || batch > bpw::kMaxBatch) return fail(BPW_E_INVAL, "batch %d outside [1, 64]", (int)batch);
+    char who[48];
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        std::snprintf(who, sizeof who, "small-batch job %d", i);
+        const bpw_sb_job &j = jobs[i];
+        bpw_status st = check_small_batch(&j.m, j.d_X, batch, j.ldx, j.x_scales, j.d_out_i32, who);
+        if (st) return st;
+    }
+    const SBLayout L = sb_layout(jobs, n_jobs, batch);
+    if (L.n_tiles > (int64_t)INT32_MAX) return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
+    if (n_jobs > 0 && L.total > ws_len) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, L.total);
+    if (n_jobs > 0 && !d_ws) return fail(BPW_E_INVAL, "d_ws is NULL");
+    if (((uintptr_t)d_ws & (kAlign - 1)) != 0) return fail(BPW_E_INVAL, "d_ws must be 256-byte aligned");
+    bpw_status st = check_device();
+    if (st) return st;
+    auto *plan = new (std::nothrow) bpw_sb_plan;
+    if (!plan) return fail(BPW_E_INVAL, "out of host memory");
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    uint8_t *ws = static_cast<uint8_t *>(d_ws);
+    plan->device = dev;
+    plan->jobs = reinterpret_cast<const bpw::SmallBatchArgs *>(ws + L.jobs_off);
+    plan->tiles = reinterpret_cast<const bpw::SBTile *>(ws + L.tiles_off);
+    plan->n_tiles = L.n_tiles;
+    if (n_jobs == 0 || L.n_tiles == 0) {
+        *out = plan;
+        return BPW_OK;
+    }
+    std::vector<uint8_t> host(L.total, 0);
+    auto *hj = reinterpret_cast<bpw::SmallBatchArgs *>(host.data() + L.jobs_off);
+    auto *ht = reinterpret_cast<bpw::SBTile *>(host.data() + L.tiles_off);
+    const int32_t groups = (batch + 15) / 16;
+    int64_t t = 0;
+    for (int32_t i = 0; i < n_jobs; ++i) {
+        const bpw_sb_job &j = jobs[i];
+        hj[i] = small_batch_args(&j.m, j.d_X, batch, j.ldx, j.x_scales, j.d_out_i32, j.d_out_f32);
+        const int64_t rt = (j.m.rows + 15) / 16;
+        for (int64_t r = 0; r < rt; ++r)
+            for (int32_t gq = 0; gq < groups; ++gq) ht[t++] = bpw::SBTile{i, (int32_t)r, gq, 0};
+    }
+    xcd_contiguous(ht, t, device_xcds());
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    st = hip_status(hipMemcpyAsync(d_ws, host.data(), L.total, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+    if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
+    if (st) {
+        delete plan;
+        return st;
+    }
+    *out = plan;
+    return BPW_OK;
+}
+
+bpw_status bpw_gemm_small_batch_plan_run(const bpw_sb_plan *plan, void *stream) {
+    if (!plan) return fail(BPW_E_INVAL, "plan is NULL");
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != plan->device)
+        return fail(BPW_E_INVAL, "plan was created on device %d, current device is %d", plan->device, dev);
+    bpw_status st = check_device();
+    if (st) return st;
+    return hip_status(bpw::launch_gemm_small_batch_grouped(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
+                      "grouped small batch launch");
+}
+
+void bpw_gemm_small_batch_plan_free(bpw_sb_plan *plan) { delete plan; }
 
 bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t cols, const uint16_t *d_x_bf16,
                                float *d_y, void *stream) {

@@ -77,6 +77,15 @@ struct SmallBatchArgs {
     float x_scales[kMaxBatch];
 };
 
+// A tile of the grouped small-batch launch: rows 16 * row_tile .. +15 and tokens 16 * tok_group .. +15
+// of call `job`.
+struct SBTile {
+    int32_t job;
+    int32_t row_tile;
+    int32_t tok_group;
+    int32_t pad;
+};
+
 // One activation of the Folded quantiser (lives in the caller's workspace).
 struct QuantJob {
     const float *h;
@@ -95,6 +104,7 @@ int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles,
 int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_quantize(const QuantJob *jobs, int32_t n_jobs, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);

@@ -175,33 +175,39 @@ __device__ __forceinline__ v4i mfma_beat(const uint32_t *lut, const u32x4 &beat,
     return acc;
 }
 
-template <int WAVES>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(SmallBatchArgs A) {
-    static_assert(64 * WAVES >= 256, "every thread of the first four waves fills one table entry");
-    __shared__ uint32_t lut[256];
-    __shared__ v4i part[WAVES][64];
+// The decode table, filled by the first 256 threads of the workgroup (made visible by the barrier in
+// mfma_tile).
+__device__ __forceinline__ void fill_lut(uint32_t *lut) {
     if (threadIdx.x < 256) lut[threadIdx.x] = lut_entry(threadIdx.x);
+}
+
+// Rows 16 * row_tile .. +15 and tokens 16 * tok_group .. +15 of the call A, by the workgroup's WAVES
+// waves. part holds one partial per wave and lane.
+template <int WAVES>
+__device__ __forceinline__ void mfma_tile(const SmallBatchArgs &A, uint32_t row_tile, uint32_t tok_group,
+                                          const uint32_t *lut, v4i (*part)[64]) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const uint32_t row = blockIdx.x * kMfmaRows + (lane & 15);
-    const uint32_t tok = blockIdx.y * kMfmaTokens + (lane & 15);
+    const uint32_t row = row_tile * kMfmaRows + (lane & 15);
+    const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
     const int bq = lane >> 4;  // which block of the iteration's four this lane holds
     const int bpr = A.bpr;
     const int n_it = (bpr + 3) / 4;
+    const int64_t ldx = A.ldx;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(A.X, A.x_bytes);
     __syncthreads();  // the table is complete
     v4i acc = {0, 0, 0, 0};
     u32x4 beat0, beat1, x0[4], x1[4];
     int it = wave;
-    mfma_issue(beat0, x0, wr, xr, row, tok, 4 * it + bq, bpr, A.ldx, it < n_it);
+    mfma_issue(beat0, x0, wr, xr, row, tok, 4 * it + bq, bpr, ldx, it < n_it);
     // Two load sets alternate, as in the batch-1 kernel: iteration it + WAVES is in flight while
     // iteration it is multiplied; one trip covers two iterations with no exit in between.
     for (; it < n_it; it += 2 * WAVES) {
-        mfma_issue(beat1, x1, wr, xr, row, tok, 4 * (it + WAVES) + bq, bpr, A.ldx, it + WAVES < n_it);
+        mfma_issue(beat1, x1, wr, xr, row, tok, 4 * (it + WAVES) + bq, bpr, ldx, it + WAVES < n_it);
         asm volatile("" ::: "memory");
         acc = mfma_beat(lut, beat0, x0, acc);
-        mfma_issue(beat0, x0, wr, xr, row, tok, 4 * (it + 2 * WAVES) + bq, bpr, A.ldx, it + 2 * WAVES < n_it);
+        mfma_issue(beat0, x0, wr, xr, row, tok, 4 * (it + 2 * WAVES) + bq, bpr, ldx, it + 2 * WAVES < n_it);
         asm volatile("" ::: "memory");
         acc = mfma_beat(lut, beat1, x1, acc);
     }
@@ -213,8 +219,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(Small
     int32_t sum = 0;
 #pragma unroll
     for (int w = 0; w < WAVES; ++w) sum += part[w][l][r];
-    const int orow = blockIdx.x * kMfmaRows + 4 * (l >> 4) + r;
-    const int otok = blockIdx.y * kMfmaTokens + (l & 15);
+    const int orow = (int)row_tile * kMfmaRows + 4 * (l >> 4) + r;
+    const int otok = (int)tok_group * kMfmaTokens + (l & 15);
     if (orow < A.rows && otok < A.batch) {
         const int64_t idx = (int64_t)otok * A.rows + orow;
         A.out_i32[idx] = sum;
@@ -223,6 +229,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(Small
             A.out_f32[idx] = f * A.w_scale;                  // then the weight scale
         }
     }
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(SmallBatchArgs A) {
+    static_assert(64 * WAVES >= 256, "every thread of the first four waves fills one table entry");
+    __shared__ uint32_t lut[256];
+    __shared__ v4i part[WAVES][64];
+    fill_lut(lut);
+    mfma_tile<WAVES>(A, blockIdx.x, blockIdx.y, lut, part);
+}
+
+// Several calls in one launch: workgroup b runs tile tiles[b] (16 rows x up to 16 tokens of one
+// call) with four waves, whatever the row width.
+__global__ __launch_bounds__(256) void gemm_small_batch_mfma_grouped_kernel(const SmallBatchArgs *__restrict__ jobs,
+                                                                            const SBTile *__restrict__ tiles) {
+    __shared__ uint32_t lut[256];
+    __shared__ v4i part[4][64];
+    fill_lut(lut);
+    const SBTile t = tiles[blockIdx.x];
+    mfma_tile<4>(jobs[t.job], (uint32_t)t.row_tile, (uint32_t)t.tok_group, lut, part);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -236,6 +262,13 @@ int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream) {
         hipLaunchKernelGGL(gemm_small_batch_mfma_kernel<8>, dim3(row_wgs, groups), dim3(512), 0, as_stream(stream), a);
     else
         hipLaunchKernelGGL(gemm_small_batch_mfma_kernel<4>, dim3(row_wgs, groups), dim3(256), 0, as_stream(stream), a);
+    return hipGetLastError();
+}
+
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream) {
+    if (n_tiles <= 0) return hipSuccess;
+    hipLaunchKernelGGL(gemm_small_batch_mfma_grouped_kernel, dim3((unsigned)n_tiles), dim3(256), 0, as_stream(stream),
+                       jobs, tiles);
     return hipGetLastError();
 }
 

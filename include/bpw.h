@@ -274,6 +274,34 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
                                 const float *x_scales, int32_t *d_out_i32, float *d_out_f32, int32_t kernel,
                                 void *stream);
 
+/* Several small-batch calls in one launch (the same computation as bpw_gemm_small_batch per job,
+ * each beat decoded once per 16 tokens). All jobs of a plan share the batch size; their X, ldx and
+ * outputs follow the rules of bpw_gemm_small_batch. */
+typedef struct bpw_sb_job {
+    bpw_dev_mat m;
+    const int8_t *d_X;      /* device int8 [batch][ldx], 16-byte aligned, ldx % 16 == 0, ldx >= bpr * 64 */
+    int64_t ldx;
+    const float *x_scales;  /* host float [batch]: copied when the plan is made */
+    int32_t *d_out_i32;     /* device int32 [batch][rows] */
+    float *d_out_f32;       /* device float [batch][rows] or NULL */
+} bpw_sb_job;
+
+typedef struct bpw_sb_plan bpw_sb_plan;
+
+/* Device workspace bytes of a plan over these jobs at this batch size (0 if n_jobs <= 0). */
+size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch);
+
+/* Check the jobs, write the job and tile tables into d_ws (256-byte aligned; the call waits for the
+ * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues one launch for all of them on the
+ * int8 matrix cores (kernel AUTO or BPW_KERNEL_MFMA; others are BPW_E_UNSUPPORTED). 1 <= batch <= 64.
+ * The X buffers are read as they are when a run executes; the scales are the ones given here. The
+ * workspace, matrices, X and outputs must outlive the plan; outputs of different jobs must not
+ * overlap. */
+bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch, int32_t kernel,
+                                            void *d_ws, size_t ws_len, void *stream, bpw_sb_plan **out);
+bpw_status bpw_gemm_small_batch_plan_run(const bpw_sb_plan *plan, void *stream);
+void bpw_gemm_small_batch_plan_free(bpw_sb_plan *plan);
+
 /* ------------------------------------------------------------------------ dense head */
 
 /* The dense tied LM head at batch 1 (Tritium paper, "Where the bytes are"; format page 2.4):

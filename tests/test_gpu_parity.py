@@ -6,6 +6,7 @@ binary32 roundings, equal the oracle's fp32 bits). The bf16 head must satisfy
 |err| <= 1e-3 * sum|w*x| + 1e-5 per element. Inputs come from the seeded generator only;
 the oracle packs its own planes from the same trits.
 """
+import ctypes
 import os
 import sys
 
@@ -624,3 +625,80 @@ def test_intmlp_argument_errors(dev):
     assert ei.value.status == _lib.E_UNSUPPORTED
     _run_plan([], [p.job()], dev)  # and a good pair still runs
     p.check("after errors")
+
+
+# ----------------------------------------------------------------------------- grouped small batch
+
+GROUPED_SHAPES = ((6912, 2560), (2560, 6912), (640, 2560), (1, 1), (7, 65), (65, 129), (33, 8193), (129, 2500), (5, 0))
+
+
+def _sb_inputs(dev, seed, rows, cols, batch):
+    case = synth.ternary_case(seed, rows % 7, cols % 7, rows, cols)
+    u = Uploaded(case, dev)
+    bpr = (cols + 63) // 64
+    X, sc = synth.small_batch_x(seed + 1, batch, max(cols, 1))
+    ldx = bpr * 64 + 48
+    Xh = synth.u64(seed + 2, batch * ldx).astype(np.uint8).view(np.int8).reshape(batch, ldx).copy()
+    Xh[:, :cols] = X[:, :cols]
+    Xd = torch.from_numpy(Xh).to(dev)
+    oi = torch.full((batch, rows), -7, dtype=torch.int32, device=dev)
+    of = torch.full((batch, rows), -7.0, dtype=torch.float32, device=dev)
+    return case, u, Xh, Xd, sc, oi, of
+
+
+@pytest.mark.parametrize("batch", (1, 3, 16, 17, 64))
+def test_small_batch_grouped(dev, batch):
+    """Every shape (model widths, ragged tails, wide rows, no columns) as jobs of one grouped launch,
+    run twice; each job equals the oracle and the single-call matrix-core kernel bit for bit."""
+    log(f"case: grouped small batch B={batch}, {len(GROUPED_SHAPES)} jobs")
+    sets = [_sb_inputs(dev, 900 + 11 * i + batch, r, c, batch) for i, (r, c) in enumerate(GROUPED_SHAPES)]
+    jobs = [bpw.sb_job(u.m, Xd, sc, oi, of) for (case, u, Xh, Xd, sc, oi, of) in sets]
+    ws = torch.empty(max(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), 256), dtype=torch.uint8, device=dev)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws)
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    for (case, u, Xh, Xd, sc, oi, of) in sets:
+        acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), case.rows, case.cols, Xh, sc, case.w_scale,
+                                                nthreads=NT)
+        assert np.array_equal(oi.cpu().numpy(), acc), f"{case.rows}x{case.cols}"
+        assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32)), f"{case.rows}x{case.cols}"
+        oi2 = torch.empty_like(oi)
+        of2 = torch.empty_like(of)
+        bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi2, of2, bpw.KERNEL_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(oi2, oi) and torch.equal(of2.view(torch.int32), of.view(torch.int32))
+    plan.free()
+
+
+def test_small_batch_grouped_new_inputs_and_errors(dev):
+    log("case: grouped small batch plan reuse and argument errors")
+    batch = 4
+    case, u, Xh, Xd, sc, oi, of = _sb_inputs(dev, 950, 6912, 2560, batch)
+    jobs = [bpw.sb_job(u.m, Xd, sc, oi, of)]
+    ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws)
+    plan.run()
+    X2, _ = synth.small_batch_x(951, batch, 2560)
+    Xh2 = Xh.copy()
+    Xh2[:, :2560] = X2
+    Xd.copy_(torch.from_numpy(Xh2))
+    plan.run()  # reads the new contents, keeps the scales given at creation
+    torch.cuda.synchronize()
+    acc, y32, _ = oracle.gemm_small_batch(oracle.pack(case.w), 6912, 2560, Xh2, sc, case.w_scale, nthreads=NT)
+    assert np.array_equal(oi.cpu().numpy(), acc)
+    assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32))
+    plan.free()
+    for kernel in (bpw.KERNEL_BITSERIAL, bpw.KERNEL_BYTELANE):
+        with pytest.raises(bpw.BpwError) as ei:
+            bpw.SmallBatchPlan(jobs, batch, ws, kernel)
+        assert ei.value.status == _lib.E_UNSUPPORTED
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.SmallBatchPlan(jobs, batch, ws[:256])
+    assert ei.value.status == _lib.E_SIZE
+    with pytest.raises(ValueError):
+        bpw.SmallBatchPlan(jobs, batch + 1, ws)  # X holds fewer rows than the plan's batch
+    arr = (_lib.BpwSbJob * 1)(jobs[0].c)
+    h = ctypes.c_void_p()
+    assert _lib.lib().bpw_gemm_small_batch_plan_create(arr, 1, 65, 0, ws.data_ptr(), ws.numel(), None,
+                                                       ctypes.byref(h)) == _lib.E_INVAL
