@@ -300,6 +300,39 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0)
     return out
 
 
+def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50) -> list[dict]:
+    """The decode-step set (210 matrices, 521 MB of planes) at batch B: every matrix times its own B
+    int8 activation vectors, all in one grouped launch on the int8 matrix cores, the HBM copies in
+    rotation. Shows where the weight stream stops being the limit as B grows."""
+    import numpy as np
+    out = []
+    for batch in (1, 2, 4, 8, 16):
+        xs = []
+        for i, (layer, proj, name, rows, cols) in enumerate(ds.shapes):
+            X, sc = synth.small_batch_x(BASE_SEED + 1009 * i + batch, batch, cols)
+            xs.append((torch.from_numpy(X).to(dev), sc, torch.empty((batch, rows), dtype=torch.int32, device=dev),
+                       torch.empty((batch, rows), dtype=torch.float32, device=dev)))
+        plans = []
+        for _, mats, _ in ds.copies:
+            jobs = [bpw.sb_job(m, X, sc, oi, of) for m, (X, sc, oi, of) in zip(mats, xs)]
+            ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
+            plans.append((bpw.SmallBatchPlan(jobs, batch, ws), ws))
+        settle(torch, lambda: [plans[i % len(plans)][0].run() for i in range(6)])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            plans[i % len(plans)][0].run()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / steps * 1e3
+        out.append({"batch": batch, "us": round(us, 2), "weight_gbs": round(ds.plane_bytes / (us * 1e-6) / 1e9, 1),
+                    "tops_equiv": round(2.0 * ds.weights * batch / (us * 1e-6) / 1e12, 2)})
+        for p, _ in plans:
+            p.free()
+        del plans, xs
+    return out
+
+
 def z_sweep_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
     """Decode-step-shaped sets (one generated layer repeated over 30 layers, 2 HBM copies) at
     P(0) in the sweep; GEMV kernel median per step."""
@@ -473,6 +506,8 @@ def main() -> int:
         result["prologue"] = prologue_measure(bpw, torch, synth, dev, ds)
         log("IntMlp pairs")
         result["intmlp"] = intmlp_measure(bpw, torch, dev, ds)
+        log("grouped small batch over the decode-step set")
+        result["small_batch_decode_step"] = grouped_small_batch_measure(bpw, torch, synth, dev, ds)
         del ds
         torch.cuda.empty_cache()
         log("probe")

@@ -77,8 +77,10 @@ struct SmallBatchArgs {
     float x_scales[kMaxBatch];
 };
 
-// A tile of the grouped small-batch launch: rows 16 * row_tile .. +15 and tokens 16 * tok_group .. +15
-// of call `job`.
+// A tile of the grouped small-batch launch: rows kSBGroupRows * row_tile .. +kSBGroupRows-1 and tokens
+// 16 * tok_group .. +15 of call `job` (4 waves x kSBWaveTiles row tiles of 16 rows).
+constexpr int kSBWaveTiles = 2;
+constexpr int kSBGroupRows = 4 * kSBWaveTiles * 16;
 struct SBTile {
     int32_t job;
     int32_t row_tile;

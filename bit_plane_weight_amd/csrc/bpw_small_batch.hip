@@ -240,15 +240,91 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_batch_mfma_kernel(Small
     mfma_tile<WAVES>(A, blockIdx.x, blockIdx.y, lut, part);
 }
 
-// Several calls in one launch: workgroup b runs tile tiles[b] (16 rows x up to 16 tokens of one
-// call) with four waves, whatever the row width.
+// A beat load without the non-temporal hint. One iteration reads 64 of the 128 bytes of a row's cache
+// line and the next iteration the other 64; with the hint the fetch counter showed 1.68x the plane
+// bytes read from HBM on the decode-step set, cached it shows 1.02x (batch 2).
+__device__ __forceinline__ u32x4 load_beat_cached(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Several calls in one launch. Workgroup b runs tile tiles[b]: kSBGroupRows rows x up to 16 tokens of
+// one call. Each wave owns kSBWaveTiles row tiles of 16 rows over every block of the row (no split of
+// the row across waves, so a wave streams a whole row tile with its next iteration in flight); the
+// activation pieces it loads for an iteration serve all of its row tiles. Results leave straight from
+// the matrix-core registers.
+template <int RT>
+__device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_t rt0, uint32_t tok_group,
+                                                const uint32_t *lut) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
+    const int bq = lane >> 4;
+    const int bpr = A.bpr;
+    const int n_it = (bpr + 3) / 4;
+    const int64_t ldx = A.ldx;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(A.X, A.x_bytes);
+    uint32_t row[RT];
+    bool live[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        row[r] = (rt0 + r) * kMfmaRows + (lane & 15);
+        live[r] = (int)((rt0 + r) * kMfmaRows) < A.rows;
+    }
+    v4i acc[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) acc[r] = v4i{0, 0, 0, 0};
+    u32x4 b0[RT], b1[RT], x0[4], x1[4];
+    auto issue = [&](u32x4 (&beat)[RT], u32x4 (&xv)[4], int it) {
+        const int b = 4 * it + bq;
+        const bool in = it < n_it && b < bpr;
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+            beat[r] = load_beat_cached(wr, (in && live[r]) ? (row[r] * (uint32_t)bpr + (uint32_t)b) * 16u : kOutOfRange);
+        const uint32_t xo = (uint32_t)((int64_t)tok * ldx + (int64_t)b * 64);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            xv[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? xo + 16u * m : kOutOfRange, 0, 0));
+    };
+    int it = 0;
+    issue(b0, x0, it);
+    for (; it < n_it; it += 2) {
+        issue(b1, x1, it + 1);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = mfma_beat(lut, b0[r], x0, acc[r]);
+        issue(b0, x0, it + 2);
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int r = 0; r < RT; ++r) acc[r] = mfma_beat(lut, b1[r], x1, acc[r]);
+    }
+    // lane l, register i of row tile r: row 16 (rt0 + r) + 4 (l / 16) + i, token l % 16
+    const int otok = (int)tok;
+    if (otok >= A.batch) return;
+    const float xs = A.x_scales[otok];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int orow = (int)(rt0 + r) * kMfmaRows + 4 * (lane >> 4) + i;
+            if (orow < A.rows) {
+                const int64_t idx = (int64_t)otok * A.rows + orow;
+                const int32_t sum = acc[r][i];
+                A.out_i32[idx] = sum;
+                if (A.out_f32) A.out_f32[idx] = ((float)sum * xs) * A.w_scale;  // the scales in turn
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void gemm_small_batch_mfma_grouped_kernel(const SmallBatchArgs *__restrict__ jobs,
                                                                             const SBTile *__restrict__ tiles) {
     __shared__ uint32_t lut[256];
-    __shared__ v4i part[4][64];
     fill_lut(lut);
+    __syncthreads();  // the table is complete
     const SBTile t = tiles[blockIdx.x];
-    mfma_tile<4>(jobs[t.job], (uint32_t)t.row_tile, (uint32_t)t.tok_group, lut, part);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    mfma_wave_tiles<kSBWaveTiles>(jobs[t.job], (uint32_t)(t.row_tile * 4 * kSBWaveTiles + wave * kSBWaveTiles),
+                                  (uint32_t)t.tok_group, lut);
 }
 
 // ------------------------------------------------------------------------------------------

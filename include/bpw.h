@@ -292,8 +292,10 @@ typedef struct bpw_sb_plan bpw_sb_plan;
 size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch);
 
 /* Check the jobs, write the job and tile tables into d_ws (256-byte aligned; the call waits for the
- * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues one launch for all of them on the
- * int8 matrix cores (kernel AUTO or BPW_KERNEL_MFMA; others are BPW_E_UNSUPPORTED). 1 <= batch <= 64.
+ * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues one launch for all of them:
+ * on the int8 matrix cores (BPW_KERNEL_MFMA, or AUTO at batch >= 2), or at batch 1 under AUTO as the
+ * bit-serial batch-1 grouped GEMV (the same integers and floats, bit for bit). Other kernels are
+ * BPW_E_UNSUPPORTED. 1 <= batch <= 64.
  * The X buffers are read as they are when a run executes; the scales are the ones given here. The
  * workspace, matrices, X and outputs must outlive the plan; outputs of different jobs must not
  * overlap. */

@@ -646,15 +646,17 @@ def _sb_inputs(dev, seed, rows, cols, batch):
     return case, u, Xh, Xd, sc, oi, of
 
 
+@pytest.mark.parametrize("kernel", (bpw.KERNEL_AUTO, bpw.KERNEL_MFMA))
 @pytest.mark.parametrize("batch", (1, 3, 16, 17, 64))
-def test_small_batch_grouped(dev, batch):
+def test_small_batch_grouped(dev, batch, kernel):
     """Every shape (model widths, ragged tails, wide rows, no columns) as jobs of one grouped launch,
-    run twice; each job equals the oracle and the single-call matrix-core kernel bit for bit."""
-    log(f"case: grouped small batch B={batch}, {len(GROUPED_SHAPES)} jobs")
+    run twice; each job equals the oracle and the single-call matrix-core kernel bit for bit. (AUTO at
+    batch 1 runs the batch-1 GEMV.)"""
+    log(f"case: grouped small batch B={batch} kernel={kernel}, {len(GROUPED_SHAPES)} jobs")
     sets = [_sb_inputs(dev, 900 + 11 * i + batch, r, c, batch) for i, (r, c) in enumerate(GROUPED_SHAPES)]
     jobs = [bpw.sb_job(u.m, Xd, sc, oi, of) for (case, u, Xh, Xd, sc, oi, of) in sets]
     ws = torch.empty(max(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), 256), dtype=torch.uint8, device=dev)
-    plan = bpw.SmallBatchPlan(jobs, batch, ws)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws, kernel)
     plan.run()
     plan.run()
     torch.cuda.synchronize()
