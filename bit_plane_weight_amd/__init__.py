@@ -23,6 +23,7 @@ __all__ = [
     "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
     "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
+    "TritFile", "TritFormatError", "TritTensor", "bpw_fnv1a64", "TRIT_F32", "TRIT_TERNARY", "TRIT_BF16",
 ]
 
 
@@ -374,6 +375,101 @@ class SmallBatchPlan:
     def __del__(self):
         try:
             self.free()
+        except Exception:
+            pass
+
+
+# ------------------------------------------------------------------------------ .trit v1 container
+
+TRIT_F32, TRIT_TERNARY, TRIT_BF16 = 0, 1, 2
+
+
+class TritFormatError(BpwError):
+    """A failed container check: check is its number in the format page's section 4 (1..19)."""
+
+    def __init__(self, status: int, reason: str, e):
+        super().__init__(status, reason, e.row, e.beat, e.col)
+        self.check, self.offset, self.tensor = e.check, e.offset, e.tensor
+
+
+class TritTensor:
+    def __init__(self, t, index: int):
+        self.index = index
+        self.name = ctypes.string_at(t.name, t.name_len).decode("utf-8")
+        self.dtype, self.dims = t.dtype, list(t.dims[: t.ndim])
+        self.scale, self.offset, self.byte_len = t.scale, t.offset, t.byte_len
+        self._data = t.data
+
+    def bytes(self) -> bytes:
+        return ctypes.string_at(self._data, self.byte_len) if self.byte_len else b""
+
+
+def bpw_fnv1a64(data) -> int:
+    buf = np.frombuffer(memoryview(data), dtype=np.uint8)
+    return _lib.lib().bpw_fnv1a64(buf.ctypes.data if buf.size else None, buf.size)
+
+
+class TritFile:
+    """bpw_trit_file: a .trit v1 container in host memory (bytes, bytearray, mmap, numpy uint8), opened
+    with checks 1-16; verify() runs checks 17-19. The object keeps the buffer alive."""
+
+    def __init__(self, data):
+        self._buf = np.frombuffer(memoryview(data), dtype=np.uint8)
+        self._h = ctypes.c_void_p()
+        err = _lib.BpwTritErr()
+        st = _lib.lib().bpw_trit_open(self._buf.ctypes.data if self._buf.size else None, self._buf.size,
+                                      ctypes.byref(self._h), ctypes.byref(err))
+        if st != _lib.OK:
+            raise TritFormatError(st, _lib.lib().bpw_last_error().decode(), err)
+
+    def verify(self, check_hash: bool = True) -> None:
+        err = _lib.BpwTritErr()
+        st = _lib.lib().bpw_trit_verify(self._h, int(bool(check_hash)), ctypes.byref(err))
+        if st != _lib.OK:
+            raise TritFormatError(st, _lib.lib().bpw_last_error().decode(), err)
+
+    def __len__(self) -> int:
+        return _lib.lib().bpw_trit_tensor_count(self._h)
+
+    def tensor(self, index: int) -> TritTensor:
+        t = _lib.BpwTritTensor()
+        _lib.check(_lib.lib().bpw_trit_tensor_info(self._h, index, ctypes.byref(t)))
+        return TritTensor(t, index)
+
+    @property
+    def tensors(self) -> list:
+        return [self.tensor(i) for i in range(len(self))]
+
+    def find(self, name: str) -> int:
+        nb = name.encode("utf-8")
+        return _lib.lib().bpw_trit_find(self._h, nb, len(nb))
+
+    @property
+    def config(self) -> bytes:
+        p, n = ctypes.c_void_p(), ctypes.c_size_t()
+        _lib.check(_lib.lib().bpw_trit_config(self._h, ctypes.byref(p), ctypes.byref(n)))
+        return ctypes.string_at(p, n.value) if n.value else b""
+
+    @property
+    def stored_hash(self) -> int:
+        return _lib.lib().bpw_trit_stored_hash(self._h)
+
+    def load(self, index: int) -> HostMat:
+        """A ternary tensor as a validated host matrix (for bpw_upload)."""
+        t = self.tensor(index)
+        h = ctypes.c_void_p()
+        err = _lib.BpwErr()
+        _lib.check(_lib.lib().bpw_trit_load(self._h, index, ctypes.byref(h), ctypes.byref(err)), err)
+        return HostMat(h.value, t.dims[0], t.dims[1], t.scale)
+
+    def close(self) -> None:
+        if self._h:
+            _lib.lib().bpw_trit_close(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.close()
         except Exception:
             pass
 

@@ -9,7 +9,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libbpw.so")
 
 # bpw_status
-OK, E_INVAL, E_SIZE, E_P1_BOTH_BITS, E_P2_PADDING, E_NOT_VALIDATED, E_ARCH, E_HIP, E_UNSUPPORTED = range(9)
+OK, E_INVAL, E_SIZE, E_P1_BOTH_BITS, E_P2_PADDING, E_NOT_VALIDATED, E_ARCH, E_HIP, E_UNSUPPORTED, E_FORMAT = range(10)
 # bpw_kernel
 KERNEL_AUTO, KERNEL_BITSERIAL, KERNEL_BYTELANE, KERNEL_MFMA = 0, 1, 2, 3
 ABI_VERSION = 1
@@ -18,6 +18,18 @@ ABI_VERSION = 1
 class BpwErr(ctypes.Structure):
     _fields_ = [("code", ctypes.c_int32), ("row", ctypes.c_int64), ("beat", ctypes.c_int64),
                 ("col", ctypes.c_int64)]
+
+
+class BpwTritErr(ctypes.Structure):
+    _fields_ = [("code", ctypes.c_int32), ("check", ctypes.c_int32), ("offset", ctypes.c_int64),
+                ("tensor", ctypes.c_int64), ("row", ctypes.c_int64), ("beat", ctypes.c_int64), ("col", ctypes.c_int64)]
+
+
+class BpwTritTensor(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_void_p), ("name_len", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("dims", ctypes.c_uint32 * 4), ("scale", ctypes.c_float),
+                ("reserved", ctypes.c_uint32), ("offset", ctypes.c_uint64), ("byte_len", ctypes.c_uint64),
+                ("data", ctypes.c_void_p)]
 
 
 class BpwDevMat(ctypes.Structure):
@@ -112,6 +124,16 @@ def lib():
         "bpw_quant_plan_free": (None, [vp]),
         "bpw_dense_head_gemv": (i32, [vp, i64, i64, vp, vp, vp]),
         "bpw_stream_read_probe": (i32, [vp, sz, vp, vp]),
+        "bpw_trit_open": (i32, [vp, sz, ctypes.POINTER(vp), ctypes.POINTER(BpwTritErr)]),
+        "bpw_trit_verify": (i32, [vp, i32, ctypes.POINTER(BpwTritErr)]),
+        "bpw_trit_close": (None, [vp]),
+        "bpw_trit_tensor_count": (i64, [vp]),
+        "bpw_trit_tensor_info": (i32, [vp, i64, ctypes.POINTER(BpwTritTensor)]),
+        "bpw_trit_find": (i64, [vp, ctypes.c_char_p, sz]),
+        "bpw_trit_config": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(sz)]),
+        "bpw_trit_stored_hash": (ctypes.c_uint64, [vp]),
+        "bpw_fnv1a64": (ctypes.c_uint64, [vp, sz]),
+        "bpw_trit_load": (i32, [vp, i64, ctypes.POINTER(vp), ctypes.POINTER(BpwErr)]),
         "bpw_cache_flush": (i32, [vp, sz, vp]),
     }
     for name, (res, args) in sig.items():

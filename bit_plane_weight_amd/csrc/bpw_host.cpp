@@ -40,6 +40,14 @@ bpw_status fail(bpw_status code, const char *fmt, ...) {
     return code;
 }
 
+}  // namespace
+
+namespace bpw {
+void record_error(const char *msg) { g_last_error = msg; }
+}  // namespace bpw
+
+namespace {
+
 void set_err(bpw_err *e, bpw_status code, int64_t row, int64_t beat, int64_t col) {
     if (e) {
         e->code = code;
@@ -450,6 +458,7 @@ const char *bpw_status_string(int32_t s) {
         case BPW_E_ARCH: return "BPW_E_ARCH";
         case BPW_E_HIP: return "BPW_E_HIP";
         case BPW_E_UNSUPPORTED: return "BPW_E_UNSUPPORTED";
+        case BPW_E_FORMAT: return "BPW_E_FORMAT";
         default: return "unknown status";
     }
 }

@@ -100,6 +100,9 @@ struct QuantJob {
     int32_t pad;
 };
 
+// Host side: record the reason of a failing call for bpw_last_error() (bpw_host.cpp).
+void record_error(const char *msg);
+
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
 // bit-serial: workgroup w runs tiles[w]

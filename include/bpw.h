@@ -55,7 +55,8 @@ typedef enum bpw_status {
     BPW_E_NOT_VALIDATED = 5,  /* a device matrix descriptor that bpw_upload did not produce */
     BPW_E_ARCH = 6,           /* the current device is not gfx950 */
     BPW_E_HIP = 7,            /* a HIP runtime call failed (the reason names it) */
-    BPW_E_UNSUPPORTED = 8     /* valid input outside what the kernels serve (the reason says why) */
+    BPW_E_UNSUPPORTED = 8,    /* valid input outside what the kernels serve (the reason says why) */
+    BPW_E_FORMAT = 9          /* a .trit container check failed (bpw_trit_err.check names it) */
 } bpw_status;
 
 /* Where a validation error sits. Fields not meaningful for the error are -1. */
@@ -303,6 +304,62 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
                                             void *d_ws, size_t ws_len, void *stream, bpw_sb_plan **out);
 bpw_status bpw_gemm_small_batch_plan_run(const bpw_sb_plan *plan, void *stream);
 void bpw_gemm_small_batch_plan_free(bpw_sb_plan *plan);
+
+/* ------------------------------------------------------------------------ .trit v1 container */
+
+/* A .trit v1 container ("The .trit format, version 1"): header, embedded config, tensor table and a
+ * 64-byte aligned payload of ternary (.trit v1 planes) and dense (F32, BF16) tensors. Opening runs
+ * the header checks 1-16 of its section 4 in O(tensor count); bpw_trit_verify runs checks 17-19
+ * (P1, P2 and the payload hash) in O(file size). The file is untrusted input: every failure is a
+ * status, none a crash. Fields are read and checked in file order, so the first failure in file
+ * order is the one reported. */
+typedef struct bpw_trit_file bpw_trit_file;
+
+typedef enum bpw_trit_dtype { BPW_TRIT_F32 = 0, BPW_TRIT_TERNARY = 1, BPW_TRIT_BF16 = 2 } bpw_trit_dtype;
+
+/* Where a container check failed. Fields that do not apply are -1 (check 0 when none failed). */
+typedef struct bpw_trit_err {
+    int32_t code;    /* a bpw_status: BPW_E_FORMAT, or BPW_E_P1_BOTH_BITS / BPW_E_P2_PADDING */
+    int32_t check;   /* the failed check, numbered as in the format page's section 4 (1..19) */
+    int64_t offset;  /* file offset of the offending field */
+    int64_t tensor;  /* tensor record index */
+    int64_t row, beat, col;  /* checks 17 and 18: first offending row, beat and column */
+} bpw_trit_err;
+
+/* One tensor of an opened container. name and data point into the caller's file bytes. */
+typedef struct bpw_trit_tensor {
+    const char *name;      /* UTF-8, name_len bytes, not NUL-terminated */
+    int64_t name_len;
+    int32_t dtype;         /* bpw_trit_dtype */
+    int32_t ndim;          /* 1..4 */
+    uint32_t dims[4];      /* outermost first; a ternary tensor is rows = dims[0], cols = dims[1] */
+    float scale;           /* finite, > 0 */
+    uint32_t reserved;
+    uint64_t offset;       /* from the payload start, a multiple of 64 */
+    uint64_t byte_len;
+    const uint8_t *data;   /* the tensor's bytes inside the file */
+} bpw_trit_tensor;
+
+/* Open a container held in host memory (for example a mapped file) and run checks 1-16. The handle
+ * borrows `bytes`, which must stay unchanged and alive until bpw_trit_close. err may be NULL. */
+bpw_status bpw_trit_open(const uint8_t *bytes, size_t len, bpw_trit_file **out, bpw_trit_err *err);
+/* Checks 17 (P1) and 18 (P2) on every ternary tensor in record order, then 19 (FNV-1a-64 of the
+ * bytes from the payload start to the end of the file against the stored hash) when check_hash is
+ * nonzero and a hash is stored (0 = absent). */
+bpw_status bpw_trit_verify(const bpw_trit_file *f, int32_t check_hash, bpw_trit_err *err);
+void bpw_trit_close(bpw_trit_file *f);
+int64_t bpw_trit_tensor_count(const bpw_trit_file *f);
+bpw_status bpw_trit_tensor_info(const bpw_trit_file *f, int64_t index, bpw_trit_tensor *out);
+/* Index of the tensor with this name, or -1. */
+int64_t bpw_trit_find(const bpw_trit_file *f, const char *name, size_t name_len);
+/* The embedded config (UTF-8 JSON as stored) and the stored payload hash (0 = absent). */
+bpw_status bpw_trit_config(const bpw_trit_file *f, const char **json, size_t *len);
+uint64_t bpw_trit_stored_hash(const bpw_trit_file *f);
+/* FNV-1a, 64-bit, of len bytes (the container's payload hash). */
+uint64_t bpw_fnv1a64(const uint8_t *data, size_t len);
+/* A ternary tensor of an opened container as a host matrix, ready for bpw_upload: its planes are
+ * copied and validated exactly as bpw_load does (P1, P2), with the record's scale as w_scale. */
+bpw_status bpw_trit_load(const bpw_trit_file *f, int64_t index, bpw_host_mat **out, bpw_err *err);
 
 /* ------------------------------------------------------------------------ dense head */
 

@@ -83,7 +83,7 @@ def test_fnv1a64_published_vectors():
 # tensor_count 41, record 45: name_len 45, name 47, dtype 48, ndim 49, reserved0 50, reserved1 51,
 # dims 52..59, scale 60, flags 64, offset 68, byte_len 76; payload 128.
 
-@pytest.mark.parametrize("off,new,check", [
+CHECK_CASES = [
     (0, b"TRIX", 1),
     (4, struct.pack("<I", 0), 2),
     (4, struct.pack("<I", 2), 3),
@@ -107,7 +107,10 @@ def test_fnv1a64_published_vectors():
     (68, struct.pack("<Q", 32), 11),
     (68, struct.pack("<Q", 64), 12),
     (76, struct.pack("<Q", 48), 15),
-])
+]
+
+
+@pytest.mark.parametrize("off,new,check", CHECK_CASES)
 def test_each_check_fires_on_page_file(off, new, check):
     assert check_of(PAGE) == 0
     assert check_of(patched(PAGE, off, new)) == check
