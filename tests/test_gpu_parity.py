@@ -704,3 +704,36 @@ def test_small_batch_grouped_new_inputs_and_errors(dev):
     h = ctypes.c_void_p()
     assert _lib.lib().bpw_gemm_small_batch_plan_create(arr, 1, 65, 0, ws.data_ptr(), ws.numel(), None,
                                                        ctypes.byref(h)) == _lib.E_INVAL
+
+
+# ----------------------------------------------------------------------------- .trit container -> GPU
+
+
+def test_container_to_grouped_gemv(dev):
+    """One layer's seven projections written into a .trit v1 container (by the oracle's writer), opened
+    and verified by the library, loaded, uploaded and run as one grouped GEMV: equal to the oracle on
+    the same trits, bit for bit."""
+    from oracle import trit_container as tc
+    log("case: .trit container -> load -> upload -> grouped GEMV")
+    cases = synth.layer_cases(31337, 0)
+    data = tc.write(b'{"hidden_size": 2560}', [(c.name, tc.TRIT, [c.rows, c.cols], c.w_scale, oracle.pack(c.w).tobytes())
+                                               for c in cases], with_hash=False)
+    f = bpw.TritFile(data)
+    f.verify()
+    ups = []
+    for c in cases:
+        i = f.find(c.name)
+        assert i >= 0
+        hm = f.load(i)
+        u = Uploaded(c, dev)
+        buf = torch.empty(max(hm.nbytes, 1), dtype=torch.uint8, device=dev)
+        u.m, u.buf = bpw.bpw_upload(hm, buf), buf  # the container's planes, not the packer's
+        hm.free()
+        ups.append(u)
+    jobs = [u.job() for u in ups]
+    ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+    bpw.bpw_gemv(jobs, ws)
+    torch.cuda.synchronize()
+    for u in ups:
+        check_case(u, oracle_ref(u.case), f"container {u.case.name}")
+    f.close()
