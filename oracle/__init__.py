@@ -73,9 +73,14 @@ def _load():
         lib.oracle_dense_head.argtypes = [vp, i64, i64, vp, vp, vp, ci]
         lib.oracle_quantize.argtypes = [vp, vp, i64, f32, ci, vp, vp]
         lib.oracle_intmlp.argtypes = [vp, vp, i64, i64, i64, vp, i64, f32, f32, f32, vp, vp, vp, vp, ci, ep]
+        lib.oracle_bitcos_pack_flat.argtypes = [vp, i64, vp, vp, vp]
+        lib.oracle_bitcos_unpack_flat.argtypes = [vp, vp, i64, vp]
+        lib.oracle_bitcos_pack_rows.argtypes = [vp, i64, i64, vp, vp, vp]
+        lib.oracle_bitcos_gemv.argtypes = [vp, vp, vp, i64, i64, vp, f32, f32, vp, vp, vp, ci]
         for f in ("oracle_pack", "oracle_validate", "oracle_unpack", "oracle_gemv",
                   "oracle_gemv_bitserial", "oracle_gemm_small_batch", "oracle_dense_head", "oracle_quantize",
-                  "oracle_intmlp"):
+                  "oracle_intmlp", "oracle_bitcos_pack_flat", "oracle_bitcos_unpack_flat",
+                  "oracle_bitcos_pack_rows", "oracle_bitcos_gemv"):
             getattr(lib, f).restype = ci
         _lib = lib
     return _lib
@@ -213,3 +218,62 @@ def intmlp(gate_planes, up_planes, rows, cols, x, x_scale, w_gate, w_up, nthread
                                float(w_up), _p(t), _p(k), _p(ag), _p(au), int(nthreads), ctypes.byref(err))
     _check(rc, err)
     return t, float(k[0]), ag, au
+
+
+def bitcos_pack_flat(w):
+    """Flat BITCOS of a ternary array (any shape, flattened): (bitmap bytes, sign bytes, nnz)."""
+    w = np.ascontiguousarray(w, dtype=np.int8).reshape(-1)
+    n = w.size
+    bitmap = np.zeros(max((n + 7) // 8, 1), np.uint8)
+    signs = np.zeros(max((n + 7) // 8, 1), np.uint8)
+    nnz = np.zeros(1, np.int64)
+    rc = _load().oracle_bitcos_pack_flat(_p(w), n, _p(bitmap), _p(signs), _p(nnz))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    k = int(nnz[0])
+    return bitmap[: (n + 7) // 8].tobytes(), signs[: (k + 7) // 8].tobytes(), k
+
+
+def bitcos_unpack_flat(bitmap: bytes, signs: bytes, n: int) -> np.ndarray:
+    b = np.frombuffer(bitmap, np.uint8).copy() if bitmap else np.zeros(1, np.uint8)
+    s = np.frombuffer(signs, np.uint8).copy() if signs else np.zeros(1, np.uint8)
+    w = np.zeros(max(n, 1), np.int8)
+    rc = _load().oracle_bitcos_unpack_flat(_p(b), _p(s), n, _p(w))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    return w[:n]
+
+
+def bitcos_pack_rows(w):
+    """Row-form BITCOS of a [rows, cols] ternary matrix: (presence u64[rows*bpr], sign words u32,
+    row_start u32[rows+1])."""
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    rows, cols = w.shape
+    bpr = (cols + 63) // 64
+    row_start = np.zeros(rows + 1, np.uint32)
+    rc = _load().oracle_bitcos_pack_rows(_p(w), rows, cols, None, None, _p(row_start))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    presence = np.zeros(max(rows * bpr, 1), np.uint64)
+    signs = np.zeros(max(int(row_start[rows]), 1), np.uint32)
+    rc = _load().oracle_bitcos_pack_rows(_p(w), rows, cols, _p(presence), _p(signs), _p(row_start))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    return presence[: rows * bpr], signs[: int(row_start[rows])], row_start
+
+
+def bitcos_gemv(presence, signs, row_start, rows, cols, x, x_scale=1.0, w_scale=1.0, nthreads=1):
+    """Returns (acc int32[rows], y fp32[rows], y float64[rows]) from the row form."""
+    presence = np.ascontiguousarray(presence, dtype=np.uint64)
+    signs = np.ascontiguousarray(signs, dtype=np.uint32)
+    row_start = np.ascontiguousarray(row_start, dtype=np.uint32)
+    x = np.ascontiguousarray(x, dtype=np.int8)
+    acc = np.empty(max(rows, 1), np.int32)
+    y32 = np.empty(max(rows, 1), np.float32)
+    y64 = np.empty(max(rows, 1), np.float64)
+    rc = _load().oracle_bitcos_gemv(_p(presence) if presence.size else None, _p(signs) if signs.size else None,
+                                    _p(row_start), rows, cols, _p(x), float(x_scale), float(w_scale), _p(acc),
+                                    _p(y32), _p(y64), int(nthreads))
+    if rc != OK:
+        raise OracleError(rc, -1, -1, -1)
+    return acc[:rows], y32[:rows], y64[:rows]

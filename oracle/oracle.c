@@ -12,6 +12,7 @@
  *        layout" (Equations 2-3 in the introduction), "Invariants", "On popcount",
  *        "The hardware core", "Verification", "Numerics" (the Reference, Folded and IntMlp
  *        modes around the matvec).
+ *   [BC] "BITCOS: Intel's Ternary LLM Weight Format Goes Below 1.58 Bits" - "A bitmap and a sign".
  *   [TF] "The .trit format, version 1" - section 1 "Why bit planes", 2.3 "Ternary
  *        payload", 2.4 "Dense payload", 3 "A complete file", 4 "Validation".
  *
@@ -25,6 +26,9 @@
  *     at its lowest offending bit; within one beat P1 is checked before P2.
  *   - The dense head is y = W x over bfloat16 inputs; the oracle accumulates in float64
  *     and also returns sum |w * x| for the tolerance.
+ *   - BITCOS row form: the page fixes the two arrays (presence, compacted signs) but not how a
+ *     kernel blocks them; here each row's signs start on a 32-bit word, found through a per-row
+ *     word index (oracle_bitcos_pack_rows).
  *   - IntMlp: gate and up share the activation (and so its scale); K = S_g^2 S_u is one
  *     float64 number, (S_g * S_g) * S_u with S = (double)x_scale * (double)w_scale.
  *
@@ -430,4 +434,117 @@ int oracle_intmlp(const uint8_t *gate, const uint8_t *up, int64_t len, int64_t r
     free(ag);
     free(au);
     return rc;
+}
+
+/*
+ * BITCOS ("BITCOS: Intel's Ternary LLM Weight Format Goes Below 1.58 Bits", "A bitmap and a sign"):
+ * every weight gets a presence bit (set when it is nonzero); every nonzero weight, in the same
+ * order, gets a sign bit (set when it is -1). Zeros cost their presence bit only, so n weights with
+ * nnz nonzeros take n + nnz bits, 2 - z bits per weight at zero density z.
+ *
+ * Flat form (the page's packer works on a flat list): bit i of the bitmap is bit (i & 7) of byte
+ * i >> 3; the k-th nonzero's sign is bit (k & 7) of byte k >> 3 of the sign vector. Sizes:
+ * ceil(n / 8) + ceil(nnz / 8) bytes.
+ *
+ * Row form (the layout the GPU reads; the page leaves the blocking to the kernel): per row,
+ * bpr = ceil(cols / 64) presence words (u64, column c at bit c & 63 of word c >> 6, padding clear),
+ * then the row's signs in u32 words, the row's k-th nonzero at bit k & 31 of word
+ * row_start[r] + (k >> 5), unused bits clear; row_start[rows] is the total word count.
+ */
+int oracle_bitcos_pack_flat(const int8_t *w, int64_t n, uint8_t *bitmap, uint8_t *signs, int64_t *nnz) {
+    if (n < 0 || (n && (!w || !bitmap || !signs)) || !nnz) return OR_E_INVAL;
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i)
+        if (w[i] < -1 || w[i] > 1) return OR_E_INVAL;
+    memset(bitmap, 0, (size_t)((n + 7) / 8));
+    for (int64_t i = 0; i < n; ++i) {
+        if (w[i] == 0) continue;
+        bitmap[i >> 3] |= (uint8_t)(1u << (i & 7));
+        if ((k & 7) == 0) signs[k >> 3] = 0;
+        if (w[i] < 0) signs[k >> 3] |= (uint8_t)(1u << (k & 7));
+        ++k;
+    }
+    *nnz = k;
+    return OR_OK;
+}
+
+int oracle_bitcos_unpack_flat(const uint8_t *bitmap, const uint8_t *signs, int64_t n, int8_t *w) {
+    if (n < 0 || (n && (!bitmap || !w))) return OR_E_INVAL;
+    int64_t k = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        if ((bitmap[i >> 3] >> (i & 7)) & 1) {
+            w[i] = ((signs[k >> 3] >> (k & 7)) & 1) ? -1 : 1;
+            ++k;
+        } else {
+            w[i] = 0;
+        }
+    }
+    return OR_OK;
+}
+
+/* Row form. sign_words receives row_start[rows] words; pass sign_words = NULL to get the count
+ * into row_start only. */
+int oracle_bitcos_pack_rows(const int8_t *w, int64_t rows, int64_t cols, uint64_t *presence, uint32_t *sign_words,
+                            uint32_t *row_start) {
+    if (rows < 0 || cols < 0 || !row_start || (rows * cols && !w)) return OR_E_INVAL;
+    const int64_t bpr = oracle_beats_per_row(cols);
+    uint64_t total = 0;
+    for (int64_t r = 0; r < rows; ++r) {
+        row_start[r] = (uint32_t)total;
+        int64_t k = 0;
+        for (int64_t c = 0; c < cols; ++c) {
+            const int8_t v = w[r * cols + c];
+            if (v < -1 || v > 1) return OR_E_INVAL;
+            if (v != 0) ++k;
+        }
+        total += (uint64_t)((k + 31) / 32);
+        if (total > 0xFFFFFFFFull) return OR_E_RANGE;
+    }
+    row_start[rows] = (uint32_t)total;
+    if (!sign_words) return OR_OK;
+    if (rows * bpr && !presence) return OR_E_INVAL;
+    memset(sign_words, 0, (size_t)total * 4);
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < bpr; ++b) presence[r * bpr + b] = 0;
+        int64_t k = 0;
+        for (int64_t c = 0; c < cols; ++c) {
+            const int8_t v = w[r * cols + c];
+            if (v == 0) continue;
+            presence[r * bpr + (c >> 6)] |= UINT64_C(1) << (c & 63);
+            if (v < 0) sign_words[row_start[r] + (k >> 5)] |= UINT32_C(1) << (k & 31);
+            ++k;
+        }
+    }
+    return OR_OK;
+}
+
+/* y = W x from the row form, one weight at a time: weight (r, c) is 0 without its presence bit, else
+ * -1 or +1 by the sign bit of the row's nonzero it is. Dequantisation as oracle_gemv. */
+int oracle_bitcos_gemv(const uint64_t *presence, const uint32_t *sign_words, const uint32_t *row_start, int64_t rows,
+                       int64_t cols, const int8_t *x, float x_scale, float w_scale, int32_t *out_i32, float *out_f32,
+                       double *out_f64, int nthreads) {
+    if (rows < 0 || cols < 0 || !row_start || !out_i32) return OR_E_INVAL;
+    const int64_t bpr = oracle_beats_per_row(cols);
+    int bad = 0;
+#pragma omp parallel for schedule(static) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : bad)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t acc = 0, k = 0;
+        for (int64_t c = 0; c < cols; ++c) {
+            if (!((presence[r * bpr + (c >> 6)] >> (c & 63)) & 1)) continue;
+            const int neg = (int)((sign_words[row_start[r] + (k >> 5)] >> (k & 31)) & 1);
+            acc += neg ? -(int64_t)x[c] : (int64_t)x[c];
+            ++k;
+        }
+        if (acc > INT32_MAX || acc < INT32_MIN) {
+            bad |= 1;
+            continue;
+        }
+        out_i32[r] = (int32_t)acc;
+        float y32;
+        double y64;
+        oracle_dequant((int32_t)acc, x_scale, w_scale, &y32, &y64);
+        if (out_f32) out_f32[r] = y32;
+        if (out_f64) out_f64[r] = y64;
+    }
+    return bad ? OR_E_RANGE : OR_OK;
 }
