@@ -92,9 +92,13 @@ class DecodeSet:
             ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
             self.copies.append((bpw.GemvPlan(jobs, ws), mats, ws))
         self.shapes = shapes
-        for hm in host_mats:
-            hm.free()
+        self.host_mats = host_mats  # freed by free_host()
         self.xs, self.outs = xs, outs
+
+    def free_host(self):
+        for hm in self.host_mats:
+            hm.free()
+        self.host_mats = []
 
     def plan(self, i):
         return self.copies[i % len(self.copies)][0]
@@ -210,6 +214,47 @@ def intmlp_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
         p.free()
     return {"decode_step_intmlp_us": round(us, 2), "weight_gbs": round(ds.plane_bytes / (us * 1e-6) / 1e9, 1),
             "pairs": len(ts), "plain_jobs": len(ds.shapes) - 2 * len(ts)}
+
+
+def bitcos_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
+    """The same 210 matrices re-encoded as BITCOS (presence bitmap + compacted signs, from the .trit
+    host copies), in as many HBM copies as the .trit set, one grouped launch per step, timed between
+    HIP events. Bytes: presence words, sign words and row_start words the launch reads."""
+    plans, nbytes, sign_bytes, nnz = [], 0, 0, 0
+    hosts = [bpw.bpw_bitcos_from_planes(hm) for hm in ds.host_mats]
+    for h in hosts:
+        p, s, r, k = h.arrays()
+        nbytes += p.nbytes + s.nbytes + r.nbytes
+        sign_bytes += s.nbytes
+        nnz += k
+    for _ in ds.copies:
+        mats, bufs = [], []
+        for h in hosts:
+            buf = torch.empty(h.device_bytes, dtype=torch.uint8, device=dev)
+            mats.append(bpw.bpw_bitcos_upload(h, buf))
+            bufs.append(buf)
+        jobs = [bpw.bitcos_job(m, x, s, oi, of) for m, (x, s), (oi, of) in zip(mats, ds.xs, ds.outs)]
+        ws = torch.empty(bpw.bpw_bitcos_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+        plans.append((bpw.BitcosPlan(jobs, ws), bufs, ws))
+    for h in hosts:
+        h.free()
+
+    def some():
+        for i in range(10):
+            plans[i % len(plans)][0].run()
+    settle(torch, some)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        plans[i % len(plans)][0].run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    for p, _, _ in plans:
+        p.free()
+    return {"decode_step_bitcos_us": round(us, 2), "bytes": nbytes, "sign_bytes": sign_bytes, "nnz": nnz,
+            "bits_per_weight": round(8.0 * nbytes / ds.weights, 4), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "trit_plane_bytes": ds.plane_bytes}
 
 
 def probe_gbs(bpw, torch, dev) -> float:
@@ -508,7 +553,11 @@ def main() -> int:
         result["intmlp"] = intmlp_measure(bpw, torch, dev, ds)
         log("grouped small batch over the decode-step set")
         result["small_batch_decode_step"] = grouped_small_batch_measure(bpw, torch, synth, dev, ds)
-        del ds
+        log("BITCOS decode step")
+        result["bitcos"] = bitcos_measure(bpw, torch, dev, ds)
+        result["bitcos"]["vs_trit_step"] = round(result["bitcos"]["decode_step_bitcos_us"] / (kern_avg_ms * 1e3), 3)
+        ds.free_host()
+        ds = None
         torch.cuda.empty_cache()
         log("probe")
         pg = probe_gbs(bpw, torch, dev)
@@ -525,6 +574,8 @@ def main() -> int:
         result["small_batch"] = small_batch_measure(bpw, torch, synth, dev)  # auto: the matrix-core kernel
         result["small_batch_bitserial"] = small_batch_measure(bpw, torch, synth, dev, kernel=bpw.KERNEL_BITSERIAL)
 
+    if ds is not None:
+        ds.free_host()
     print(json.dumps(result), flush=True)
     return 0
 

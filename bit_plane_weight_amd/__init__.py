@@ -24,6 +24,8 @@ __all__ = [
     "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
     "TritFile", "TritFormatError", "TritTensor", "bpw_fnv1a64", "TRIT_F32", "TRIT_TERNARY", "TRIT_BF16",
+    "BitcosHost", "bpw_bitcos_pack_i8", "bpw_bitcos_from_planes", "DevBitcos", "bpw_bitcos_upload", "bitcos_job",
+    "bpw_bitcos_workspace_bytes", "BitcosPlan",
 ]
 
 
@@ -494,3 +496,140 @@ def bpw_stream_read_probe(d_buf, d_sink, stream=None) -> None:
 
 def bpw_cache_flush(d_buf, stream=None) -> None:
     _lib.check(_lib.lib().bpw_cache_flush(_dptr(d_buf), d_buf.numel() * d_buf.element_size(), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------ BITCOS
+
+
+class BitcosHost:
+    """A library-owned BITCOS matrix on the host (bpw_bitcos_host)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+
+    def arrays(self):
+        """(presence uint64 [rows * bpr], signs uint32 [sign_words], row_start uint32 [rows + 1], nnz),
+        copied out of the library's arrays."""
+        p, s, r = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_void_p()
+        nw, nnz = ctypes.c_int64(), ctypes.c_int64()
+        _lib.check(_lib.lib().bpw_bitcos_arrays(self._h, ctypes.byref(p), ctypes.byref(s), ctypes.byref(r),
+                                                ctypes.byref(nw), ctypes.byref(nnz)))
+        rows = self.rows
+
+        def view(ptr, n, ct, dt):
+            if n == 0:
+                return np.zeros(0, dt)
+            return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ct)), shape=(n,)).copy()
+
+        return (view(p, rows * self.bpr, ctypes.c_uint64, np.uint64), view(s, nw.value, ctypes.c_uint32, np.uint32),
+                view(r, rows + 1, ctypes.c_uint32, np.uint32), nnz.value)
+
+    @property
+    def device_bytes(self) -> int:
+        return _lib.lib().bpw_bitcos_device_bytes(self._h)
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_bitcos_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+def bpw_bitcos_pack_i8(w: np.ndarray, w_scale: float) -> BitcosHost:
+    """int8 [rows, cols] in {-1, 0, +1} -> a BITCOS matrix."""
+    w = _np(w, np.int8)
+    rows, cols = w.shape
+    h = ctypes.c_void_p()
+    err = _lib.BpwErr()
+    _lib.check(_lib.lib().bpw_bitcos_pack_i8(w.ctypes.data, rows, cols, float(w_scale), ctypes.byref(h),
+                                             ctypes.byref(err)), err)
+    out = BitcosHost(h.value)
+    out.rows, out.cols, out.bpr, out.w_scale = rows, cols, (cols + 63) // 64, w_scale
+    return out
+
+
+def bpw_bitcos_from_planes(m: HostMat) -> BitcosHost:
+    """The same matrix as a validated .trit host matrix, re-encoded."""
+    h = ctypes.c_void_p()
+    _lib.check(_lib.lib().bpw_bitcos_from_planes(m._h, ctypes.byref(h)))
+    out = BitcosHost(h.value)
+    out.rows, out.cols, out.bpr, out.w_scale = m.rows, m.cols, (m.cols + 63) // 64, m.w_scale
+    return out
+
+
+class DevBitcos:
+    """A BITCOS matrix resident on the GPU (bpw_dev_bitcos) plus the tensor that holds it."""
+
+    def __init__(self, desc: _lib.BpwDevBitcos, buf):
+        self.desc, self.buf = desc, buf
+
+    @property
+    def rows(self) -> int:
+        return self.desc.rows
+
+    @property
+    def cols(self) -> int:
+        return self.desc.cols
+
+    @property
+    def bpr(self) -> int:
+        return self.desc.bpr
+
+
+def bpw_bitcos_upload(h: BitcosHost, d_buf, stream=None) -> DevBitcos:
+    """Copy h into the uint8 GPU tensor d_buf (>= h.device_bytes, 256-byte aligned)."""
+    desc = _lib.BpwDevBitcos()
+    nbytes = d_buf.numel() * d_buf.element_size()
+    _lib.check(_lib.lib().bpw_bitcos_upload(h._h, _dptr(d_buf), nbytes, _stream(stream), ctypes.byref(desc)))
+    return DevBitcos(desc, d_buf)
+
+
+def bitcos_job(m: DevBitcos, x, x_scale: float, out_i32, out_f32=None) -> _lib.BpwBitcosJob:
+    j = _lib.BpwBitcosJob()
+    j.m = m.desc
+    j.d_x = _dptr(x)
+    j.x_len = x.numel() * x.element_size()
+    j.x_scale = float(x_scale)
+    j.d_out_i32 = _dptr(out_i32)
+    j.d_out_f32 = _dptr(out_f32)
+    return j
+
+
+def _bitcos_array(jobs):
+    jobs = list(jobs)
+    return (_lib.BpwBitcosJob * max(1, len(jobs)))(*jobs), len(jobs)
+
+
+def bpw_bitcos_workspace_bytes(jobs) -> int:
+    arr, n = _bitcos_array(jobs)
+    return _lib.lib().bpw_bitcos_workspace_bytes(arr, n)
+
+
+class BitcosPlan:
+    """bpw_bitcos_plan: job and tile tables written once into d_ws; run() queues the one launch."""
+
+    def __init__(self, jobs, d_ws, stream=None):
+        arr, n = _bitcos_array(jobs)
+        ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
+        h = ctypes.c_void_p()
+        _lib.check(_lib.lib().bpw_bitcos_plan_create(arr, n, _dptr(d_ws), ws_len, _stream(stream), ctypes.byref(h)))
+        self._h, self._keep = h, (jobs, d_ws)
+
+    def run(self, stream=None) -> None:
+        _lib.check(_lib.lib().bpw_bitcos_plan_run(self._h, _stream(stream)))
+
+    def free(self) -> None:
+        if self._h:
+            _lib.lib().bpw_bitcos_plan_free(self._h)
+            self._h = ctypes.c_void_p(None)
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

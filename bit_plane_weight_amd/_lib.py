@@ -56,6 +56,19 @@ class BpwSbJob(ctypes.Structure):
                 ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p)]
 
 
+class BpwDevBitcos(ctypes.Structure):
+    _fields_ = [("d_base", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("bpr", ctypes.c_int64), ("sign_words", ctypes.c_int64), ("row_start_off", ctypes.c_uint64),
+                ("signs_off", ctypes.c_uint64), ("w_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
+                ("seal", ctypes.c_uint64)]
+
+
+class BpwBitcosJob(ctypes.Structure):
+    _fields_ = [("m", BpwDevBitcos), ("d_x", ctypes.c_void_p), ("x_len", ctypes.c_int64),
+                ("x_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
+                ("d_out_i32", ctypes.c_void_p), ("d_out_f32", ctypes.c_void_p)]
+
+
 class BpwQuantJob(ctypes.Structure):
     _fields_ = [("d_h", ctypes.c_void_p), ("d_g", ctypes.c_void_p), ("n", ctypes.c_int64),
                 ("d_q", ctypes.c_void_p), ("q_len", ctypes.c_int64), ("d_scale", ctypes.c_void_p),
@@ -135,6 +148,17 @@ def lib():
         "bpw_fnv1a64": (ctypes.c_uint64, [vp, sz]),
         "bpw_trit_load": (i32, [vp, i64, ctypes.POINTER(vp), ctypes.POINTER(BpwErr)]),
         "bpw_cache_flush": (i32, [vp, sz, vp]),
+        "bpw_bitcos_pack_i8": (i32, [vp, i64, i64, f32, ctypes.POINTER(vp), E]),
+        "bpw_bitcos_from_planes": (i32, [vp, ctypes.POINTER(vp)]),
+        "bpw_bitcos_free": (None, [vp]),
+        "bpw_bitcos_arrays": (i32, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                    ctypes.POINTER(i64), ctypes.POINTER(i64)]),
+        "bpw_bitcos_device_bytes": (sz, [vp]),
+        "bpw_bitcos_upload": (i32, [vp, vp, sz, vp, ctypes.POINTER(BpwDevBitcos)]),
+        "bpw_bitcos_workspace_bytes": (sz, [ctypes.POINTER(BpwBitcosJob), i32]),
+        "bpw_bitcos_plan_create": (i32, [ctypes.POINTER(BpwBitcosJob), i32, vp, sz, vp, ctypes.POINTER(vp)]),
+        "bpw_bitcos_plan_run": (i32, [vp, vp]),
+        "bpw_bitcos_plan_free": (None, [vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(L, name)

@@ -22,30 +22,6 @@
 
 namespace bpw {
 
-// Planes of blocks [b0, b0 + nb) of x (nb <= kXPassBlocks), built in LDS by the workgroup's waves
-// in turn, 16 blocks per wave-round: a lane loads one 16-byte piece (piece p = block p / 4, quarter
-// p % 4) and stores its 16 bits of every plane as one 16-bit LDS write. Pieces of the last round
-// past nb * 4 read zeros through the buffer range check and write zero planes into blocks no beat
-// of this pass selects from. Each trip consumes its own load, so no load is left outstanding behind
-// the (wave-uniform) loop.
-__device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
-    const int need = (nb * 4 + 63) / 64;  // waves' worth of pieces
-    uint16_t *xh = reinterpret_cast<uint16_t *>(xl);
-    for (int wv = wave; wv < need; wv += kWaves) {
-        const int p = wv * 64 + lane;
-        const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
-        const int b = p >> 2, qq = p & 3;
-        uint32_t pl[8];
-        piece_planes(v.x, v.y, v.z, v.w, pl);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int w = 2 * j + (qq >> 1);
-            xh[(xq_slot(b, w >> 2) * 4 + (w & 3)) * 2 + (qq & 1)] = (uint16_t)pl[j];
-        }
-    }
-}
-
 // ------------------------------------------------------------------------------------------
 // Batch-1 grouped GEMV, bit-serial select. The host cuts every job's row-groups into tiles of about
 // 80 KB of planes (one job each) and the grid has one workgroup of kWaves waves per tile; the

@@ -1104,3 +1104,21 @@ bpw_status bpw_cache_flush(void *d_buf, size_t len, void *stream) {
 }
 
 }  // extern "C"
+
+namespace bpw {
+uint64_t seal_words(const uint64_t *w, int n) {
+    uint64_t h = seal_key();
+    for (int i = 0; i < n; ++i) h = mix64(h ^ w[i]);
+    return h;
+}
+int host_check_device() { return check_device(); }
+int host_xcds() { return device_xcds(); }
+void host_xcd_layout(Tile *tiles, int64_t n) { xcd_contiguous(tiles, n, device_xcds()); }
+const uint8_t *host_mat_view(const ::bpw_host_mat *m, int64_t *rows, int64_t *cols, float *w_scale) {
+    *rows = m->rows;
+    *cols = m->cols;
+    *w_scale = m->w_scale;
+    return m->planes;
+}
+}  // namespace bpw
+

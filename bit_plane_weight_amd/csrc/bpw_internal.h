@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+struct bpw_host_mat;  // include/bpw.h
+
 namespace bpw {
 
 // Launch geometry of the ternary GEMV kernels.
@@ -88,6 +90,20 @@ struct SBTile {
     int32_t pad;
 };
 
+// One BITCOS GEMV of a grouped launch (lives in the caller's workspace).
+struct BitcosJob {
+    const uint64_t *presence;   // rows * bpr words
+    const uint32_t *row_start;  // rows + 1 words
+    const uint32_t *signs;
+    const int8_t *x;
+    int32_t *out_i32;
+    float *out_f32;             // may be null
+    int32_t rows, bpr;
+    float x_scale, w_scale;
+    uint32_t presence_bytes, row_start_bytes, sign_bytes;  // the buffer ranges
+    int32_t pad;
+};
+
 // One activation of the Folded quantiser (lives in the caller's workspace).
 struct QuantJob {
     const float *h;
@@ -100,8 +116,16 @@ struct QuantJob {
     int32_t pad;
 };
 
-// Host side: record the reason of a failing call for bpw_last_error() (bpw_host.cpp).
+// Host side (bpw_host.cpp): record the reason of a failing call for bpw_last_error(); a keyed hash
+// of a device descriptor's fields (its seal); the gfx950 check; the XCD count of the current device;
+// a tile table permuted so that each XCD runs one contiguous run of it; a validated host matrix's
+// planes and shape.
 void record_error(const char *msg);
+uint64_t seal_words(const uint64_t *w, int n);
+int host_check_device();  // a bpw_status
+int host_xcds();
+void host_xcd_layout(Tile *tiles, int64_t n);
+const uint8_t *host_mat_view(const ::bpw_host_mat *m, int64_t *rows, int64_t *cols, float *w_scale);
 
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
@@ -110,6 +134,7 @@ int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
 int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream);
+int launch_gemv_bitcos(const BitcosJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_quantize(const QuantJob *jobs, int32_t n_jobs, void *stream);
 int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);

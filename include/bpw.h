@@ -361,6 +361,63 @@ uint64_t bpw_fnv1a64(const uint8_t *data, size_t len);
  * copied and validated exactly as bpw_load does (P1, P2), with the record's scale as w_scale. */
 bpw_status bpw_trit_load(const bpw_trit_file *f, int64_t index, bpw_host_mat **out, bpw_err *err);
 
+/* ------------------------------------------------------------------------ BITCOS */
+
+/* BITCOS ("BITCOS: Intel's Ternary LLM Weight Format Goes Below 1.58 Bits", "A bitmap and a sign"): a
+ * second, lossless layout of the same ternary matrix. Every weight has a presence bit (nonzero);
+ * every nonzero, in column order, a sign bit (set for -1): n + nnz bits, 2 - z bits per weight at
+ * zero density z. The layout the kernel reads (the page leaves the blocking open): per row,
+ * bpr = ceil(cols / 64) presence words (u64, column c at bit c & 63 of word c >> 6, padding clear),
+ * and the row's signs in u32 words from word row_start[r] (the row's k-th nonzero at bit k & 31 of
+ * word row_start[r] + (k >> 5)); row_start[rows] is the word count. cols <= 8192. */
+typedef struct bpw_bitcos_host bpw_bitcos_host;
+
+/* Pack row-major int8 trits (values outside {-1, 0, +1}: BPW_E_INVAL with the position in *err). */
+bpw_status bpw_bitcos_pack_i8(const int8_t *w, int64_t rows, int64_t cols, float w_scale, bpw_bitcos_host **out,
+                              bpw_err *err);
+/* Re-encode a validated .trit matrix (same trits, same scale). */
+bpw_status bpw_bitcos_from_planes(const bpw_host_mat *m, bpw_bitcos_host **out);
+void bpw_bitcos_free(bpw_bitcos_host *h);
+/* Read-only views of the host arrays: presence [rows * bpr], signs [sign_words], row_start [rows + 1]. */
+bpw_status bpw_bitcos_arrays(const bpw_bitcos_host *h, const uint64_t **presence, const uint32_t **signs,
+                             const uint32_t **row_start, int64_t *sign_words, int64_t *nnz);
+/* Device bytes bpw_bitcos_upload needs (the three arrays, each at a 256-byte boundary). */
+size_t bpw_bitcos_device_bytes(const bpw_bitcos_host *h);
+
+/* A BITCOS matrix resident on the GPU, filled in by bpw_bitcos_upload only (sealed like bpw_dev_mat). */
+typedef struct bpw_dev_bitcos {
+    const void *d_base;      /* presence words, then row_start, then signs */
+    int64_t rows, cols, bpr;
+    int64_t sign_words;
+    uint64_t row_start_off;  /* byte offsets from d_base */
+    uint64_t signs_off;
+    float w_scale;
+    uint32_t reserved;
+    uint64_t seal;
+} bpw_dev_bitcos;
+
+bpw_status bpw_bitcos_upload(const bpw_bitcos_host *h, void *d_dst, size_t d_len, void *stream, bpw_dev_bitcos *out);
+
+/* One batch-1 GEMV on a BITCOS matrix: the same sums and dequantisation as bpw_gemv_job. */
+typedef struct bpw_bitcos_job {
+    bpw_dev_bitcos m;
+    const int8_t *d_x;   /* device int8 codes, 16-byte aligned, x_len >= bpr * 64 */
+    int64_t x_len;
+    float x_scale;
+    uint32_t reserved;
+    int32_t *d_out_i32;  /* device int32 [rows] */
+    float *d_out_f32;    /* device float [rows] or NULL */
+} bpw_bitcos_job;
+
+typedef struct bpw_bitcos_plan bpw_bitcos_plan;
+size_t bpw_bitcos_workspace_bytes(const bpw_bitcos_job *jobs, int32_t n_jobs);
+/* Job and tile tables written once into d_ws (256-byte aligned; waits for the copy); each run is one
+ * launch over all jobs. */
+bpw_status bpw_bitcos_plan_create(const bpw_bitcos_job *jobs, int32_t n_jobs, void *d_ws, size_t ws_len, void *stream,
+                                  bpw_bitcos_plan **out);
+bpw_status bpw_bitcos_plan_run(const bpw_bitcos_plan *plan, void *stream);
+void bpw_bitcos_plan_free(bpw_bitcos_plan *plan);
+
 /* ------------------------------------------------------------------------ dense head */
 
 /* The dense tied LM head at batch 1 (Tritium paper, "Where the bytes are"; format page 2.4):
