@@ -55,7 +55,6 @@ constexpr size_t kAlign = 256;
 constexpr int64_t kMaxCols = 64 * bpw::kXPassBlocks;  // one LDS pass of activation planes
 constexpr int64_t kSignPadWords = 4;                 // a 16-byte sign window read at the last word stays in range
 constexpr uint64_t kMaxRange = 0xFFFFFFF0ull;        // the kernel's buffer offsets are 32-bit
-constexpr int64_t kTileUnits = 16;                   // row-groups of 8 rows per workgroup tile
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
@@ -255,9 +254,14 @@ bpw_status check_job(const bpw_bitcos_job &j, int32_t i) {
     return BPW_OK;
 }
 
+// Row-groups of one job: 64 / 2^glog rows each (the rows one wave covers at a time).
+inline int64_t job_units(const bpw_dev_bitcos &m) {
+    const int64_t unit_rows = 64 >> bpw::bitcos_geometry(m.bpr).glog;
+    return (m.rows + unit_rows - 1) / unit_rows;
+}
+
 inline int64_t job_tiles(const bpw_bitcos_job &j) {
-    const int64_t units = (j.m.rows + 7) / 8;
-    return (units + kTileUnits - 1) / kTileUnits;
+    return (job_units(j.m) + bpw::kBcTileUnits - 1) / bpw::kBcTileUnits;
 }
 
 struct PlanLayout {
@@ -370,9 +374,9 @@ bpw_status bpw_bitcos_plan_create(const bpw_bitcos_job *jobs, int32_t n_jobs, vo
         d.row_start_bytes = (uint32_t)D.row_start_bytes;
         d.sign_bytes = (uint32_t)D.sign_bytes;
         hj[i] = d;
-        const int64_t U = (j.m.rows + 7) / 8;
-        for (int64_t u = 0; u < U; u += kTileUnits)
-            ht[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + kTileUnits), 0};
+        const int64_t U = job_units(j.m);
+        for (int64_t u = 0; u < U; u += bpw::kBcTileUnits)
+            ht[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + bpw::kBcTileUnits), 0};
     }
     bpw::host_xcd_layout(ht, t);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

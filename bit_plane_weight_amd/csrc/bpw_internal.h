@@ -90,6 +90,20 @@ struct SBTile {
     int32_t pad;
 };
 
+// BITCOS GEMV launch geometry: 8 waves per workgroup (two workgroups per CU share the LDS, each
+// holding the 64 KiB deposit table), tiles of kBcTileUnits row-groups. A row of bpr blocks is held by
+// 2^glog lanes with k contiguous blocks each (k * 2^glog >= bpr); a row-group is the 64 >> glog rows
+// one wave covers at a time.
+constexpr int kBcWaves = 8;
+constexpr int kBcThreads = 64 * kBcWaves;
+constexpr int kBcTileUnits = 32;
+struct BcGeometry {
+    int k, glog;
+};
+constexpr BcGeometry bitcos_geometry(int64_t bpr) {
+    return bpr <= 16 ? BcGeometry{2, 3} : bpr <= 40 ? BcGeometry{5, 3} : bpr <= 64 ? BcGeometry{4, 4} : BcGeometry{4, 5};
+}
+
 // One BITCOS GEMV of a grouped launch (lives in the caller's workspace).
 struct BitcosJob {
     const uint64_t *presence;   // rows * bpr words

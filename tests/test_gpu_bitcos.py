@@ -113,6 +113,7 @@ def test_zero_density_sweep_layer(dev, z):
 
 
 RAGGED = ((1, 1), (3, 63), (5, 64), (7, 65), (17, 200), (9, 2560), (33, 6912), (129, 8192), (1, 4096), (8, 640),
+          (65, 3000), (31, 4000), (70, 1025), (3, 7000),
           (130, 127), (1025, 2560), (0, 100), (5, 0))
 
 
