@@ -34,15 +34,24 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bitserial_decode_step_traffi
 # sources of the decode-step GEMV kernel; the committed counter summary holds their hash
 KERNEL_SRCS = [os.path.join(ROOT, "bit_plane_weight_amd", "csrc", f)
                for f in ("bpw_gemv.hip", "bpw_device.h", "bpw_internal.h")]
+# the BITCOS GEMV kernel: its VALU instruction count per decode-step launch, from a committed counter
+# run on the same sources
+BITCOS_FILE = os.path.join(ROOT, "profiles", "gemv_bitcos_decode_step_counters.json")
+BITCOS_SRCS = [os.path.join(ROOT, "bit_plane_weight_amd", "csrc", f)
+               for f in ("bpw_bitcos.hip", "bpw_device.h", "bpw_internal.h")]
+# Integer VALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a wave64
+# VALU instruction occupies its SIMD for 4 clocks), in lane-operations per second.
+VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
+LEGS = ("prologue", "intmlp", "small_batch_decode_step", "bitcos", "probe", "head", "z_sweep", "small_batch")
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(paths=None) -> str:
     h = hashlib.sha256()
-    for path in KERNEL_SRCS:
+    for path in paths or KERNEL_SRCS:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -252,9 +261,34 @@ def bitcos_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
     us = a.elapsed_time(b) / steps * 1e3
     for p, _, _ in plans:
         p.free()
-    return {"decode_step_bitcos_us": round(us, 2), "bytes": nbytes, "sign_bytes": sign_bytes, "nnz": nnz,
-            "bits_per_weight": round(8.0 * nbytes / ds.weights, 4), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
-            "trit_plane_bytes": ds.plane_bytes}
+    gbs = nbytes / (us * 1e-6) / 1e9
+    out = {"decode_step_bitcos_us": round(us, 2), "bytes": nbytes, "sign_bytes": sign_bytes, "nnz": nnz,
+           "bits_per_weight": round(8.0 * nbytes / ds.weights, 4), "gbs": round(gbs, 1),
+           "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2), "trit_plane_bytes": ds.plane_bytes}
+    insts = bitcos_valu_from_profile()
+    out["roofline"] = {
+        "bound": "alu",
+        "achieved": None if insts is None else round(insts * 64 / (us * 1e-6) / 1e12, 2),
+        "peak": round(VALU_PEAK_LANE_OPS / 1e12, 2),
+        "unit": "T int32 VALU lane-ops/s",
+        "frac": None if insts is None else round(insts * 64 / (us * 1e-6) / VALU_PEAK_LANE_OPS, 4),
+        "valu_insts_per_launch": insts,
+        "kernel": "gemv_bitcos_kernel",
+    }
+    return out
+
+
+def bitcos_valu_from_profile() -> float | None:
+    """VALU wave-instructions per BITCOS decode-step launch from the committed counter run, if it was
+    taken on the current kernel source; otherwise None."""
+    try:
+        with open(BITCOS_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != kernel_source_hash(BITCOS_SRCS):
+        return None
+    return rec.get("sq_insts_valu_per_launch")
 
 
 def probe_gbs(bpw, torch, dev) -> float:
@@ -388,6 +422,7 @@ def z_sweep_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
         ms = statistics.median(time_steps(torch, ds, reps)[0] for _ in range(3))
         out.append({"p_zero": z, "gemv_us": round(ms * 1e3, 2),
                     "weight_gbs": round(ds.plane_bytes / (ms * 1e-3) / 1e9, 1)})
+        ds.free_host()
         del ds
         torch.cuda.empty_cache()
     return out
@@ -438,7 +473,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=3, help="HBM copies of the weight set used in rotation")
     ap.add_argument("--kernel", choices=("auto", "bitserial", "bytelane"), default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true", help="skip probe, head, sweep and small batch")
+    ap.add_argument("--no-extras", action="store_true", help="skip every companion measurement")
+    ap.add_argument("--legs", default="all",
+                    help="comma-separated companion measurements to run (default all): " + ",".join(LEGS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, read 1 GiB with the streaming probe and rewrite 1 GiB with the cache "
                          "flush (3 times each): kernels of known traffic for scaling hardware byte counters")
@@ -546,36 +583,46 @@ def main() -> int:
         del cal
 
     # ---------------------------------------------------------------- companion measurements
-    if not args.no_extras:
+    legs = set() if args.no_extras else (set(LEGS) if args.legs == "all" else set(args.legs.split(",")))
+    unknown = legs - set(LEGS)
+    if unknown:
+        print(f"unknown --legs {sorted(unknown)}; choose from {','.join(LEGS)}", file=sys.stderr)
+        return 2
+    if "prologue" in legs:
         log("quantiser prologue")
         result["prologue"] = prologue_measure(bpw, torch, synth, dev, ds)
+    if "intmlp" in legs:
         log("IntMlp pairs")
         result["intmlp"] = intmlp_measure(bpw, torch, dev, ds)
+    if "small_batch_decode_step" in legs:
         log("grouped small batch over the decode-step set")
         result["small_batch_decode_step"] = grouped_small_batch_measure(bpw, torch, synth, dev, ds)
+    if "bitcos" in legs:
         log("BITCOS decode step")
         result["bitcos"] = bitcos_measure(bpw, torch, dev, ds)
         result["bitcos"]["vs_trit_step"] = round(result["bitcos"]["decode_step_bitcos_us"] / (kern_avg_ms * 1e3), 3)
-        ds.free_host()
-        ds = None
-        torch.cuda.empty_cache()
+    ds.free_host()
+    ds = None
+    torch.cuda.empty_cache()
+    if "probe" in legs:
         log("probe")
         pg = probe_gbs(bpw, torch, dev)
         result["probe_gbs"] = round(pg, 1)
         result["pct_probe"] = round(100.0 * achieved / pg, 2)
+    if "head" in legs:
         log("dense head")
         head = head_measure(bpw, torch, synth, dev)
         result["head"] = {k: (round(v, 2) if isinstance(v, float) else v) for k, v in head.items()}
         result["per_token_us"] = round(kern_avg_ms * 1e3 + head["us"], 2)
         result["per_token_bytes"] = result["config"]["plane_bytes"] + head["bytes"]
+    if "z_sweep" in legs:
         log("zero-density sweep")
         result["z_sweep"] = z_sweep_measure(bpw, torch, synth, dev)
+    if "small_batch" in legs:
         log("small batch")
         result["small_batch"] = small_batch_measure(bpw, torch, synth, dev)  # auto: the matrix-core kernel
         result["small_batch_bitserial"] = small_batch_measure(bpw, torch, synth, dev, kernel=bpw.KERNEL_BITSERIAL)
 
-    if ds is not None:
-        ds.free_host()
     print(json.dumps(result), flush=True)
     return 0
 
