@@ -42,7 +42,7 @@ BITCOS_SRCS = [os.path.join(ROOT, "bit_plane_weight_amd", "csrc", f)
 # Integer VALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes per clock x 2.4 GHz (a wave64
 # VALU instruction occupies its SIMD for 4 clocks), in lane-operations per second.
 VALU_PEAK_LANE_OPS = 256 * 4 * 16 * 2.4e9
-LEGS = ("prologue", "intmlp", "small_batch_decode_step", "bitcos", "probe", "head", "z_sweep", "small_batch")
+LEGS = ("configs", "prologue", "intmlp", "small_batch_decode_step", "bitcos", "probe", "head", "z_sweep", "small_batch")
 
 
 def log(msg: str) -> None:
@@ -289,6 +289,77 @@ def bitcos_valu_from_profile() -> float | None:
     if rec.get("kernel_source_sha256") != kernel_source_hash(BITCOS_SRCS):
         return None
     return rec.get("sq_insts_valu_per_launch")
+
+
+def configs_measure(bpw, torch, dev, ds, reps: int = 30) -> dict:
+    """The smaller configurations of the same workload, timed the pages' way: HIP events around each
+    launch, median and min over `reps`; hot = launches back to back (the weights stay in L2 and the
+    last-level cache), cold = a 1 GiB read-modify-write flush before each timed launch (the flush is
+    outside the timed span).
+      k_proj: one 640 x 2560 matrix, 409,600 plane bytes (launch-latency dominated);
+      layer: one layer's seven projections as one grouped launch (17,367,040 B), and each alone;
+      decode step as 210 single-matrix launches in stream order, for context beside the grouped one."""
+    mats = ds.copies[0][1]
+
+    def plan(idx):
+        jobs = []
+        for i in idx:
+            x, s = ds.xs[i]
+            oi, of = ds.outs[i]
+            jobs.append(bpw.gemv_job(mats[i], x, s, oi, of))
+        ws = torch.empty(bpw.bpw_gemv_workspace_bytes(jobs), dtype=torch.uint8, device=dev)
+        return bpw.GemvPlan(jobs, ws), ws
+
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def timed(fn, cold):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        settle(torch, fn)
+        for a, b in ev:
+            if cold:
+                bpw.bpw_cache_flush(flush_buf)
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+        return statistics.median(t), t[0]
+
+    def entry(nbytes, fn):
+        out = {"bytes": nbytes}
+        for kind in ("hot", "cold"):
+            med, best = timed(fn, kind == "cold")
+            out[kind] = {"us": round(med, 2), "min_us": round(best, 2), "gbs": round(nbytes / (med * 1e-6) / 1e9, 1)}
+        return out
+
+    layer0 = [i for i, sh in enumerate(ds.shapes) if sh[0] == 0]
+    k_idx = [i for i in layer0 if ds.shapes[i][2] == "k_proj"]
+    res = {}
+    pk, _wk = plan(k_idx)
+    res["k_proj_640x2560"] = entry(mats[k_idx[0]].rows * mats[k_idx[0]].bpr * 16, pk.run)
+    pl, _wl = plan(layer0)
+    layer_bytes = sum(mats[i].rows * mats[i].bpr * 16 for i in layer0)
+    res["layer_grouped"] = entry(layer_bytes, pl.run)
+    res["layer_per_matrix_hot_us"] = {}
+    for i in layer0:
+        p1, _w1 = plan([i])
+        res["layer_per_matrix_hot_us"][ds.shapes[i][2]] = round(timed(p1.run, False)[0], 2)
+        p1.free()
+    singles = [plan([i]) for i in range(len(ds.shapes))]
+
+    def step_singles():
+        for p, _ in singles:
+            p.run()
+    med, best = timed(step_singles, False)
+    res["decode_step_210_single_launches"] = {"us": round(med, 2), "min_us": round(best, 2),
+                                              "gbs": round(ds.plane_bytes / (med * 1e-6) / 1e9, 1)}
+    for p, _ in singles:
+        p.free()
+    pk.free()
+    pl.free()
+    del flush_buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def probe_gbs(bpw, torch, dev) -> float:
@@ -588,6 +659,9 @@ def main() -> int:
     if unknown:
         print(f"unknown --legs {sorted(unknown)}; choose from {','.join(LEGS)}", file=sys.stderr)
         return 2
+    if "configs" in legs:
+        log("k_proj, one layer (hot and cold), 210 single launches")
+        result["configs"] = configs_measure(bpw, torch, dev, ds)
     if "prologue" in legs:
         log("quantiser prologue")
         result["prologue"] = prologue_measure(bpw, torch, synth, dev, ds)
