@@ -153,6 +153,22 @@ int device_xcds() {
     return n;
 }
 
+// Compute units of the current device (1 if the runtime cannot say), cached per device.
+std::atomic<int> g_cus[64];
+int device_cus() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return 1;
+    const int slot = dev >= 0 && dev < 64 ? dev : -1;
+    if (slot >= 0) {
+        const int v = g_cus[slot].load(std::memory_order_acquire);
+        if (v > 0) return v;
+    }
+    int n = 1;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+    if (slot >= 0) g_cus[slot].store(n, std::memory_order_release);
+    return n;
+}
+
 bpw_status hip_status(int e, const char *what) {
     if (e == hipSuccess) return BPW_OK;
     return fail(BPW_E_HIP, "%s: %s", what, hipGetErrorString((hipError_t)e));
@@ -316,10 +332,13 @@ inline int64_t units_of(int64_t rows, const Geometry &g) {
     return (rows + rpi - 1) / rpi;
 }
 
-// Row-groups in one bit-serial tile of a job: 16, or fewer where kTileRows caps the rows; a pair's
-// tile holds half as many of each matrix. (Measured on the decode step: 16 beat 12 and 24, and 24
-// for the 6912-column rows alone was 1 us slower.)
-constexpr int64_t kTileUnits = 16;
+// Row-groups in one bit-serial tile of a job: kTileUnits, or fewer where kTileRows caps the rows; a
+// pair's tile holds half as many of each matrix. The plan then cuts the last kTailShare of each XCD's
+// run of tiles into tiles of 1/kTailDiv the width (8 row-groups, two per wave), see xcd_runs.
+constexpr int64_t kTileUnits = 32;
+constexpr double kTailShare = 0.75;
+constexpr int64_t kTailDiv = 4;
+constexpr int64_t kMaxXcds = 64;  // bound on the XCD count used to size the workspace
 inline int64_t tile_units(const Geometry &g) {
     return std::min<int64_t>(kTileUnits, bpw::kTileRows / (64 >> g.glog));
 }
@@ -343,6 +362,8 @@ int64_t pair_tiles(const bpw_intmlp_job &j) {
     return (units_of(j.gate.rows, g) + tu - 1) / tu;
 }
 
+// n_work counts the tiles before the tail split; total bounds the table after it: the split and the
+// padding of the XCD runs (xcd_runs) give at most (n_work + kMaxXcds) * kTailDiv bit-serial tiles.
 Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial, const bpw_intmlp_job *mlp = nullptr,
                   int32_t n_mlp = 0) {
     Layout L{};
@@ -352,7 +373,8 @@ Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial, const bpw
     for (int32_t i = 0; i < n_mlp; ++i) L.n_work += pair_tiles(mlp[i]);
     L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)(n + n_mlp));
     const size_t tile_bytes = bitserial ? sizeof(bpw::Tile) : sizeof(bpw::DevTile);
-    L.total = align_up(L.work_off + tile_bytes * (size_t)L.n_work);
+    const int64_t tile_bound = bitserial && L.n_work > 0 ? (L.n_work + kMaxXcds) * kTailDiv : L.n_work;
+    L.total = align_up(L.work_off + tile_bytes * (size_t)tile_bound);
     return L;
 }
 
@@ -396,6 +418,43 @@ void xcd_contiguous(T *tiles, int64_t n, int X) {
     std::vector<int64_t> start(X + 1, 0);
     for (int x = 0; x < X; ++x) start[x + 1] = start[x] + (n - x + X - 1) / X;  // blocks b with b % X == x
     for (int64_t b = 0; b < n; ++b) tiles[b] = src[start[b % X] + b / X];
+}
+
+// The bit-serial table per XCD: XCD x runs one contiguous run of the job-ordered tiles (as
+// xcd_contiguous), and the last kTailShare of each run is cut into tiles of 1/kTailDiv the width, so
+// the large tiles go first and the run ends in small ones that finish close together. Runs are padded
+// to one length with empty tiles (u0 == u1, no rows; they only stage the job's activation) and
+// interleaved, workgroup b taking entry b / X of run b mod X. Returns the table length. Measured on
+// the decode step, same box: tiles of 16 row-groups in job-ordered XCD runs 81.4-81.7 us; all 8
+// 79.6; 16 with the last 62 % at 8 78.1-78.4; 32 with the last 75 % at 8 77.9; tails of 4, 6, 10 or
+// 12 row-groups 80-91 (an odd share per wave, or too little work per tile).
+int64_t xcd_runs(bpw::Tile *tiles, int64_t n, int X, double tail_share) {
+    X = std::max(1, X);
+    std::vector<bpw::Tile> src(tiles, tiles + n);
+    std::vector<std::vector<bpw::Tile>> runs((size_t)X);
+    size_t longest = 0;
+    int64_t s0 = 0;
+    for (int x = 0; x < X; ++x) {
+        const int64_t len = (n - x + X - 1) / X;
+        const int64_t fine_from = s0 + len - (int64_t)((double)len * tail_share + 0.5);
+        for (int64_t i = s0; i < s0 + len; ++i) {
+            const bpw::Tile b = src[(size_t)i];
+            if (i < fine_from) {
+                runs[(size_t)x].push_back(b);
+                continue;
+            }
+            const int64_t w = std::max<int64_t>(1, (b.u1 - b.u0 + kTailDiv - 1) / kTailDiv);
+            for (int64_t u = b.u0; u < b.u1; u += w)
+                runs[(size_t)x].push_back(bpw::Tile{b.job, (int32_t)u, (int32_t)std::min<int64_t>(b.u1, u + w), 0});
+        }
+        s0 += len;
+        longest = std::max(longest, runs[(size_t)x].size());
+    }
+    const bpw::Tile pad{n > 0 ? src[0].job : 0, 1, 1, 0};
+    int64_t t = 0;
+    for (size_t k = 0; k < longest; ++k)
+        for (int x = 0; x < X; ++x) tiles[t++] = k < runs[(size_t)x].size() ? runs[(size_t)x][k] : pad;
+    return t;
 }
 
 // Widest pair whose t = relu(a_g)^2 * a_u cannot overflow int64: |a| <= 128 * cols < 2^21.
@@ -711,10 +770,22 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         return fail(BPW_E_UNSUPPORTED, "internal: %lld tiles written, %lld expected", (long long)t, (long long)L.n_work);
     }
     const int xccs = device_xcds();
-    if (bitserial)
-        xcd_contiguous(hb, t, xccs);
-    else
+    if (bitserial) {
+        if (xccs > kMaxXcds) {
+            delete plan;
+            return fail(BPW_E_UNSUPPORTED, "device has %d XCDs; the tile table is sized for %lld", xccs,
+                        (long long)kMaxXcds);
+        }
+        // a plan too small to give every CU two wide tiles (one layer: 119) takes only narrow ones
+        const double share = t < 2 * (int64_t)device_cus() ? 1.0 : kTailShare;
+        plan->n_tiles = xcd_runs(hb, t, xccs, share);
+        if (plan->n_tiles > (int64_t)INT32_MAX) {
+            delete plan;
+            return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
+        }
+    } else {
         xcd_contiguous(ht, t, xccs);
+    }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
