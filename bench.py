@@ -452,11 +452,15 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0)
 
 def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50) -> list[dict]:
     """The decode-step set (210 matrices, 521 MB of planes) at batch B: every matrix times its own B
-    int8 activation vectors, all in one grouped launch on the int8 matrix cores, the HBM copies in
-    rotation. Shows where the weight stream stops being the limit as B grows."""
-    import numpy as np
+    int8 activation vectors, all in one grouped launch, the HBM copies in rotation. Under AUTO, B = 1
+    runs the batch-1 GEMV, B = 2 .. 4 the bit-serial token kernel (each beat streamed once, reduced
+    against every token on the VALU) and larger B the int8 matrix cores; B = 2 and 4 are also timed on
+    the matrix cores. Shows where the weight stream stops being the limit as B grows."""
     out = []
-    for batch in (1, 2, 4, 8, 16):
+    runs = [(1, bpw.KERNEL_AUTO), (2, bpw.KERNEL_AUTO), (2, bpw.KERNEL_MFMA), (3, bpw.KERNEL_AUTO),
+            (4, bpw.KERNEL_AUTO), (4, bpw.KERNEL_MFMA), (8, bpw.KERNEL_AUTO), (16, bpw.KERNEL_AUTO)]
+    names = {bpw.KERNEL_AUTO: "auto", bpw.KERNEL_MFMA: "mfma"}
+    for batch, kernel in runs:
         xs = []
         for i, (layer, proj, name, rows, cols) in enumerate(ds.shapes):
             X, sc = synth.small_batch_x(BASE_SEED + 1009 * i + batch, batch, cols)
@@ -466,7 +470,7 @@ def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50) -> 
         for _, mats, _ in ds.copies:
             jobs = [bpw.sb_job(m, X, sc, oi, of) for m, (X, sc, oi, of) in zip(mats, xs)]
             ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
-            plans.append((bpw.SmallBatchPlan(jobs, batch, ws), ws))
+            plans.append((bpw.SmallBatchPlan(jobs, batch, ws, kernel), ws))
         settle(torch, lambda: [plans[i % len(plans)][0].run() for i in range(6)])
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
@@ -475,7 +479,8 @@ def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50) -> 
         b.record()
         torch.cuda.synchronize()
         us = a.elapsed_time(b) / steps * 1e3
-        out.append({"batch": batch, "us": round(us, 2), "weight_gbs": round(ds.plane_bytes / (us * 1e-6) / 1e9, 1),
+        out.append({"batch": batch, "kernel": names[kernel], "us": round(us, 2),
+                    "weight_gbs": round(ds.plane_bytes / (us * 1e-6) / 1e9, 1),
                     "tops_equiv": round(2.0 * ds.weights * batch / (us * 1e-6) / 1e12, 2)})
         for p, _ in plans:
             p.free()

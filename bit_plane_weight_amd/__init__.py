@@ -319,7 +319,8 @@ def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, kernel: int =
 
 
 class _SbJob:
-    """One grouped small-batch job; keeps its host scales alive until the plan has copied them."""
+    """One grouped small-batch job; keeps its host scales alive until the plan has copied them, and
+    its device tensors as long as the job (the plan reads X and writes the outputs at every run)."""
 
     def __init__(self, m: DevMat, X, x_scales, out_i32, out_f32=None):
         batch, ldx = X.shape
@@ -335,6 +336,7 @@ class _SbJob:
         j.d_out_i32 = _dptr(out_i32)
         j.d_out_f32 = _dptr(out_f32)
         self.c = j
+        self._keep = (X, out_i32, out_f32)
 
 
 def sb_job(m: DevMat, X, x_scales, out_i32, out_f32=None) -> _SbJob:

@@ -1010,6 +1010,11 @@ struct bpw_sb_plan {
     const bpw::SBTile *tiles;
     int64_t n_tiles;
     bpw_gemv_plan *gemv;  // batch 1 under AUTO: the batch-1 grouped GEMV over the same jobs
+    // 2 to 4 tokens on the bit-serial kernel: its job and tile tables (n_tok_tiles > 0)
+    const bpw::TokJob *tok_jobs;
+    const bpw::Tile *tok_tiles;
+    int64_t n_tok_tiles;
+    int32_t nt;
 };
 
 namespace {
@@ -1025,6 +1030,45 @@ SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
     L.jobs_off = 0;
     L.tiles_off = align_up(sizeof(bpw::SmallBatchArgs) * (size_t)n);
     L.total = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)L.n_tiles);
+    return L;
+}
+}  // namespace
+
+// The bit-serial token kernel serves 2 to 4 tokens of matrices 2560 or 6912 columns wide (40 or 108
+// beats per row); its tables: one TokJob per job, tiles as the batch-1 plan cuts them (rows per tile
+// capped at kTokTileRows), the same bound for the XCD runs.
+namespace {
+constexpr int32_t kTokAutoMax = 3;  // AUTO: tokens per call the token kernel serves faster than the matrix cores
+bool tok_shape(const bpw_dev_mat &m) { return m.bpr == 40 || m.bpr == 108; }
+
+bool tok_ok(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
+    if (batch < 2 || batch > bpw::kTokMax) return false;
+    for (int32_t i = 0; i < n; ++i)
+        if (!tok_shape(jobs[i].m)) return false;
+    return true;
+}
+
+inline int64_t tok_tile_units(const Geometry &g) {
+    return std::min<int64_t>(kTileUnits, bpw::kTokTileRows / (64 >> g.glog));
+}
+
+int64_t tok_base_tiles(const bpw_sb_job *jobs, int32_t n) {
+    int64_t t = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        const Geometry g = geometry_for(jobs[i].m.bpr, true);
+        const int64_t tu = tok_tile_units(g);
+        t += (units_of(jobs[i].m.rows, g) + tu - 1) / tu;
+    }
+    return t;
+}
+
+SBLayout tok_layout(const bpw_sb_job *jobs, int32_t n) {
+    SBLayout L{};
+    L.n_tiles = tok_base_tiles(jobs, n);
+    L.jobs_off = 0;
+    L.tiles_off = align_up(sizeof(bpw::TokJob) * (size_t)n);
+    const int64_t bound = L.n_tiles > 0 ? (L.n_tiles + kMaxXcds) * kTailDiv : 0;
+    L.total = align_up(L.tiles_off + sizeof(bpw::Tile) * (size_t)bound);
     return L;
 }
 }  // namespace
@@ -1047,6 +1091,7 @@ static std::vector<bpw_gemv_job> sb_as_gemv(const bpw_sb_job *jobs, int32_t n) {
 size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch) {
     if (!jobs || n_jobs <= 0 || batch < 1) return 0;
     size_t need = sb_layout(jobs, n_jobs, batch).total;
+    if (tok_ok(jobs, n_jobs, batch)) need = std::max(need, tok_layout(jobs, n_jobs).total);
     if (batch == 1) {
         const std::vector<bpw_gemv_job> g = sb_as_gemv(jobs, n_jobs);
         need = std::max(need, bpw_gemv_workspace_bytes(g.data(), n_jobs));
@@ -1059,9 +1104,13 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
     if (!out) return fail(BPW_E_INVAL, "out is NULL");
     *out = nullptr;
     if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return fail(BPW_E_INVAL, "bad job list");
-    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_MFMA)
-        return fail(BPW_E_UNSUPPORTED, "grouped small batch runs on the matrix cores only (kernel %d)", (int)kernel);
+    if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_MFMA && kernel != BPW_KERNEL_BITSERIAL)
+        return fail(BPW_E_UNSUPPORTED, "grouped small batch: unknown kernel %d", (int)kernel);
     if (batch < 1 || batch > bpw::kMaxBatch) return fail(BPW_E_INVAL, "batch %d outside [1, 64]", (int)batch);
+    if (kernel == BPW_KERNEL_BITSERIAL && batch > 1 && !tok_ok(jobs, n_jobs, batch))
+        return fail(BPW_E_UNSUPPORTED,
+                    "grouped small batch, bit-serial: 2 to %d tokens of 2560- or 6912-column matrices only (pinned: "
+                    "bit-serial)", bpw::kTokMax);
     char who[48];
     for (int32_t i = 0; i < n_jobs; ++i) {
         std::snprintf(who, sizeof who, "small-batch job %d", i);
@@ -1087,11 +1136,65 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
     plan->tiles = reinterpret_cast<const bpw::SBTile *>(ws + L.tiles_off);
     plan->n_tiles = L.n_tiles;
     plan->gemv = nullptr;
+    plan->tok_jobs = nullptr;
+    plan->tok_tiles = nullptr;
+    plan->n_tok_tiles = 0;
+    plan->nt = 0;
     if (n_jobs == 0 || L.n_tiles == 0) {
         *out = plan;
         return BPW_OK;
     }
-    if (batch == 1 && kernel == BPW_KERNEL_AUTO) {
+    // Measured on the decode-step set (three HBM copies in rotation): the token kernel takes 114.7 us
+    // at B = 2 (matrix cores 151.5), 149.3 at B = 3, 188.3 at B = 4 (matrix cores 158.6): each token
+    // adds ~36 us of select work and plane reads. AUTO therefore sends 2 and 3 tokens to it.
+    const bool tok_auto = kernel == BPW_KERNEL_AUTO && batch <= kTokAutoMax && tok_ok(jobs, n_jobs, batch);
+    if (tok_auto || (kernel == BPW_KERNEL_BITSERIAL && batch > 1)) {
+        // each beat streamed once and reduced against every token's planes on the VALU
+        const SBLayout T = tok_layout(jobs, n_jobs);
+        std::vector<uint8_t> host(T.total, 0);
+        auto *hj = reinterpret_cast<bpw::TokJob *>(host.data() + T.jobs_off);
+        auto *hb = reinterpret_cast<bpw::Tile *>(host.data() + T.tiles_off);
+        int64_t t = 0;
+        for (int32_t i = 0; i < n_jobs; ++i) {
+            const bpw_sb_job &j = jobs[i];
+            bpw::TokJob d{};
+            d.planes = static_cast<const uint8_t *>(j.m.d_planes);
+            d.X = j.d_X;
+            d.out_i32 = j.d_out_i32;
+            d.out_f32 = j.d_out_f32;
+            d.ldx = j.ldx;
+            d.plane_bytes = (uint32_t)((uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u);
+            d.rows = (int32_t)j.m.rows;
+            d.bpr = (int32_t)j.m.bpr;
+            d.w_scale = j.m.w_scale;
+            for (int32_t k = 0; k < batch; ++k) d.x_scales[k] = j.x_scales[k];
+            hj[i] = d;
+            const Geometry g = geometry_for(j.m.bpr, true);
+            const int64_t U = units_of(j.m.rows, g), w = tok_tile_units(g);
+            for (int64_t u = 0; u < U; u += w) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + w), 0};
+        }
+        const int xccs = device_xcds();
+        if (xccs > kMaxXcds) {
+            delete plan;
+            return fail(BPW_E_UNSUPPORTED, "device has %d XCDs; the tile table is sized for %lld", xccs,
+                        (long long)kMaxXcds);
+        }
+        const double share = t < 2 * (int64_t)device_cus() ? 1.0 : kTailShare;
+        plan->n_tok_tiles = xcd_runs(hb, t, xccs, share);
+        plan->tok_jobs = reinterpret_cast<const bpw::TokJob *>(ws + T.jobs_off);
+        plan->tok_tiles = reinterpret_cast<const bpw::Tile *>(ws + T.tiles_off);
+        plan->nt = batch;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        st = hip_status(hipMemcpyAsync(d_ws, host.data(), T.total, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+        if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
+        if (st) {
+            delete plan;
+            return st;
+        }
+        *out = plan;
+        return BPW_OK;
+    }
+    if (batch == 1 && kernel != BPW_KERNEL_MFMA) {
         // one token: the bit-serial batch-1 GEMV streams the planes without decoding them (measured on
         // the decode-step set: 81.7 us against 148 us on the matrix cores)
         const std::vector<bpw_gemv_job> g = sb_as_gemv(jobs, n_jobs);
@@ -1135,6 +1238,10 @@ bpw_status bpw_gemm_small_batch_plan_run(const bpw_sb_plan *plan, void *stream) 
     bpw_status st = check_device();
     if (st) return st;
     if (plan->gemv) return bpw_gemv_plan_run(plan->gemv, stream);
+    if (plan->n_tok_tiles > 0)
+        return hip_status(bpw::launch_gemv_tokens(plan->tok_jobs, plan->tok_tiles, (int32_t)plan->n_tok_tiles, plan->nt,
+                                                  stream),
+                          "grouped small batch (bit-serial tokens) launch");
     return hip_status(bpw::launch_gemm_small_batch_grouped(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
                       "grouped small batch launch");
 }

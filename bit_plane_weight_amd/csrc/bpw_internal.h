@@ -90,6 +90,22 @@ struct SBTile {
     int32_t pad;
 };
 
+// One GEMV of 2 to 4 tokens in the grouped small-batch launch (bit-serial; 2560 or 6912 columns).
+// The tile table is the batch-1 one (Tile); a tile holds at most kTokTileRows rows.
+constexpr int kTokMax = 4;
+constexpr int kTokTileRows = 256;
+struct TokJob {
+    const uint8_t *planes;
+    const int8_t *X;      // [batch][ldx]
+    int32_t *out_i32;     // [batch][rows]
+    float *out_f32;       // [batch][rows] or null
+    int64_t ldx;
+    uint32_t plane_bytes;
+    int32_t rows, bpr;
+    float w_scale;
+    float x_scales[kTokMax];
+};
+
 // BITCOS GEMV launch geometry: 8 waves per workgroup (two workgroups per CU share the LDS, each
 // holding the 64 KiB deposit table), tiles of kBcTileUnits row-groups. A row of bpr blocks is held by
 // 2^glog lanes with k contiguous blocks each (k * 2^glog >= bpr); a row-group is the 64 >> glog rows
@@ -148,6 +164,7 @@ int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
 int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream);
+int launch_gemv_tokens(const TokJob *jobs, const Tile *tiles, int32_t n_tiles, int32_t nt, void *stream);
 int launch_gemv_bitcos(const BitcosJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_quantize(const QuantJob *jobs, int32_t n_jobs, void *stream);

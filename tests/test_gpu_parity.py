@@ -673,6 +673,66 @@ def test_small_batch_grouped(dev, batch, kernel):
     plan.free()
 
 
+TOKEN_SHAPES = ((6912, 2560), (2560, 6912), (640, 2560), (1, 2560), (7, 2500), (65, 6850), (129, 6900),
+                (1025, 2560), (3, 6912))
+
+
+@pytest.mark.parametrize("kernel", (bpw.KERNEL_AUTO, bpw.KERNEL_BITSERIAL))
+@pytest.mark.parametrize("batch", (2, 3, 4))
+def test_small_batch_grouped_tokens(dev, batch, kernel):
+    """2 to 4 tokens over the two model row widths (with ragged rows, ragged columns and junk past
+    cols in X): the bit-serial token kernel, under AUTO and pinned, equals the oracle and the matrix-core
+    kernel bit for bit, on two runs of one plan."""
+    log(f"case: grouped small batch, bit-serial tokens, B={batch} kernel={kernel}")
+    sets = [_sb_inputs(dev, 1200 + 13 * i + batch, r, c, batch) for i, (r, c) in enumerate(TOKEN_SHAPES)]
+    jobs = [bpw.sb_job(u.m, Xd, sc, oi, of) for (case, u, Xh, Xd, sc, oi, of) in sets]
+    ws = torch.empty(max(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), 256), dtype=torch.uint8, device=dev)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws, kernel)
+    plan.run()
+    plan.run()
+    torch.cuda.synchronize()
+    for (case, u, Xh, Xd, sc, oi, of) in sets:
+        if case.rows == 0:
+            continue
+        acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), case.rows, case.cols, Xh, sc, case.w_scale,
+                                                nthreads=NT)
+        assert np.array_equal(oi.cpu().numpy(), acc), f"{case.rows}x{case.cols}"
+        assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32)), f"{case.rows}x{case.cols}"
+        oi2 = torch.empty_like(oi)
+        of2 = torch.empty_like(of)
+        bpw.bpw_gemm_small_batch(u.m, Xd, sc, oi2, of2, bpw.KERNEL_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(oi2, oi) and torch.equal(of2.view(torch.int32), of.view(torch.int32))
+    plan.free()
+
+
+def test_small_batch_grouped_tokens_decode_step(dev):
+    """The 210 matrices of a decode step at B = 2 in one launch of the token kernel (the benchmark's
+    launch), every output against the oracle."""
+    log("case: grouped small batch, decode step, B=2 (bit-serial tokens)")
+    batch = 2
+    sets, jobs = [], []
+    for layer in range(synth.N_LAYERS):
+        for c in synth.layer_cases(707, layer):
+            u = Uploaded(c, dev)
+            X, sc = synth.small_batch_x(7000 + 7 * layer + len(sets), batch, c.cols)
+            Xd = torch.from_numpy(np.ascontiguousarray(X)).to(dev)
+            oi = torch.full((batch, c.rows), -7, dtype=torch.int32, device=dev)
+            of = torch.full((batch, c.rows), -7.0, dtype=torch.float32, device=dev)
+            sets.append((c, u, X, Xd, sc, oi, of))
+            jobs.append(bpw.sb_job(u.m, Xd, sc, oi, of))
+    ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws)
+    plan.run()
+    torch.cuda.synchronize()
+    log("  GPU done; oracle over 210 matrices x 2 tokens")
+    for (c, u, X, Xd, sc, oi, of) in sets:
+        acc, y32, _ = oracle.gemm_small_batch(oracle.pack(c.w), c.rows, c.cols, X, sc, c.w_scale, nthreads=NT)
+        assert np.array_equal(oi.cpu().numpy(), acc), c.name
+        assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32)), c.name
+    plan.free()
+
+
 def test_small_batch_grouped_new_inputs_and_errors(dev):
     log("case: grouped small batch plan reuse and argument errors")
     batch = 4
@@ -691,10 +751,22 @@ def test_small_batch_grouped_new_inputs_and_errors(dev):
     assert np.array_equal(oi.cpu().numpy(), acc)
     assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32))
     plan.free()
-    for kernel in (bpw.KERNEL_BITSERIAL, bpw.KERNEL_BYTELANE):
-        with pytest.raises(bpw.BpwError) as ei:
-            bpw.SmallBatchPlan(jobs, batch, ws, kernel)
-        assert ei.value.status == _lib.E_UNSUPPORTED
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.SmallBatchPlan(jobs, batch, ws, bpw.KERNEL_BYTELANE)
+    assert ei.value.status == _lib.E_UNSUPPORTED
+    # the bit-serial token kernel: at most 4 tokens, model row widths only
+    case5, u5, _, Xd5, sc5, oi5, of5 = _sb_inputs(dev, 952, 64, 2560, 5)
+    j5 = [bpw.sb_job(u5.m, Xd5, sc5, oi5, of5)]
+    ws5 = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(j5, 5), dtype=torch.uint8, device=dev)
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.SmallBatchPlan(j5, 5, ws5, bpw.KERNEL_BITSERIAL)
+    assert ei.value.status == _lib.E_UNSUPPORTED
+    case3, u3, _, Xd3, sc3, oi3, of3 = _sb_inputs(dev, 953, 64, 2000, 3)
+    j3 = [bpw.sb_job(u3.m, Xd3, sc3, oi3, of3)]
+    ws3 = torch.empty(max(bpw.bpw_gemm_small_batch_workspace_bytes(j3, 3), 256), dtype=torch.uint8, device=dev)
+    with pytest.raises(bpw.BpwError) as ei:
+        bpw.SmallBatchPlan(j3, 3, ws3, bpw.KERNEL_BITSERIAL)
+    assert ei.value.status == _lib.E_UNSUPPORTED
     with pytest.raises(bpw.BpwError) as ei:
         bpw.SmallBatchPlan(jobs, batch, ws[:256])
     assert ei.value.status == _lib.E_SIZE

@@ -48,3 +48,22 @@ def test_streaming_loops_wait_only_for_the_older_loads(tmp_path):
     for name, body in loops.items():
         waits = [int(m.group(1)) for x in body if (m := re.search(r"vmcnt\((\d+)\)", x))]
         assert waits and min(waits) > 0, f"loop {name}: vmcnt waits {waits}"
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
+def test_token_kernel_loops_wait_only_for_the_older_loads(tmp_path):
+    """The same property for the 2-, 3- and 4-token kernels of the grouped small batch: per kernel one
+    2560-column loop (2 x 5 beat loads) and one 6912-column loop (2 x 4), waits never vmcnt(0)."""
+    out = tmp_path / "tokens.s"
+    src = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_gemv_tokens.hip")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
+                    src, "-o", str(out)], check=True, capture_output=True)
+    kernels = re.split(r"\n(?=_ZN3bpw18gemv_tokens_kernel)", out.read_text())[1:]
+    assert len(kernels) == 3
+    for k in kernels:
+        loops = {n: b for n, b in loop_bodies(k).items() if sum("buffer_load_dwordx4" in x for x in b) >= 4}
+        assert sorted(sum("buffer_load_dwordx4" in x for x in b) for b in loops.values()) == [8, 10], loops.keys()
+        for name, body in loops.items():
+            waits = [int(m.group(1)) for x in body if (m := re.search(r"vmcnt\((\d+)\)", x))]
+            assert waits and min(waits) > 0, f"loop {name}: vmcnt waits {waits}"
