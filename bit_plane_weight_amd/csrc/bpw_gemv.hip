@@ -23,8 +23,9 @@
 namespace bpw {
 
 // ------------------------------------------------------------------------------------------
-// Batch-1 grouped GEMV, bit-serial select. The host cuts every job's row-groups into tiles of about
-// 80 KB of planes (one job each) and the grid has one workgroup of kWaves waves per tile; the
+// Batch-1 grouped GEMV, bit-serial select. The host cuts every job's row-groups into tiles (one job
+// each; wide ones first and narrow ones last on each XCD) and the grid has one workgroup of kWaves
+// waves per tile; the
 // hardware dispatcher hands tiles to compute units as earlier ones finish, so every compute unit
 // streams until the whole list is done. Per tile the workgroup builds the job's activation planes
 // in LDS, then its waves claim row-groups from an LDS counter: a compute unit serves older waves
