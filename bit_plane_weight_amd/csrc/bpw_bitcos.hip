@@ -176,9 +176,10 @@ __device__ __forceinline__ void bc_load_windows(u32x4 (&W)[K], const BcPresence<
     }
 }
 
-// Decode the lane's K blocks to planes and accumulate their select-popcounts (cs[j]: plane j, cn: neg).
+// Decode the lane's K blocks to planes and accumulate their select-popcounts (cs[j], ch[j]: plane j
+// over the low and high 32 columns; cn: neg).
 template <int K, int GLOG>
-__device__ __forceinline__ void bc_decode(uint32_t (&cs)[8], uint32_t &cn, const BcPresence<K> &P,
+__device__ __forceinline__ void bc_decode(uint32_t (&cs)[8], uint32_t (&ch)[8], uint32_t &cn, const BcPresence<K> &P,
                                           const u32x4 (&W)[K], const BcShared &sh, const BcRowCtx &c) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
@@ -194,18 +195,20 @@ __device__ __forceinline__ void bc_decode(uint32_t (&cs)[8], uint32_t &cn, const
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u32x4 X = sh.xl[bc_quarter(k, c.g, 1 << GLOG, i)];
-            // words 4i .. 4i+3: planes 2i (lo, hi) and 2i + 1 (lo, hi)
+            // words 4i .. 4i+3: planes 2i (lo, hi) and 2i + 1 (lo, hi); the halves count separately, so
+            // each popcount adds into its own counter in one v_bcnt_u32_b32
             cs[2 * i] = __builtin_popcount(select_bits(X.x, qlo, nlo)) + cs[2 * i];
-            cs[2 * i] = __builtin_popcount(select_bits(X.y, qhi, nhi)) + cs[2 * i];
+            ch[2 * i] = __builtin_popcount(select_bits(X.y, qhi, nhi)) + ch[2 * i];
             cs[2 * i + 1] = __builtin_popcount(select_bits(X.z, qlo, nlo)) + cs[2 * i + 1];
-            cs[2 * i + 1] = __builtin_popcount(select_bits(X.w, qhi, nhi)) + cs[2 * i + 1];
+            ch[2 * i + 1] = __builtin_popcount(select_bits(X.w, qhi, nhi)) + ch[2 * i + 1];
         }
         cn = __builtin_popcount(nlo) + cn;
         cn = __builtin_popcount(nhi) + cn;
         // keep the next block's table and plane reads (and any later load) below this block: hoisted,
         // they would hold more registers than the occupancy allows
         asm volatile("" : "+v"(cs[0]), "+v"(cs[1]), "+v"(cs[2]), "+v"(cs[3]), "+v"(cs[4]), "+v"(cs[5]), "+v"(cs[6]),
-                     "+v"(cs[7]), "+v"(cn)::"memory");
+                     "+v"(cs[7]), "+v"(ch[0]), "+v"(ch[1]), "+v"(ch[2]), "+v"(ch[3]), "+v"(ch[4]), "+v"(ch[5]),
+                     "+v"(ch[6]), "+v"(ch[7]), "+v"(cn)::"memory");
     }
 }
 
@@ -236,12 +239,13 @@ __device__ __forceinline__ void bc_tile(const BitcosJob &J, int u0, int u1, int 
         if (i >= 2 && ud < u1) {  // wave-uniform
             const int row = ud * kUnitRows + q;
             uint32_t cs[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+            uint32_t ch[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
             uint32_t cn = 0;
-            bc_decode<K, GLOG>(cs, cn, P[i - 2], W[i - 2], sh, c);
+            bc_decode<K, GLOG>(cs, ch, cn, P[i - 2], W[i - 2], sh, c);
             int32_t acc = (int32_t)cn;
 #pragma unroll
-            for (int j = 0; j < 7; ++j) acc += (int32_t)(cs[j] << j);
-            acc -= (int32_t)(cs[7] << 7);
+            for (int j = 0; j < 7; ++j) acc += (int32_t)((cs[j] + ch[j]) << j);
+            acc -= (int32_t)((cs[7] + ch[7]) << 7);
             const int32_t tot = group_sum(acc, GLOG);
             if (c.g == 0 && row < J.rows) {
                 J.out_i32[row] = tot;
