@@ -131,6 +131,13 @@ __device__ __forceinline__ void read_planes(uint32_t (&X)[16], const u32x4 *xl, 
     }
 }
 
+// acc += popc(v) as one accumulating v_bcnt_u32_b32. Written as an asm statement because with two
+// popcounts into one counter the compiler emits two plain popcounts and a v_add3 instead (8 more VALU
+// per beat; measured on the decode step: 77.2 against 77.9-78.1 us).
+__device__ __forceinline__ void bcnt_acc(uint32_t &acc, uint32_t v) {
+    asm("v_bcnt_u32_b32 %0, %1, %0" : "+v"(acc) : "v"(v));
+}
+
 // Exact partial sum of one row over the K beats a lane holds, activation planes from LDS:
 //   sum_j w_j * popc(select(X_j, pos, neg)) + popc(neg),  w_j = 2^j, w_7 = -128.
 // The planes of beat k+1 are read while beat k is reduced; the empty asm statements keep the
@@ -150,7 +157,7 @@ __device__ __forceinline__ int32_t row_partial(const u32x4 *xl, const u32x4 (&B)
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             c[j] = __builtin_popcount(select_bits(X[2 * j], B[k].x, B[k].z)) + c[j];
-            c[j] = __builtin_popcount(select_bits(X[2 * j + 1], B[k].y, B[k].w)) + c[j];
+            bcnt_acc(c[j], select_bits(X[2 * j + 1], B[k].y, B[k].w));
         }
         cn = __builtin_popcount(B[k].z) + cn;
         cn = __builtin_popcount(B[k].w) + cn;
