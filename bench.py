@@ -527,6 +527,31 @@ def cpu_baseline(sample, nthreads: int, min_seconds: float = 10.0) -> dict:
     }
 
 
+def cpu_single_thread(sample, min_seconds: float = 3.0) -> dict:
+    """The same oracle passes on one host thread (a shorter bounded sample), and the host it ran on."""
+    import oracle
+    packed = [(oracle.pack(c.w), c) for c in sample]
+    seconds, nbytes = 0.0, 0
+    while seconds < min_seconds:
+        for planes, c in packed:
+            t = time.perf_counter()
+            oracle.gemv(planes, c.rows, c.cols, c.x, c.x_scale, c.w_scale, nthreads=1)
+            seconds += time.perf_counter() - t
+            nbytes += planes.size
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"single_thread_gbs": round(nbytes / seconds / 1e9, 4),
+            "host": f"{model}, {len(os.sched_getaffinity(0))} CPUs available to this process",
+            "seconds": round(seconds, 1)}
+
+
 def traffic_from_profile() -> float | None:
     """HBM bytes per GEMV launch from the committed rocprofv3 counter summary, if it was taken on
     the current kernel source; otherwise None."""
@@ -646,6 +671,7 @@ def main() -> int:
     }
     if sample:
         result["cpu_baseline"] = cpu_baseline(sample, nthreads)
+        result["cpu_oracle_single_thread"] = cpu_single_thread(sample)
 
     if args.copy_calibration:
         log("copy calibration: probe reads 1 GiB, flush reads and writes 1 GiB, 3 times each")
