@@ -47,6 +47,45 @@ def _dptr(t) -> int | None:
     return t.data_ptr()
 
 
+def _checked(t, dtype: str, n: int, what: str) -> int | None:
+    """Device address of a tensor the kernels read or write, after checking its element type and
+    that it holds at least n elements (None stays NULL). The C ABI carries no lengths for outputs,
+    so this is where an undersized or mistyped buffer is refused, before anything is launched."""
+    if t is None:
+        return None
+    import torch
+    want = getattr(torch, dtype)
+    if t.dtype != want:
+        raise TypeError(f"{what} must be {want}, got {t.dtype}")
+    if t.numel() < n:
+        raise ValueError(f"{what} holds {t.numel()} elements, needs at least {n}")
+    return _dptr(t)
+
+
+def _bytes_of(t, what: str) -> int:
+    """Byte length of a one-byte-element tensor (int8 codes, uint8 planes)."""
+    if t.element_size() != 1:
+        raise TypeError(f"{what} must have one-byte elements (int8 or uint8), got {t.dtype}")
+    return t.numel()
+
+
+class _Job:
+    """One job of a grouped call: the ctypes record the C ABI reads (``c``) plus every object whose
+    device memory that record names (the matrix and its plane buffer, activations, scales, outputs).
+    Plans hold their jobs, so those buffers live as long as the plan that launches on them."""
+
+    def __init__(self, c, keep):
+        object.__setattr__(self, "c", c)
+        object.__setattr__(self, "_keep", keep)
+
+    # the record's fields read and write through the job (job.d_x, job.m.rows, ...)
+    def __getattr__(self, name):
+        return getattr(self.c, name)
+
+    def __setattr__(self, name, value):
+        setattr(self.c, name, value)
+
+
 def _stream(stream) -> int | None:
     if stream is None:
         import torch
@@ -157,23 +196,31 @@ def bpw_upload(m: HostMat, d_buf, stream=None) -> DevMat:
 # ------------------------------------------------------------------------------ batch-1 GEMV
 
 
-def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None, x_scale_dev=None) -> BpwGemvJob:
+def gemv_job(m: DevMat, x, x_scale: float, out_i32, out_f32=None, x_scale_dev=None) -> _Job:
     """One bpw_gemv_job: x int8 GPU tensor (>= bpr * 64 bytes), outputs int32 / float32 [rows].
-    x_scale_dev (a float32 GPU tensor of one element) makes the kernel read the scale there."""
+    x_scale_dev (a float32 GPU tensor of one element) makes the kernel read the scale there. The
+    returned job keeps m, x, the outputs and x_scale_dev alive."""
     j = BpwGemvJob()
     j.m = m.desc
+    j.x_len = _bytes_of(x, "x")
     j.d_x = _dptr(x)
-    j.x_len = x.numel() * x.element_size()
     j.x_scale = float(x_scale)
-    j.d_out_i32 = _dptr(out_i32)
-    j.d_out_f32 = _dptr(out_f32)
-    j.d_x_scale = _dptr(x_scale_dev)
-    return j
+    if out_i32 is None:
+        raise ValueError("out_i32 is required")
+    j.d_out_i32 = _checked(out_i32, "int32", m.rows, "out_i32")
+    j.d_out_f32 = _checked(out_f32, "float32", m.rows, "out_f32")
+    j.d_x_scale = _checked(x_scale_dev, "float32", 1, "x_scale_dev")
+    return _Job(j, (m, x, out_i32, out_f32, x_scale_dev))
+
+
+def _records(jobs, ctype):
+    """ctypes array of the jobs' records (a _Job's ``c``, or a bare record)."""
+    recs = [j.c if isinstance(j, _Job) else j for j in jobs]
+    return (ctype * max(1, len(recs)))(*recs), len(recs)
 
 
 def _jobs_array(jobs):
-    arr = (BpwGemvJob * max(1, len(jobs)))(*jobs)
-    return arr, len(jobs)
+    return _records(jobs, BpwGemvJob)
 
 
 def bpw_gemv_workspace_bytes(jobs) -> int:
@@ -182,27 +229,27 @@ def bpw_gemv_workspace_bytes(jobs) -> int:
 
 
 def intmlp_job(gate: DevMat, up: DevMat, x, x_scale: float, t_out, k_out, gate_i32=None, up_i32=None,
-               x_scale_dev=None) -> _lib.BpwIntMlpJob:
+               x_scale_dev=None) -> _Job:
     """One bpw_intmlp_job: gate and up (same shape) read the int8 GPU tensor x; t_out int64 [rows]
     receives relu(a_g)^2 * a_u, k_out float64 [1] receives K; gate_i32 / up_i32 optional int32 [rows]."""
     j = _lib.BpwIntMlpJob()
     j.gate = gate.desc
     j.up = up.desc
+    j.x_len = _bytes_of(x, "x")
     j.d_x = _dptr(x)
-    j.x_len = x.numel() * x.element_size()
     j.x_scale = float(x_scale)
-    j.d_x_scale = _dptr(x_scale_dev)
-    j.d_t = _dptr(t_out)
-    j.d_k = _dptr(k_out)
-    j.d_gate_i32 = _dptr(gate_i32)
-    j.d_up_i32 = _dptr(up_i32)
-    return j
+    j.d_x_scale = _checked(x_scale_dev, "float32", 1, "x_scale_dev")
+    if t_out is None or k_out is None:
+        raise ValueError("t_out and k_out are required")
+    j.d_t = _checked(t_out, "int64", gate.rows, "t_out")
+    j.d_k = _checked(k_out, "float64", 1, "k_out")
+    j.d_gate_i32 = _checked(gate_i32, "int32", gate.rows, "gate_i32")
+    j.d_up_i32 = _checked(up_i32, "int32", gate.rows, "up_i32")
+    return _Job(j, (gate, up, x, x_scale_dev, t_out, k_out, gate_i32, up_i32))
 
 
 def _mlp_array(mlp):
-    mlp = list(mlp or [])
-    arr = (_lib.BpwIntMlpJob * max(1, len(mlp)))(*mlp)
-    return arr, len(mlp)
+    return _records(list(mlp or []), _lib.BpwIntMlpJob)
 
 
 def bpw_gemv_intmlp_workspace_bytes(jobs, mlp) -> int:
@@ -252,22 +299,24 @@ class GemvPlan:
 # ------------------------------------------------------------------------------ quantiser
 
 
-def quant_job(h, g, q, scale, eps: float) -> BpwQuantJob:
+def quant_job(h, g, q, scale, eps: float) -> _Job:
     """One bpw_quant_job: h, g float32 GPU tensors [n]; q int8 GPU tensor (>= n); scale float32 [1]."""
     j = BpwQuantJob()
-    j.d_h, j.d_g = _dptr(h), _dptr(g)
     j.n = h.numel()
     if g.numel() != j.n:
         raise ValueError("h and g must have the same length")
-    j.d_q, j.q_len = _dptr(q), q.numel()
-    j.d_scale = _dptr(scale)
+    j.d_h, j.d_g = _checked(h, "float32", j.n, "h"), _checked(g, "float32", j.n, "g")
+    j.q_len = _bytes_of(q, "q")
+    j.d_q = _dptr(q)
+    if scale is None:
+        raise ValueError("scale is required")
+    j.d_scale = _checked(scale, "float32", 1, "scale")
     j.eps = float(eps)
-    return j
+    return _Job(j, (h, g, q, scale))
 
 
 def _quant_array(jobs):
-    arr = (BpwQuantJob * max(1, len(jobs)))(*jobs)
-    return arr, len(jobs)
+    return _records(jobs, BpwQuantJob)
 
 
 def bpw_quantize_workspace_bytes(n_jobs: int) -> int:
@@ -311,11 +360,16 @@ class QuantPlan:
 def bpw_gemm_small_batch(m: DevMat, X, x_scales, out_i32, out_f32, kernel: int = KERNEL_AUTO, stream=None) -> None:
     """X int8 GPU tensor [batch, ldx]; x_scales host float32 [batch]; outputs [batch, rows]."""
     batch, ldx = X.shape
+    _bytes_of(X, "X")
     xs = np.ascontiguousarray(np.asarray(x_scales, dtype=np.float32))
     if xs.shape != (batch,):
         raise ValueError(f"x_scales must hold {batch} values")
+    if out_i32 is None:
+        raise ValueError("out_i32 is required")
+    oi = _checked(out_i32, "int32", batch * m.rows, "out_i32")
+    of = _checked(out_f32, "float32", batch * m.rows, "out_f32")
     _lib.check(_lib.lib().bpw_gemm_small_batch(ctypes.byref(m.desc), _dptr(X), batch, ldx, xs.ctypes.data,
-                                               _dptr(out_i32), _dptr(out_f32), kernel, _stream(stream)))
+                                               oi, of, kernel, _stream(stream)))
 
 
 class _SbJob:
@@ -328,15 +382,18 @@ class _SbJob:
         self.scales = np.ascontiguousarray(np.asarray(x_scales, dtype=np.float32))
         if self.scales.shape != (batch,):
             raise ValueError(f"x_scales must hold {batch} values")
+        _bytes_of(X, "X")
+        if out_i32 is None:
+            raise ValueError("out_i32 is required")
         j = _lib.BpwSbJob()
         j.m = m.desc
         j.d_X = _dptr(X)
         j.ldx = ldx
         j.x_scales = self.scales.ctypes.data
-        j.d_out_i32 = _dptr(out_i32)
-        j.d_out_f32 = _dptr(out_f32)
+        j.d_out_i32 = _checked(out_i32, "int32", batch * m.rows, "out_i32")
+        j.d_out_f32 = _checked(out_f32, "float32", batch * m.rows, "out_f32")
         self.c = j
-        self._keep = (X, out_i32, out_f32)
+        self._keep = (m, X, out_i32, out_f32)
 
 
 def sb_job(m: DevMat, X, x_scales, out_i32, out_f32=None) -> _SbJob:
@@ -484,14 +541,21 @@ class TritFile:
 def bpw_dense_head_gemv(w_bf16, x_bf16, y, stream=None) -> None:
     """w_bf16 [rows, cols] and x_bf16 [cols] GPU tensors of bf16 bits (int16/uint16/bfloat16); y float32."""
     rows, cols = w_bf16.shape
-    _lib.check(_lib.lib().bpw_dense_head_gemv(_dptr(w_bf16), rows, cols, _dptr(x_bf16), _dptr(y),
-                                              _stream(stream)))
+    for t, what in ((w_bf16, "w_bf16"), (x_bf16, "x_bf16")):
+        if t.element_size() != 2:
+            raise TypeError(f"{what} must hold 16-bit elements (bf16 bit patterns), got {t.dtype}")
+    if x_bf16.numel() < cols:
+        raise ValueError(f"x_bf16 holds {x_bf16.numel()} elements, needs at least {cols}")
+    _lib.check(_lib.lib().bpw_dense_head_gemv(_dptr(w_bf16), rows, cols, _dptr(x_bf16),
+                                              _checked(y, "float32", rows, "y"), _stream(stream)))
 
 
 # ------------------------------------------------------------------------------ measurement
 
 
 def bpw_stream_read_probe(d_buf, d_sink, stream=None) -> None:
+    if d_sink is None or d_sink.element_size() != 4 or d_sink.numel() < 1:
+        raise ValueError("d_sink must be a 4-byte-element tensor of at least one element")
     _lib.check(_lib.lib().bpw_stream_read_probe(_dptr(d_buf), d_buf.numel() * d_buf.element_size(),
                                                 _dptr(d_sink), _stream(stream)))
 
@@ -591,20 +655,22 @@ def bpw_bitcos_upload(h: BitcosHost, d_buf, stream=None) -> DevBitcos:
     return DevBitcos(desc, d_buf)
 
 
-def bitcos_job(m: DevBitcos, x, x_scale: float, out_i32, out_f32=None) -> _lib.BpwBitcosJob:
+def bitcos_job(m: DevBitcos, x, x_scale: float, out_i32, out_f32=None) -> _Job:
+    """One bpw_bitcos_job (outputs int32 / float32 [rows]); the job keeps m, x and the outputs alive."""
     j = _lib.BpwBitcosJob()
     j.m = m.desc
+    j.x_len = _bytes_of(x, "x")
     j.d_x = _dptr(x)
-    j.x_len = x.numel() * x.element_size()
     j.x_scale = float(x_scale)
-    j.d_out_i32 = _dptr(out_i32)
-    j.d_out_f32 = _dptr(out_f32)
-    return j
+    if out_i32 is None:
+        raise ValueError("out_i32 is required")
+    j.d_out_i32 = _checked(out_i32, "int32", m.rows, "out_i32")
+    j.d_out_f32 = _checked(out_f32, "float32", m.rows, "out_f32")
+    return _Job(j, (m, x, out_i32, out_f32))
 
 
 def _bitcos_array(jobs):
-    jobs = list(jobs)
-    return (_lib.BpwBitcosJob * max(1, len(jobs)))(*jobs), len(jobs)
+    return _records(list(jobs), _lib.BpwBitcosJob)
 
 
 def bpw_bitcos_workspace_bytes(jobs) -> int:

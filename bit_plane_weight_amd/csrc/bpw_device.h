@@ -71,7 +71,8 @@ __device__ __host__ __forceinline__ void delta_swap(uint32_t &lo, uint32_t &hi, 
 
 // 8 x 8 bit-matrix transpose of the eight bytes in hi:lo (byte i = row i, bit j = column j): after
 // it, byte j holds bit j of every input byte, input byte i at bit i. Three delta swaps at distances
-// 7, 14 and 28 exchange the off-diagonal 1x1, 2x2 and 4x4 blocks.
+// 7, 14 and 28 exchange the off-diagonal 1x1, 2x2 and 4x4 blocks: the published 8 x 8 transpose of
+// H. S. Warren, "Hacker's Delight", section 7-3 ("Transposing a Bit Matrix"), with its masks.
 __device__ __host__ __forceinline__ void transpose8x8(uint32_t &lo, uint32_t &hi) {
     delta_swap<7>(lo, hi, 0x00AA00AAu, 0x00AA00AAu);
     delta_swap<14>(lo, hi, 0x0000CCCCu, 0x0000CCCCu);

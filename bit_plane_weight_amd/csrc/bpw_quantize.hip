@@ -43,9 +43,12 @@ __device__ __forceinline__ void block_reduce(float &m, double &ss, float *smax, 
     }
 }
 
+// One code. A code whose float32 value is NaN (a NaN input, or an infinite one once m is infinite)
+// is 0; NaN inputs never raise m (fmaxf drops a NaN operand). Finite values clamp to +-127.
 __device__ __forceinline__ int8_t code_of(float u, float m) {
     if (!(m > 0.0f)) return 0;
     const float r = rintf((127.0f * u) / m);
+    if (r != r) return 0;
     return (int8_t)fminf(fmaxf(r, -127.0f), 127.0f);
 }
 

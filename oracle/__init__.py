@@ -74,7 +74,7 @@ def _load():
         lib.oracle_quantize.argtypes = [vp, vp, i64, f32, ci, vp, vp]
         lib.oracle_intmlp.argtypes = [vp, vp, i64, i64, i64, vp, i64, f32, f32, f32, vp, vp, vp, vp, ci, ep]
         lib.oracle_bitcos_pack_flat.argtypes = [vp, i64, vp, vp, vp]
-        lib.oracle_bitcos_unpack_flat.argtypes = [vp, vp, i64, vp]
+        lib.oracle_bitcos_unpack_flat.argtypes = [vp, i64, vp, i64, i64, vp]
         lib.oracle_bitcos_pack_rows.argtypes = [vp, i64, i64, vp, vp, vp]
         lib.oracle_bitcos_gemv.argtypes = [vp, vp, vp, i64, i64, vp, f32, f32, vp, vp, vp, ci]
         for f in ("oracle_pack", "oracle_validate", "oracle_unpack", "oracle_gemv",
@@ -235,10 +235,12 @@ def bitcos_pack_flat(w):
 
 
 def bitcos_unpack_flat(bitmap: bytes, signs: bytes, n: int) -> np.ndarray:
+    """n weights from a flat bitmap and sign vector; OracleError(SIZE) when the bitmap has more set
+    bits than the sign bytes hold."""
     b = np.frombuffer(bitmap, np.uint8).copy() if bitmap else np.zeros(1, np.uint8)
     s = np.frombuffer(signs, np.uint8).copy() if signs else np.zeros(1, np.uint8)
     w = np.zeros(max(n, 1), np.int8)
-    rc = _load().oracle_bitcos_unpack_flat(_p(b), _p(s), n, _p(w))
+    rc = _load().oracle_bitcos_unpack_flat(_p(b), len(bitmap), _p(s), len(signs), n, _p(w))
     if rc != OK:
         raise OracleError(rc, -1, -1, -1)
     return w[:n]

@@ -358,9 +358,13 @@ static double oracle_rms(const float *h, int64_t n, float eps) {
     return sqrt(ss / (double)n + (double)eps);
 }
 
+/* One absmax code. Non-finite input (the pages give no rule; reading adopted on both sides): a code
+ * whose float32 value is NaN is 0. That covers u = NaN, and u = +-inf once m is infinite (inf / inf);
+ * NaN entries never raise m, since a comparison with NaN is false. Finite values clamp to +-127. */
 static int8_t oracle_code(float v, float m) {
     float t = (127.0f * v) / m;
     float r = rintf(t);
+    if (r != r) return 0;
     if (r > 127.0f) r = 127.0f;
     if (r < -127.0f) r = -127.0f;
     return (int8_t)r;
@@ -468,16 +472,26 @@ int oracle_bitcos_pack_flat(const int8_t *w, int64_t n, uint8_t *bitmap, uint8_t
     return OR_OK;
 }
 
-int oracle_bitcos_unpack_flat(const uint8_t *bitmap, const uint8_t *signs, int64_t n, int8_t *w) {
-    if (n < 0 || (n && (!bitmap || !w))) return OR_E_INVAL;
-    int64_t k = 0;
+/* The inverse, from the definition of the two arrays: the k-th set presence bit (in weight order)
+ * takes sign bit k. The page prints an unpacker of its own; this one is written from the definition
+ * and checks its bounds: bitmap_len must cover n bits, and a bitmap with more set bits than the
+ * sign_len bytes hold sign bits is refused (OR_E_SIZE) instead of read past the signs. */
+int oracle_bitcos_unpack_flat(const uint8_t *bitmap, int64_t bitmap_len, const uint8_t *signs, int64_t sign_len,
+                              int64_t n, int8_t *w) {
+    if (n < 0 || bitmap_len < (n + 7) / 8 || sign_len < 0) return OR_E_INVAL;
+    if (n && (!bitmap || !w)) return OR_E_INVAL;
+    if (sign_len > 0 && !signs) return OR_E_INVAL;
+    int64_t next_sign = 0; /* the sign bit the next nonzero weight takes */
     for (int64_t i = 0; i < n; ++i) {
-        if ((bitmap[i >> 3] >> (i & 7)) & 1) {
-            w[i] = ((signs[k >> 3] >> (k & 7)) & 1) ? -1 : 1;
-            ++k;
-        } else {
+        const int present = (bitmap[i / 8] >> (i % 8)) & 1;
+        if (!present) {
             w[i] = 0;
+            continue;
         }
+        if (next_sign >= 8 * sign_len) return OR_E_SIZE;
+        const int negative = (signs[next_sign / 8] >> (next_sign % 8)) & 1;
+        w[i] = negative ? (int8_t)-1 : (int8_t)1;
+        ++next_sign;
     }
     return OR_OK;
 }

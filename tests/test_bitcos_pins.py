@@ -32,6 +32,20 @@ def test_flat_packer_equals_numpy_packbits(z):
     assert np.array_equal(oracle.bitcos_unpack_flat(bitmap, signs, w.size), w)
 
 
+def test_unpack_refuses_more_nonzeros_than_sign_bits():
+    """A bitmap whose set bits outnumber the sign bits is refused, not read past the signs: 9 set
+    presence bits need 2 sign bytes; one byte is short by a bit."""
+    w = np.array([1, -1, 1, 1, -1, 1, 1, 1, -1, 0, 0], np.int8)
+    bitmap, signs, nnz = oracle.bitcos_pack_flat(w)
+    assert nnz == 9 and len(signs) == 2
+    assert np.array_equal(oracle.bitcos_unpack_flat(bitmap, signs, w.size), w)
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.bitcos_unpack_flat(bitmap, signs[:1], w.size)
+    assert e.value.code == oracle.E_SIZE
+    # eight nonzeros fit exactly in one sign byte
+    assert np.array_equal(oracle.bitcos_unpack_flat(bitmap, signs[:1], 8), w[:8])
+
+
 def test_page_table_sizes():
     """The two tensors of the page's table: n weights at zero density z take ceil(n/8) + ceil(nnz/8)
     bytes, printed as 1.222 MB (1.4917 bits/w) and 3.571 MB (1.6146 bits/w); 2 - z at 0.5148 is

@@ -402,6 +402,66 @@ def test_quantize_closed_forms():
     assert not q.any() and s == 0.0
 
 
+def test_quantize_eps_inside_the_root_closed_forms():
+    """The norm's epsilon sits under the root: rms = sqrt(mean(h^2) + eps). Inputs are chosen so the
+    mean square plus eps is an exact square of a dyadic number, which makes the expected scale exact;
+    an eps added outside the root (or dropped) gives a different float32 scale in every case.
+    Constant h = c, g = 1: every code 127 sign(c), Folded scale (|c| / 127) / sqrt(c^2 + eps).
+    One-hot h = c e_k over n: code +-127 at k only, scale (|c| / 127) / sqrt(c^2 / n + eps).
+    The Reference mode materialises h / rms and gives the same scale here (rms is exact)."""
+    from fractions import Fraction
+    cases = [  # (n, one-hot?, c, eps, exact rms)
+        (64, False, 0.375, 7 / 64, Fraction(1, 2)),   # 9/64 + 7/64 = 1/4
+        (2560, False, -0.75, 0.4375, Fraction(1)),    # 9/16 + 7/16 = 1
+        (4, True, 1.0, 0.75, Fraction(1)),            # 1/4 + 3/4 = 1
+        (16, True, -2.0, 0.0, Fraction(1, 2)),        # 4/16 + 0 = 1/4
+        (256, True, 4.0, 3 / 16, Fraction(1, 2)),     # 16/256 + 3/16 = 1/4
+    ]
+    for n, onehot, c, eps, rms in cases:
+        h = np.zeros(n, np.float32) if onehot else np.full(n, c, np.float32)
+        if onehot:
+            h[n // 3] = c
+        g = np.ones(n, np.float32)
+        want = np.float32(float(Fraction(abs(c)) / 127 / rms))
+        for folded in (True, False):
+            q, s = oracle.quantize(h, g, eps, folded)
+            assert s == want, (n, c, eps, folded, s, want)
+            if onehot:
+                assert q[n // 3] == (127 if c > 0 else -127) and np.count_nonzero(q) == 1
+            else:
+                assert np.all(q == (127 if c > 0 else -127))
+        if eps > 0:  # the closed form separates eps under the root from eps added to the root
+            mean_sq = float(Fraction(c) ** 2 / (n if onehot else 1))
+            outside = np.float32((abs(c) / 127.0) / (mean_sq ** 0.5 + eps))
+            assert outside != want
+
+
+def test_quantize_non_finite_rule():
+    """Reading adopted on both sides: a code whose float32 value is NaN is 0 (a NaN input, or an
+    infinite one once the absmax is infinite); NaN never raises the absmax; finite codes are
+    unaffected by a NaN elsewhere."""
+    n = 64
+    h = np.linspace(-1.0, 1.0, n, dtype=np.float32)
+    g = np.ones(n, np.float32)
+    q0, s0 = oracle.quantize(h, g, 0.0, True)
+    hn = h.copy()
+    hn[5] = np.nan
+    q1, s1 = oracle.quantize(hn, g, 0.0, True)
+    assert q1[5] == 0
+    keep = np.arange(n) != 5
+    assert np.array_equal(q1[keep], q0[keep])  # max |u| is unchanged: the NaN never wins a comparison
+    assert np.isnan(s1)                          # the sum of squares carries the NaN into the scale
+    hi = h.copy()
+    hi[7] = np.inf
+    q2, s2 = oracle.quantize(hi, g, 0.0, True)
+    assert q2[7] == 0 and not q2[keep & (np.arange(n) != 7)].any()  # finite / inf = 0, inf / inf = NaN -> 0
+    gn = g.copy()
+    gn[9] = np.nan  # NaN gain, finite h: only that code is affected
+    q3, _ = oracle.quantize(h, gn, 0.0, True)
+    keep9 = np.arange(n) != 9
+    assert q3[9] == 0 and np.array_equal(q3[keep9], q0[keep9])
+
+
 def test_quantize_codes_against_exact_rationals():
     """Each Folded code is the float32 rounding of 127 u / m; checked against the exact rational
     value: the code is within 1/2 + (float32 error) of it, and equals it at exactly representable
