@@ -329,7 +329,7 @@ def test_argument_errors_on_gpu(dev):
         bpw.bpw_gemv([u.job()], ws[:16])
     assert ei.value.status == _lib.E_SIZE
     forged = bpw.DevMat(_lib.BpwDevMat.from_buffer_copy(u.m.desc), u.buf)
-    forged.desc.rows = 65
+    forged.desc.rows = 63  # (fewer rows than the output holds, so only the seal can refuse it)
     with pytest.raises(bpw.BpwError) as ei:
         bpw.bpw_gemv([bpw.gemv_job(forged, u.x, 1.0, u.oi)], ws)
     assert ei.value.status == _lib.E_NOT_VALIDATED
@@ -386,6 +386,34 @@ def test_quantize_folded_parity(dev, n, spread):
     assert not got[n:].any()
     gs = float(sd.item())
     assert abs(gs - s) <= abs(s) * 2.0 ** -23  # the float64 sum of squares may differ in its last bits
+
+
+@pytest.mark.parametrize("n", (64, 2560, 9000))
+def test_quantize_non_finite_inputs(dev, n):
+    """Non-finite residuals and gains: both sides give NaN codes the value 0 and let NaN never raise the
+    absmax, so the codes agree bit for bit; the scale is NaN or infinite on both sides alike."""
+    log(f"case: quantiser non-finite inputs n={n}")
+    for what in ("nan_h", "nan_g", "inf_h"):
+        h, g = _hg(4242 + n, n, 2.0)
+        if what == "nan_h":
+            h[[3, n // 2]] = np.nan
+        elif what == "nan_g":
+            g[[5, n - 1]] = np.nan
+        else:
+            h[n // 3] = np.inf
+        hd, gd = torch.from_numpy(h).to(dev), torch.from_numpy(g).to(dev)
+        qd = torch.full((n,), 55, dtype=torch.int8, device=dev)
+        sd = torch.full((1,), -1.0, dtype=torch.float32, device=dev)
+        ws = torch.empty(bpw.bpw_quantize_workspace_bytes(1), dtype=torch.uint8, device=dev)
+        bpw.bpw_quantize([bpw.quant_job(hd, gd, qd, sd, 1e-5)], ws)
+        torch.cuda.synchronize()
+        q, s = oracle.quantize(h, g, 1e-5, folded=True)
+        assert np.array_equal(qd.cpu().numpy(), q), what
+        gs = float(sd.item())
+        if np.isfinite(s):
+            assert abs(gs - s) <= abs(s) * 2.0 ** -23, what
+        else:
+            assert (np.isnan(s) and np.isnan(gs)) or gs == s, (what, gs, s)
 
 
 def test_quantize_zero_and_errors(dev):
