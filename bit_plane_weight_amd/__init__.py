@@ -19,7 +19,7 @@ __all__ = [
     "BpwError", "KERNEL_AUTO", "KERNEL_BITSERIAL", "KERNEL_BYTELANE", "KERNEL_MFMA",
     "bpw_abi_version", "bpw_status_string", "bpw_last_error", "bpw_device_check",
     "bpw_pack_i8", "bpw_validate", "bpw_load", "HostMat", "bpw_upload", "DevMat",
-    "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "GemvPlan",
+    "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "bpw_gemv_noalloc", "GemvPlan",
     "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
     "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
@@ -262,6 +262,12 @@ def bpw_gemv(jobs, d_ws, kernel: int = KERNEL_AUTO, stream=None) -> None:
     arr, n = _jobs_array(jobs)
     ws_len = 0 if d_ws is None else d_ws.numel() * d_ws.element_size()
     _lib.check(_lib.lib().bpw_gemv(arr, n, kernel, _dptr(d_ws), ws_len, _stream(stream)))
+
+
+def bpw_gemv_noalloc(jobs, kernel: int = KERNEL_AUTO, stream=None) -> None:
+    """bpw_gemv with the library's fixed device scratch in place of a workspace (allocates nothing)."""
+    arr, n = _jobs_array(jobs)
+    _lib.check(_lib.lib().bpw_gemv_noalloc(arr, n, kernel, _stream(stream)))
 
 
 class GemvPlan:

@@ -118,6 +118,7 @@ def lib():
         "bpw_upload": (i32, [vp, vp, sz, vp, M]),
         "bpw_gemv_workspace_bytes": (sz, [J, i32]),
         "bpw_gemv": (i32, [J, i32, i32, vp, sz, vp]),
+        "bpw_gemv_noalloc": (i32, [J, i32, i32, vp]),
         "bpw_gemv_plan_create": (i32, [J, i32, i32, vp, sz, vp, ctypes.POINTER(vp)]),
         "bpw_gemv_intmlp_workspace_bytes": (sz, [J, i32, ctypes.POINTER(BpwIntMlpJob), i32]),
         "bpw_gemv_intmlp_plan_create": (i32, [J, i32, ctypes.POINTER(BpwIntMlpJob), i32, i32, vp, sz, vp,

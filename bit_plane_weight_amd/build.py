@@ -7,7 +7,8 @@ import subprocess
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = [os.path.join(_HERE, "csrc", f) for f in (
     "bpw_host.cpp", "bpw_gemv.hip", "bpw_gemv_tokens.hip", "bpw_bytelane.hip", "bpw_small_batch.hip", "bpw_dense_head.hip",
-    "bpw_quantize.hip", "bpw_measure.hip", "bpw_trit.cpp", "bpw_bitcos.hip", "bpw_bitcos_host.cpp")]
+    "bpw_quantize.hip", "bpw_measure.hip", "bpw_trit.cpp", "bpw_bitcos.hip", "bpw_bitcos_host.cpp",
+    "bpw_static.hip")]
 OUT = os.path.join(_HERE, "libbpw.so")
 
 HIPCC_FLAGS = [

@@ -849,6 +849,22 @@ bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, vo
     return st;
 }
 
+bpw_status bpw_gemv_noalloc(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *stream) {
+    if (n_jobs == 0) return BPW_OK;
+    if (n_jobs < 0 || !jobs) return fail(BPW_E_INVAL, "bad job list");
+    bpw_status st = check_device();
+    if (st) return st;
+    void *ws = nullptr;
+    size_t cap = 0;
+    st = hip_status(bpw::static_scratch(&ws, &cap), "static scratch lookup (hipGetSymbolAddress)");
+    if (st) return st;
+    const size_t need = bpw_gemv_workspace_bytes(jobs, n_jobs);
+    if (need > cap)
+        return fail(BPW_E_SIZE, "bpw_gemv_noalloc: these jobs need %zu bytes of tables, the static scratch holds %zu",
+                    need, cap);
+    return bpw_gemv(jobs, n_jobs, kernel, ws, cap, stream);
+}
+
 struct bpw_quant_plan {
     int device;
     const bpw::QuantJob *jobs;

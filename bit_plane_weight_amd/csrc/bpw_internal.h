@@ -157,6 +157,12 @@ int host_xcds();
 void host_xcd_layout(Tile *tiles, int64_t n);
 const uint8_t *host_mat_view(const ::bpw_host_mat *m, int64_t *rows, int64_t *cols, float *w_scale);
 
+// The fixed device scratch of bpw_gemv_noalloc (bpw_static.hip): kStaticScratchBytes per device, its
+// device address looked up once per device. Returns a hipError_t.
+constexpr size_t kStaticScratchBytes = size_t(1) << 20;
+constexpr int kStaticMaxDevices = 64;
+int static_scratch(void **ptr, size_t *len);
+
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
 int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
 // bit-serial: workgroup w runs tiles[w]

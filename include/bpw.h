@@ -169,6 +169,18 @@ size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs);
 bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *d_ws, size_t ws_len,
                     void *stream);
 
+/* bpw_gemv without a workspace argument, for callers that cannot allocate device memory (code under
+ * graph capture, serving loops, harnesses that forbid hipMalloc). The job and tile tables go into the
+ * library's own fixed device array of 1 MiB (one per GPU, held from the first call on that GPU until
+ * the process ends); the call allocates no device memory and calls no allocating routine of HIP or
+ * torch. The same computation, kernels and results as bpw_gemv, bit for bit. Jobs whose tables need
+ * more than 1 MiB (bpw_gemv_workspace_bytes: a decode step's 210 GEMVs need 0.25 MiB) return
+ * BPW_E_SIZE and launch nothing. Every call on one GPU rewrites that GPU's array: calls may follow
+ * one another on one stream (each waits for its table copy, which is ordered after the previous
+ * launch), but calls that overlap on one GPU (other streams, other host threads) race on the tables.
+ * Errors as bpw_gemv; n_jobs == 0 does nothing. */
+bpw_status bpw_gemv_noalloc(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, void *stream);
+
 /* A prepared grouped GEMV: the job table already sits in the caller's workspace. */
 typedef struct bpw_gemv_plan bpw_gemv_plan;
 
