@@ -450,15 +450,18 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0)
     return out
 
 
-def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50) -> list[dict]:
+SB_RUNS = "1,2,2m,3,4,4m,8,16"  # batch sizes of the grouped small-batch leg; "m" pins the matrix cores
+
+
+def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50, runs_spec: str = SB_RUNS) -> list[dict]:
     """The decode-step set (210 matrices, 521 MB of planes) at batch B: every matrix times its own B
     int8 activation vectors, all in one grouped launch, the HBM copies in rotation. Under AUTO, B = 1
     runs the batch-1 GEMV, B = 2 .. 4 the bit-serial token kernel (each beat streamed once, reduced
     against every token on the VALU) and larger B the int8 matrix cores; B = 2 and 4 are also timed on
     the matrix cores. Shows where the weight stream stops being the limit as B grows."""
     out = []
-    runs = [(1, bpw.KERNEL_AUTO), (2, bpw.KERNEL_AUTO), (2, bpw.KERNEL_MFMA), (3, bpw.KERNEL_AUTO),
-            (4, bpw.KERNEL_AUTO), (4, bpw.KERNEL_MFMA), (8, bpw.KERNEL_AUTO), (16, bpw.KERNEL_AUTO)]
+    runs = [(int(r.rstrip("m")), bpw.KERNEL_MFMA if r.endswith("m") else bpw.KERNEL_AUTO)
+            for r in runs_spec.split(",")]
     names = {bpw.KERNEL_AUTO: "auto", bpw.KERNEL_MFMA: "mfma"}
     for batch, kernel in runs:
         xs = []
@@ -577,6 +580,9 @@ def main() -> int:
     ap.add_argument("--no-extras", action="store_true", help="skip every companion measurement")
     ap.add_argument("--legs", default="all",
                     help="comma-separated companion measurements to run (default all): " + ",".join(LEGS))
+    ap.add_argument("--sb-batches", default=SB_RUNS,
+                    help="batch sizes of the small_batch_decode_step leg, comma-separated; a trailing m pins the "
+                         "matrix cores (default %(default)s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, read 1 GiB with the streaming probe and rewrite 1 GiB with the cache "
                          "flush (3 times each): kernels of known traffic for scaling hardware byte counters")
@@ -701,7 +707,8 @@ def main() -> int:
         result["intmlp"] = intmlp_measure(bpw, torch, dev, ds)
     if "small_batch_decode_step" in legs:
         log("grouped small batch over the decode-step set")
-        result["small_batch_decode_step"] = grouped_small_batch_measure(bpw, torch, synth, dev, ds)
+        result["small_batch_decode_step"] = grouped_small_batch_measure(bpw, torch, synth, dev, ds,
+                                                                        runs_spec=args.sb_batches)
     if "bitcos" in legs:
         log("BITCOS decode step")
         result["bitcos"] = bitcos_measure(bpw, torch, dev, ds)

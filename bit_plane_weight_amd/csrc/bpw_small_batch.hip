@@ -247,68 +247,209 @@ __device__ __forceinline__ u32x4 load_beat_cached(__amdgpu_buffer_rsrc_t r, uint
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Several calls in one launch. Workgroup b runs tile tiles[b]: kSBGroupRows rows x up to 16 tokens of
-// one call. Each wave owns kSBWaveTiles row tiles of 16 rows over every block of the row (no split of
-// the row across waves, so a wave streams a whole row tile with its next iteration in flight); the
-// activation pieces it loads for an iteration serve all of its row tiles. Results leave straight from
-// the matrix-core registers.
-template <int RT>
-__device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_t rt0, uint32_t tok_group,
-                                                const uint32_t *lut) {
-    const int lane = threadIdx.x & 63;
-    const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
-    const int bq = lane >> 4;
-    const int bpr = A.bpr;
-    const int n_it = (bpr + 3) / 4;
-    const int64_t ldx = A.ldx;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(A.X, A.x_bytes);
-    uint32_t row[RT];
-    bool live[RT];
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        row[r] = (rt0 + r) * kMfmaRows + (lane & 15);
-        live[r] = (int)((rt0 + r) * kMfmaRows) < A.rows;
+// The decode table of the grouped launch in kLutCopies copies: entry e of copy c is the LDS word
+// kLutCopies e + c, and lane l reads copy l % kLutCopies, so the lanes of a wave spread their lookups
+// over the banks whatever entries they ask for (with one shared copy the random entries of a wave's
+// lookups collided: 3.1 bank conflicts per lookup, measured).
+constexpr int kLutCopies = 32;
+constexpr int kLutBytes = 256 * kLutCopies * 4;
+static_assert(kLutCopies == 32 || kLutCopies == 64, "table copies: 32 or 64");
+
+__device__ __forceinline__ void fill_lut_copies(uint32_t *lut, int nthreads) {
+    u32x4 *l4 = reinterpret_cast<u32x4 *>(lut);
+    for (int i = (int)threadIdx.x; i < kLutBytes / 16; i += nthreads) {
+        const uint32_t v = lut_entry((uint32_t)i / (kLutCopies / 4));
+        l4[i] = u32x4{v, v, v, v};
     }
+}
+
+// This lane's constant part of a table address (see lut_addr).
+__device__ __forceinline__ uint32_t lut_lane_bits(int lane) {
+    return kLutCopies == 64 ? (uint32_t)lane << 2 : (uint32_t)(lane & 31) << 3;
+}
+
+// LDS byte address of the entry named by byte k of w, in this lane's copy: e * 4 kLutCopies + 4 (lane %
+// kLutCopies). One v_perm_b32 places byte k of w in byte 1 and the lane bits in byte 0 (selectors 4 + k
+// and 0; 0x0C gives zero bytes 2 and 3): e << 8 | lane << 2 for 64 copies; for 32 copies the lane bits
+// are (lane % 32) << 3 and the result is halved, e << 7 | (lane % 32) << 2. Below kLutBytes for any input.
+__device__ __forceinline__ uint32_t lut_addr(uint32_t w, int k, uint32_t lane_bits) {
+    const uint32_t a = __builtin_amdgcn_perm(w, lane_bits, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
+    return kLutCopies == 64 ? a : a >> 1;
+}
+
+__device__ __forceinline__ int lut_at(const uint32_t *lut, uint32_t addr) {
+    return (int)*reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(lut) + addr);
+}
+
+// As decode_quarter, through this lane's copy of the table.
+__device__ __forceinline__ v4i decode_quarter_own(const uint32_t *lut, uint32_t e, uint32_t o, int m, uint32_t lb) {
+    const int b = 2 * (m & 1);
+    v4i a;
+    a.x = lut_at(lut, lut_addr(e, b, lb));      // columns 16m + 0..3
+    a.y = lut_at(lut, lut_addr(o, b, lb));      // 4..7
+    a.z = lut_at(lut, lut_addr(e, b + 1, lb));  // 8..11
+    a.w = lut_at(lut, lut_addr(o, b + 1, lb));  // 12..15
+    return a;
+}
+
+__device__ __forceinline__ v4i mfma_beat_own(const uint32_t *lut, const u32x4 &beat, const u32x4 (&xv)[4], v4i acc,
+                                             uint32_t lb) {
+    const uint32_t elo = (beat.x & 0x0F0F0F0Fu) | ((beat.z << 4) & 0xF0F0F0F0u);
+    const uint32_t olo = ((beat.x >> 4) & 0x0F0F0F0Fu) | (beat.z & 0xF0F0F0F0u);
+    const uint32_t ehi = (beat.y & 0x0F0F0F0Fu) | ((beat.w << 4) & 0xF0F0F0F0u);
+    const uint32_t ohi = ((beat.y >> 4) & 0x0F0F0F0Fu) | (beat.w & 0xF0F0F0F0u);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(decode_quarter_own(lut, m < 2 ? elo : ehi, m < 2 ? olo : ohi, m, lb),
+                                                    __builtin_bit_cast(v4i, xv[m]), acc, 0, 0, 0);
+    return acc;
+}
+
+// The weight stream of a wave. The matrix cores want lane l = 16 g + m to hold the beat of row m of a
+// 16-row tile at block 4 i + g in iteration i, so a load in that layout covers 16 rows x 64 bytes:
+// half cache lines, which a plain streaming read of the same rows showed at 4.1-4.9 TB/s (measured,
+// loads only) against 6.9 for whole lines. A step therefore covers 8 blocks (two iterations) of a
+// tile with two loads per lane whose address sets are rows 0-7 and rows 8-15, each 8 rows x 128 bytes
+// (whole lines, non-temporal: 6.5-6.7 TB/s measured, loads only):
+//   load j (j = 0, 1), lane 16 g + m: row 8 j + m % 8, block g + 4 [m / 8 != j]
+// so that, with lo = (m < 8), the beats of the two iterations are
+//   iteration 2s:     lo ? R0 : R1                          (row m, block g)
+//   iteration 2s + 1: the value of (lo ? R1 : R0) in lane l ^ 8 (row m, block 4 + g)
+// one select per word, and one DPP rotate by 8 within each row of 16 lanes.
+__device__ __forceinline__ uint32_t swap8(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); }
+
+__device__ __forceinline__ void split_step(const u32x4 &r0, const u32x4 &r1, bool lo, u32x4 &p0, u32x4 &p1) {
+    p0 = lo ? r0 : r1;
+    const u32x4 t = lo ? r1 : r0;
+    p1 = u32x4{swap8(t.x), swap8(t.y), swap8(t.z), swap8(t.w)};
+}
+
+// The activation operands (see sb_act_operands_kernel) of up to kXtPassSteps steps sit in LDS: the
+// matrix-core operand of quarter q of iteration i is the KiB at (4 i + q) KiB, lane l's 16 bytes at 16 l,
+// read with one conflict-free ds_read_b128. Loading them from memory instead, each step's eight operand
+// loads went through the same address path as the weights: the texture address unit stayed 67-76 %
+// busy (counters) while the weights moved at less than half the batch-1 rate.
+constexpr int kXtPassSteps = 6;  // 48 KiB: table + one pass = 80 KiB, two workgroups per compute unit
+constexpr int kXtStepBytes = 8192;  // 2 iterations x 4 quarters x 64 lanes x 16 bytes
+constexpr int kXtPassBytes = kXtPassSteps * kXtStepBytes;
+
+// LDS bytes of the grouped launch: the table, then one pass of operands.
+constexpr size_t kSbGroupedLds = (size_t)kLutBytes + (size_t)kXtPassBytes;
+static_assert(2 * kSbGroupedLds <= 160 * 1024, "two workgroups per compute unit");
+
+// Copy one pass of operands (kXtPassBytes) from global memory into LDS, all threads of the workgroup,
+// every load issued before the first store, with no branch: bytes past `valid` read zeros through the
+// buffer range check and are written like the rest. (With per-lane guards on the stores, a skipped
+// store left its load unwaited and the compiler answered with a wait for every load in flight at the
+// top of the streaming loop, seen in the ISA.)
+template <int NT>
+__device__ __forceinline__ void stage_operands(uint8_t *xl, const uint8_t *src, uint32_t valid) {
+    static_assert(kXtPassBytes % (NT * 16) == 0, "whole rounds of 16 bytes per thread");
+    constexpr int kPer = kXtPassBytes / (NT * 16);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, valid);
+    u32x4 v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+        v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)k * NT + threadIdx.x) * 16u, 0, 0));
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) *reinterpret_cast<u32x4 *>(xl + ((uint32_t)k * NT + threadIdx.x) * 16u) = v[k];
+}
+
+// Several calls in one launch. Workgroup b runs tile tiles[b]: kSBGroupRows rows x up to 16 tokens of
+// one call. Each wave owns RT row tiles of 16 rows over every block of the row (no split of the row
+// across waves); results leave straight from the matrix-core registers. The workgroup first stages
+// the table and the call's activation operands in LDS; rows wider than kXtPassSteps steps take several
+// passes, the operands of each staged in turn (every wave, with rows or not, takes part in the staging).
+// Within a pass the beats of the next ST - 1 steps are in flight while a step is decoded and multiplied
+// (ST register sets, the step loop unrolled ST times so each set is fixed; a wave with few waves per
+// compute unit needs several steps of weights in flight to cover the memory latency under load); the
+// first ST - 1 steps' beats leave before the pass's operands are staged. Beats past the row, past the
+// pass or past the matrix read zeros through the buffer range checks.
+template <int RT, int NT, int ST>
+__device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_t rt0, uint32_t tok_group,
+                                                uint32_t *lut, uint8_t *xl, bool active) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t lb = lut_lane_bits(lane);
+    const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
+    const int g = lane >> 4, m = lane & 15;
+    const bool lo = m < 8;
+    const int bpr = A.bpr;
+    const int n_steps = (bpr + 7) / 8;
+    const uint8_t *xt = A.xt + (size_t)tok_group * A.xt_group_bytes;
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
+    uint32_t row[RT][2];
+    bool live[RT][2];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            row[t][j] = (rt0 + t) * kMfmaRows + 8 * j + (m & 7);
+            live[t][j] = active && (int)row[t][j] < A.rows;
+        }
+    const int bj0 = g + (lo ? 0 : 4), bj1 = g + (lo ? 4 : 0);  // block of load 0 / 1 within a step
     v4i acc[RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) acc[r] = v4i{0, 0, 0, 0};
-    u32x4 b0[RT], b1[RT], x0[4], x1[4];
-    auto issue = [&](u32x4 (&beat)[RT], u32x4 (&xv)[4], int it) {
-        const int b = 4 * it + bq;
-        const bool in = it < n_it && b < bpr;
+    for (int t = 0; t < RT; ++t) acc[t] = v4i{0, 0, 0, 0};
+    u32x4 bb[ST][RT][2];
+    int s_end = 0;  // the current pass's end
+    auto issue = [&](u32x4 (&beat)[RT][2], int st) {
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
-            beat[r] = load_beat_cached(wr, (in && live[r]) ? (row[r] * (uint32_t)bpr + (uint32_t)b) * 16u : kOutOfRange);
-        const uint32_t xo = (uint32_t)((int64_t)tok * ldx + (int64_t)b * 64);
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-            xv[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? xo + 16u * m : kOutOfRange, 0, 0));
+            for (int j = 0; j < 2; ++j) {
+                const int b = 8 * st + (j ? bj1 : bj0);
+                const bool in = st < s_end && b < bpr && live[t][j];
+                beat[t][j] = load_beat(wr, in ? (row[t][j] * (uint32_t)bpr + (uint32_t)b) * 16u : kOutOfRange);
+            }
     };
-    int it = 0;
-    issue(b0, x0, it);
-    for (; it < n_it; it += 2) {
-        issue(b1, x1, it + 1);
-        asm volatile("" ::: "memory");
+    auto step = [&](const u32x4 (&beat)[RT][2], int ls) {  // ls: the step's index within the pass
+        const uint8_t *xs = xl + (uint32_t)ls * kXtStepBytes + (uint32_t)lane * 16u;
+        u32x4 xa[4], xb[4];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r] = mfma_beat(lut, b0[r], x0, acc[r]);
-        issue(b0, x0, it + 2);
-        asm volatile("" ::: "memory");
+        for (int q = 0; q < 4; ++q) {
+            xa[q] = *reinterpret_cast<const u32x4 *>(xs + q * 1024);
+            xb[q] = *reinterpret_cast<const u32x4 *>(xs + 4096 + q * 1024);
+        }
 #pragma unroll
-        for (int r = 0; r < RT; ++r) acc[r] = mfma_beat(lut, b1[r], x1, acc[r]);
+        for (int t = 0; t < RT; ++t) {
+            u32x4 p0, p1;
+            split_step(beat[t][0], beat[t][1], lo, p0, p1);
+            acc[t] = mfma_beat_own(lut, p0, xa, acc[t], lb);
+            acc[t] = mfma_beat_own(lut, p1, xb, acc[t], lb);
+        }
+    };
+    for (int s0 = 0; s0 < n_steps || s0 == 0; s0 += kXtPassSteps) {
+        s_end = min(n_steps, s0 + kXtPassSteps);
+#pragma unroll
+        for (int k = 0; k + 1 < ST; ++k) issue(bb[k], s0 + k);
+        __syncthreads();  // the previous pass's operands are no longer read
+        const uint32_t src = (uint32_t)s0 * kXtStepBytes;
+        const uint32_t avail = A.xt_group_bytes > src ? A.xt_group_bytes - src : 0u;
+        stage_operands<NT>(xl, xt + src, avail < (uint32_t)kXtPassBytes ? avail : (uint32_t)kXtPassBytes);
+        __syncthreads();  // operands (and on the first pass the table) complete
+        for (int st = s0; st < s_end; st += ST) {
+#pragma unroll
+            for (int k = 0; k < ST; ++k) {
+                if (st + k >= s_end) break;  // wave-uniform: the pass has no step st + k
+                issue(bb[(k + ST - 1) % ST], st + k + ST - 1);
+                asm volatile("" ::: "memory");
+                step(bb[k], st + k - s0);
+            }
+        }
+        if (n_steps == 0) break;
     }
-    // lane l, register i of row tile r: row 16 (rt0 + r) + 4 (l / 16) + i, token l % 16
+    // lane l, register i of row tile t: row 16 (rt0 + t) + 4 (l / 16) + i, token l % 16
     const int otok = (int)tok;
-    if (otok >= A.batch) return;
+    if (!active || otok >= A.batch) return;
     const float xs = A.x_scales[otok];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
+    for (int t = 0; t < RT; ++t) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int orow = (int)(rt0 + r) * kMfmaRows + 4 * (lane >> 4) + i;
+            const int orow = (int)(rt0 + t) * kMfmaRows + 4 * (lane >> 4) + i;
             if (orow < A.rows) {
                 const int64_t idx = (int64_t)otok * A.rows + orow;
-                const int32_t sum = acc[r][i];
+                const int32_t sum = acc[t][i];
                 A.out_i32[idx] = sum;
                 if (A.out_f32) A.out_f32[idx] = ((float)sum * xs) * A.w_scale;  // the scales in turn
             }
@@ -316,15 +457,36 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
     }
 }
 
-__global__ __launch_bounds__(256) void gemm_small_batch_mfma_grouped_kernel(const SmallBatchArgs *__restrict__ jobs,
-                                                                            const SBTile *__restrict__ tiles) {
-    __shared__ uint32_t lut[256];
-    fill_lut(lut);
-    __syncthreads();  // the table is complete
+__global__ __launch_bounds__(64 * kSBGroupWaves) void gemm_small_batch_mfma_grouped_kernel(
+    const SmallBatchArgs *__restrict__ jobs, const SBTile *__restrict__ tiles) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    uint32_t *lut = reinterpret_cast<uint32_t *>(smem);
+    fill_lut_copies(lut, 64 * kSBGroupWaves);  // made visible by the first staging barrier
     const SBTile t = tiles[blockIdx.x];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    mfma_wave_tiles<kSBWaveTiles>(jobs[t.job], (uint32_t)(t.row_tile * 4 * kSBWaveTiles + wave * kSBWaveTiles),
-                                  (uint32_t)t.tok_group, lut);
+    const SmallBatchArgs &A = jobs[t.job];
+    const uint32_t rt0 = (uint32_t)(t.row_tile * kSBGroupWaves * kSBWaveTiles + wave * kSBWaveTiles);
+    const bool active = (int64_t)rt0 * kMfmaRows < A.rows;  // wave-uniform; idle waves still stage
+    mfma_wave_tiles<kSBWaveTiles, 64 * kSBGroupWaves, kSBStages>(A, rt0, (uint32_t)t.tok_group, lut, smem + kLutBytes,
+                                                                 active);
+}
+
+// The activation operands of the grouped launch, in the order its matrix cores read them: piece (i, q, l)
+// of token group tg is the 16 bytes lane l = 16 g + n feeds as quarter q of iteration i: codes 16 q ..
+// 16 q + 15 of block 4 i + g of token 16 tg + n (zero past the batch or past the row). Each workgroup
+// writes one iteration (4 KiB); the main kernel copies them into LDS contiguously. Gathered from X by
+// the main kernel's own loads (64 scattered 16-byte pieces per instruction), the operand loads alone took
+// 137 us at 2 tokens and 261 us at 16 on the decode-step set (measured with the weight work removed),
+// against 78 us for the weight stream.
+__global__ __launch_bounds__(256) void sb_act_operands_kernel(const SmallBatchArgs *__restrict__ jobs,
+                                                              const XTile *__restrict__ xtiles) {
+    const XTile x = xtiles[blockIdx.x];
+    const SmallBatchArgs &A = jobs[x.job];
+    const int t = threadIdx.x, q = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
+    const int tok = 16 * x.tg + n, b = 4 * x.it + g;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (tok < A.batch && b < A.bpr) v = *reinterpret_cast<const u32x4 *>(A.X + (int64_t)tok * A.ldx + 64 * b + 16 * q);
+    *reinterpret_cast<u32x4 *>(A.xt + (size_t)x.tg * A.xt_group_bytes + ((size_t)(4 * x.it + q) * 64 + l) * 16) = v;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -341,10 +503,20 @@ int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream) {
     return hipGetLastError();
 }
 
-int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream) {
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles,
+                                    const XTile *xtiles, int32_t n_xtiles, void *stream) {
     if (n_tiles <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_small_batch_mfma_grouped_kernel, dim3((unsigned)n_tiles), dim3(256), 0, as_stream(stream),
-                       jobs, tiles);
+    const size_t lds = kSbGroupedLds;
+    const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_small_batch_mfma_grouped_kernel),
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (ea != hipSuccess) return ea;
+    if (n_xtiles > 0) {
+        hipLaunchKernelGGL(sb_act_operands_kernel, dim3((unsigned)n_xtiles), dim3(256), 0, as_stream(stream), jobs, xtiles);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(gemm_small_batch_mfma_grouped_kernel, dim3((unsigned)n_tiles), dim3(64 * kSBGroupWaves), lds,
+                       as_stream(stream), jobs, tiles);
     return hipGetLastError();
 }
 

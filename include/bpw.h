@@ -305,7 +305,10 @@ typedef struct bpw_sb_plan bpw_sb_plan;
 size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch);
 
 /* Check the jobs, write the job and tile tables into d_ws (256-byte aligned; the call waits for the
- * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues one launch for all of them.
+ * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues the work for all of them: one
+ * launch, or on the matrix cores two (the first writes every job's activations into the workspace in
+ * the order the matrix cores read them, 4 KiB per 4 blocks and 16 tokens, so the workspace also holds
+ * those operands: bpw_gemm_small_batch_workspace_bytes counts them; runs of one plan must not overlap).
  * Kernels: BPW_KERNEL_MFMA, the int8 matrix cores (any batch, any shape); BPW_KERNEL_BITSERIAL, at
  * batch 1 the bit-serial batch-1 grouped GEMV and at batch 2 to 4 the bit-serial token kernel (every
  * beat streamed once and reduced against each token's bit planes), which serves matrices of 2497 to

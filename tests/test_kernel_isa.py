@@ -67,3 +67,36 @@ def test_token_kernel_loops_wait_only_for_the_older_loads(tmp_path):
         for name, body in loops.items():
             waits = [int(m.group(1)) for x in body if (m := re.search(r"vmcnt\((\d+)\)", x))]
             assert waits and min(waits) > 0, f"loop {name}: vmcnt waits {waits}"
+
+
+def basic_blocks(asm: str) -> dict:
+    blk, blocks = None, {}
+    for line in asm.split("\n"):
+        m = re.match(r"^(\.LBB\d+_\d+|; %bb\.\d+):", line)
+        if m:
+            blk = m.group(1)
+            blocks[blk] = []
+            continue
+        if blk and line.startswith("\t") and not line.strip().startswith(";"):
+            blocks[blk].append(line.strip())
+    return blocks
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
+def test_grouped_small_batch_stream_waits_only_for_the_older_loads(tmp_path):
+    """The grouped matrix-core small batch: every basic block that holds matrix-core instructions (the
+    streaming loop; the compiler folds it into the pass loop, whose staging legitimately waits for all
+    loads) waits for part of the loads in flight only, never vmcnt(0). A per-lane guard on the operand
+    staging once left a load unwaited, and the compiler put a vmcnt(0) at the top of this loop."""
+    out = tmp_path / "sb.s"
+    src = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_small_batch.hip")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
+                    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
+                    src, "-o", str(out)], check=True, capture_output=True)
+    kernel = re.split(r"\n(?=_ZN3bpw36gemm_small_batch_mfma_grouped_kernel)", out.read_text())[1]
+    kernel = kernel.split("s_endpgm")[0]
+    blocks = {n: b for n, b in basic_blocks(kernel).items() if any("v_mfma" in x for x in b)}
+    assert sum(sum("buffer_load_dwordx4" in x for x in b) for b in blocks.values()) >= 4, "no streaming loop found"
+    for name, body in blocks.items():
+        waits = [int(m.group(1)) for x in body if (m := re.search(r"vmcnt\((\d+)\)", x))]
+        assert all(w > 0 for w in waits), f"block {name}: vmcnt waits {waits}"
