@@ -74,8 +74,11 @@ inline uint64_t tail_mask(int64_t cols) {
 }
 
 bool shape_ok(int64_t rows, int64_t cols) {
-    // rows * bpr * 16 must fit in size_t and the kernels address one matrix with 32-bit offsets.
-    return rows >= 0 && cols >= 0 && rows <= (int64_t)INT32_MAX && cols <= ((int64_t)1 << 40);
+    // The kernels index one matrix's rows as int32, and rows * bpr * 16 (the plane bytes, compared with
+    // the caller's length) must not wrap: a wrapped count could match a short buffer.
+    if (rows < 0 || cols < 0 || rows > (int64_t)INT32_MAX || cols > ((int64_t)1 << 40)) return false;
+    const int64_t bpr = (cols + 63) / 64;
+    return bpr == 0 || rows <= (INT64_MAX / 16) / bpr;
 }
 
 // ---------------------------------------------------------------- descriptor seal

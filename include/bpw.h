@@ -125,6 +125,9 @@ bpw_status bpw_device_check(void);
 
 /* ------------------------------------------------------------------------ host: pack / validate / load */
 
+/* Shapes that pack, validate and load accept: 0 <= rows <= INT32_MAX, 0 <= cols <= 2^40 and
+ * rows * bpr * 16 < 2^63 (bpr = ceil(cols / 64)); any other shape is BPW_E_INVAL. */
+
 /* Pack row-major int8 trits w [rows x cols] into .trit v1 planes (format page 2.3).
  * planes_len must equal rows * bpr * 16; padding bits are written clear (P2). A value outside
  * {-1, 0, +1} returns BPW_E_INVAL with its row, beat and column in *err (err may be NULL). */

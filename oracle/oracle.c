@@ -66,10 +66,16 @@ static int set_err(or_err *e, int code, int64_t row, int64_t beat, int64_t col) 
 }
 
 /* [TF] 2.3: beats_per_row = ceil(cols / 64). */
-int64_t oracle_beats_per_row(int64_t cols) { return (cols + 63) / 64; }
+int64_t oracle_beats_per_row(int64_t cols) { return cols / 64 + (cols % 64 != 0); }
 
-/* [TF] 2.3: byte_len = rows * beats_per_row * 16. */
-int64_t oracle_byte_len(int64_t rows, int64_t cols) { return rows * oracle_beats_per_row(cols) * 16; }
+/* [TF] 2.3: byte_len = rows * beats_per_row * 16; -1 for a negative shape or one whose byte count
+ * does not fit in int64 (no buffer has that length). */
+int64_t oracle_byte_len(int64_t rows, int64_t cols) {
+    if (rows < 0 || cols < 0) return -1;
+    int64_t bpr = oracle_beats_per_row(cols);
+    if (bpr && rows > INT64_MAX / 16 / bpr) return -1;
+    return rows * bpr * 16;
+}
 
 /* [TF] 2.3 / [TP] "Invariants" (P2): the valid-column mask of a row's last beat, built in 64 bits. */
 uint64_t oracle_tail_mask(int64_t cols) {
@@ -103,7 +109,7 @@ static int lowest_bit(uint64_t v) {
 int oracle_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, int64_t len, or_err *e) {
     if (rows < 0 || cols < 0) return set_err(e, OR_E_INVAL, -1, -1, -1);
     int64_t bpr = oracle_beats_per_row(cols);
-    if (len != rows * bpr * 16) return set_err(e, OR_E_SIZE, -1, -1, -1);
+    if (len != oracle_byte_len(rows, cols)) return set_err(e, OR_E_SIZE, -1, -1, -1);
     /* Rows are independent; each records its first bad column, and the first bad row wins. */
     int64_t first_bad_row = rows, first_bad_col = -1;
 #pragma omp parallel for schedule(static)
@@ -149,7 +155,7 @@ int oracle_pack(const int8_t *w, int64_t rows, int64_t cols, uint8_t *planes, in
 int oracle_validate(const uint8_t *planes, int64_t len, int64_t rows, int64_t cols, or_err *e) {
     if (rows < 0 || cols < 0) return set_err(e, OR_E_INVAL, -1, -1, -1);
     int64_t bpr = oracle_beats_per_row(cols);
-    if (len != rows * bpr * 16) return set_err(e, OR_E_SIZE, -1, -1, -1);
+    if (len != oracle_byte_len(rows, cols)) return set_err(e, OR_E_SIZE, -1, -1, -1);
     uint64_t tail = oracle_tail_mask(cols);
     for (int64_t r = 0; r < rows; ++r) {
         for (int64_t b = 0; b < bpr; ++b) {

@@ -564,3 +564,14 @@ def test_intmlp_range_error_past_int64():
     with pytest.raises(oracle.OracleError) as ei:
         oracle.intmlp(np_pack(wg), np_pack(wu), 1, cols, x, 1.0, 1.0, 1.0)
     assert ei.value.code == oracle.E_RANGE
+
+
+def test_byte_len_refuses_shapes_whose_count_does_not_fit():
+    """(2^60 + 1) beats of 16 bytes is 16 modulo 2^64: a wrapped count would match a 16-byte buffer."""
+    rows, cols = 17 * 241 * 61681, 4562284561 * 64
+    assert rows * (cols // 64) == 2**60 + 1
+    assert oracle.byte_len(rows, cols) == -1 and oracle.byte_len(-1, 64) == -1
+    assert oracle.byte_len(2**31 - 1, 64) == (2**31 - 1) * 16
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.validate(np.zeros(16, np.uint8), rows, cols)
+    assert e.value.code == oracle.E_SIZE

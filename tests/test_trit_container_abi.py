@@ -1,7 +1,6 @@
 """libbpw's .trit v1 container reader (bpw_trit_*) against the oracle's reader, on the host (no GPU):
 the same fields on valid files, the same check number (and tensor, and P1/P2 position) on every
 crafted change, every truncation and a few thousand random header mutations."""
-import random
 import struct
 
 import numpy as np
@@ -9,7 +8,7 @@ import pytest
 
 import oracle
 from oracle import trit_container as tc
-from test_trit_container_pins import CHECK_CASES, PAGE, patched
+from test_trit_container_pins import CHECK_CASES, PAGE, header_mutations, patched, payload_bit_flips, sample_file
 
 bpw = pytest.importorskip("bit_plane_weight_amd")
 from bit_plane_weight_amd import _lib  # noqa: E402
@@ -36,18 +35,6 @@ def oracle_check(data: bytes, verify: bool = False, check_hash: bool = True):
     except tc.TritError as e:
         return (e.check, e.tensor, e.row, e.beat, e.col)
     return (0, -1, -1, -1, -1)
-
-
-def sample_file(seed: int = 1, n: int = 6, hashed: bool = True) -> bytes:
-    rng = np.random.default_rng(seed)
-    tensors = []
-    for i in range(n):
-        rows, cols = int(rng.integers(1, 6)), int(rng.integers(1, 150))
-        w = rng.integers(-1, 2, size=(rows, cols)).astype(np.int8)
-        tensors.append((f"layer.{i}.w", tc.TRIT, [rows, cols], 0.25 * (i + 1), oracle.pack(w).tobytes()))
-    tensors.append(("norm", tc.F32, [7], 1.0, np.arange(7, dtype=np.float32).tobytes()))
-    tensors.append(("head", tc.BF16, [3, 4], 1.0, bytes(24)))
-    return tc.write('{"model": "tést"}'.encode(), tensors, with_hash=hashed)
 
 
 def test_fields_agree_with_oracle():
@@ -79,18 +66,8 @@ def test_random_header_mutations_agree():
     """Random byte changes in the header region (one to three bytes), and random truncations, of a
     multi-tensor file: the library and the oracle accept the same files and report the same check,
     tensor and P1/P2 position; never a crash."""
-    base = sample_file(4)
-    start = tc.TritFile(base).payload_start
-    rnd = random.Random(11)
     seen = set()
-    for k in range(3000):
-        data = bytearray(base)
-        for _ in range(rnd.randint(1, 3)):
-            p = rnd.randrange(start)
-            data[p] = rnd.choice((0, 1, 0xFF, 0x80, 0x40, rnd.randrange(256)))
-        if k % 5 == 0:
-            data = data[: rnd.randrange(len(data))]
-        data = bytes(data)
+    for k, data in enumerate(header_mutations(sample_file(4))):
         a, b = lib_check(data, verify=True), oracle_check(data, verify=True)
         assert a == b, (k, a, b)
         seen.add(a[0])
@@ -98,16 +75,7 @@ def test_random_header_mutations_agree():
 
 
 def test_verify_positions_agree():
-    base = sample_file(5, hashed=False)
-    g = tc.TritFile(base)
-    rnd = random.Random(3)
-    for k in range(300):
-        i = rnd.choice([j for j, t in enumerate(g.tensors) if t.dtype == tc.TRIT])
-        t = g.tensors[i]
-        o = g.payload_start + t.offset + rnd.randrange(t.byte_len)
-        data = bytearray(base)
-        data[o] |= 1 << rnd.randrange(8)
-        data = bytes(data)
+    for k, data in enumerate(payload_bit_flips(sample_file(5, hashed=False))):
         assert lib_check(data, verify=True) == oracle_check(data, verify=True), k
 
 

@@ -4,6 +4,7 @@ one crafted change, with the page's number), the truncation suite of section 4, 
 FNV-1a-64 test vectors. No GPU and no libbpw here."""
 import math
 import os
+import random
 import struct
 
 import numpy as np
@@ -32,6 +33,46 @@ PAGE = read_complete_file()
 
 def patched(data: bytes, off: int, new: bytes) -> bytes:
     return data[:off] + new + data[off + len(new):]
+
+
+def sample_file(seed: int = 1, n: int = 6, hashed: bool = True) -> bytes:
+    rng = np.random.default_rng(seed)
+    tensors = []
+    for i in range(n):
+        rows, cols = int(rng.integers(1, 6)), int(rng.integers(1, 150))
+        w = rng.integers(-1, 2, size=(rows, cols)).astype(np.int8)
+        tensors.append((f"layer.{i}.w", tc.TRIT, [rows, cols], 0.25 * (i + 1), oracle.pack(w).tobytes()))
+    tensors.append(("norm", tc.F32, [7], 1.0, np.arange(7, dtype=np.float32).tobytes()))
+    tensors.append(("head", tc.BF16, [3, 4], 1.0, bytes(24)))
+    return tc.write('{"model": "tést"}'.encode(), tensors, with_hash=hashed)
+
+
+def header_mutations(base: bytes, count: int = 3000, seed: int = 11):
+    """Random changes of one to three header bytes (to 0, 1, 0xFF, 0x80, 0x40 or a random value) of a
+    valid file, every fifth one also truncated at a random length."""
+    start = tc.TritFile(base).payload_start
+    rnd = random.Random(seed)
+    for k in range(count):
+        data = bytearray(base)
+        for _ in range(rnd.randint(1, 3)):
+            p = rnd.randrange(start)
+            data[p] = rnd.choice((0, 1, 0xFF, 0x80, 0x40, rnd.randrange(256)))
+        if k % 5 == 0:
+            data = data[: rnd.randrange(len(data))]
+        yield bytes(data)
+
+
+def payload_bit_flips(base: bytes, count: int = 300, seed: int = 3):
+    """One set bit in the planes of a random ternary tensor of a valid file, per case."""
+    g = tc.TritFile(base)
+    rnd = random.Random(seed)
+    for _ in range(count):
+        i = rnd.choice([j for j, t in enumerate(g.tensors) if t.dtype == tc.TRIT])
+        t = g.tensors[i]
+        o = g.payload_start + t.offset + rnd.randrange(t.byte_len)
+        data = bytearray(base)
+        data[o] |= 1 << rnd.randrange(8)
+        yield bytes(data)
 
 
 def check_of(data: bytes, verify: bool = False, check_hash: bool = True) -> int:
