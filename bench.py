@@ -507,52 +507,89 @@ def z_sweep_measure(bpw, torch, synth, dev, reps: int = 30) -> list[dict]:
     return out
 
 
-def cpu_baseline(sample, nthreads: int, min_seconds: float = 10.0) -> dict:
-    """The CPU oracle, as it is, on the host cores: whole passes over the sample (one layer's seven
-    projections) until at least min_seconds of oracle time; rate in plane GB/s."""
-    import oracle
-    packed = [(oracle.pack(c.w), c) for c in sample]
-    seconds, nbytes, passes = 0.0, 0, 0
-    while seconds < min_seconds:
-        for planes, c in packed:
-            t = time.perf_counter()
-            oracle.gemv(planes, c.rows, c.cols, c.x, c.x_scale, c.w_scale, nthreads=nthreads)
-            seconds += time.perf_counter() - t
-            nbytes += planes.size
-        passes += 1
-    return {
-        "value": round(nbytes / seconds / 1e9, 4),
-        "unit": "GB/s",
-        "cores": nthreads,
-        "kind": "oracle",
-        "sample": f"layer 0 of the decode-step set (its 7 projections, {nbytes // passes} plane bytes) x {passes} "
-                  f"passes, one oracle GEMV per matrix on {nthreads} host threads, {seconds:.1f} s",
-    }
+CPU_LAYERS = 4  # decode-step layers in the CPU oracle's sample of the full step
+CPU_HEAD_ROWS = 8192  # rows of the dense head in its CPU sample
 
 
-def cpu_single_thread(sample, min_seconds: float = 3.0) -> dict:
-    """The same oracle passes on one host thread (a shorter bounded sample), and the host it ran on."""
-    import oracle
-    packed = [(oracle.pack(c.w), c) for c in sample]
-    seconds, nbytes = 0.0, 0
-    while seconds < min_seconds:
-        for planes, c in packed:
-            t = time.perf_counter()
-            oracle.gemv(planes, c.rows, c.cols, c.x, c.x_scale, c.w_scale, nthreads=1)
-            seconds += time.perf_counter() - t
-            nbytes += planes.size
-    model = "unknown"
+def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    model = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"single_thread_gbs": round(nbytes / seconds / 1e9, 4),
-            "host": f"{model}, {len(os.sched_getaffinity(0))} CPUs available to this process",
-            "seconds": round(seconds, 1)}
+    return "unknown"
+
+
+def _median_rate(run, nbytes: int, min_seconds: float, runs: int = 3) -> tuple[float, list[float], float]:
+    """`runs` timed runs, each repeating run() (nbytes per call) until min_seconds have passed.
+    Returns (median GB/s, the per-run GB/s, total seconds)."""
+    rates, total = [], 0.0
+    for _ in range(runs):
+        seconds, done = 0.0, 0
+        while seconds < min_seconds:
+            t = time.perf_counter()
+            run()
+            seconds += time.perf_counter() - t
+            done += nbytes
+        rates.append(done / seconds / 1e9)
+        total += seconds
+    return statistics.median(rates), rates, total
+
+
+def cpu_baseline(cases, nthreads: int) -> dict:
+    """The CPU oracle, as it is, on the host cores: the one-matrix case (the k projection of layer 0,
+    640 x 2560), one layer (layer 0's seven projections), a sample of the decode step (its first
+    CPU_LAYERS layers) and the bf16 head (its first CPU_HEAD_ROWS rows). Each is the median of three
+    runs, in plane (or weight) GB/s; `value` is the decode-step sample's rate."""
+    import numpy as np
+    import oracle
+    import synth
+
+    packed = [(layer, oracle.pack(c.w), c) for layer, c in cases]
+
+    def gemvs(items, threads):
+        def run():
+            for _, planes, c in items:
+                oracle.gemv(planes, c.rows, c.cols, c.x, c.x_scale, c.w_scale, nthreads=threads)
+        return run, sum(p.size for _, p, _ in items)
+
+    layer0 = [t for t in packed if t[0] == 0]
+    kproj = [t for t in layer0 if (t[2].rows, t[2].cols) == (640, 2560)][:1]
+    out, seconds = {}, 0.0
+    for name, items, min_s in (("k_proj_640x2560", kproj, 0.5), ("one_layer", layer0, 1.0),
+                               (f"decode_step_first_{CPU_LAYERS}_layers", packed, 1.0)):
+        run, nbytes = gemvs(items, nthreads)
+        med, rates, sec = _median_rate(run, nbytes, min_s)
+        seconds += sec
+        out[name] = {"gbs": round(med, 4), "runs_gbs": [round(r, 4) for r in rates], "plane_bytes": nbytes,
+                     "matrices": len(items)}
+    w, x = synth.head_case(BASE_SEED + 5, rows=CPU_HEAD_ROWS)
+    med, rates, sec = _median_rate(lambda: oracle.dense_head(w, x, nthreads=nthreads), w.nbytes, 1.0)
+    seconds += sec
+    out["dense_head_bf16"] = {"gbs": round(med, 4), "runs_gbs": [round(r, 4) for r in rates],
+                              "weight_bytes": int(w.nbytes), "rows": CPU_HEAD_ROWS, "cols": int(w.shape[1])}
+    run, nbytes = gemvs(layer0, 1)
+    single, _, sec = _median_rate(run, nbytes, 1.0, runs=1)
+    seconds += sec
+    step = out[f"decode_step_first_{CPU_LAYERS}_layers"]
+    return {
+        "value": step["gbs"],
+        "unit": "GB/s",
+        "cores": nthreads,
+        "kind": "oracle",
+        "sample": f"the first {CPU_LAYERS} layers of the decode-step set ({step['matrices']} matrices, "
+                  f"{step['plane_bytes']} plane bytes), one oracle GEMV per matrix on {nthreads} host threads, "
+                  f"median of three runs; also the one-matrix and one-layer cases and the head's first "
+                  f"{CPU_HEAD_ROWS} rows, {seconds:.1f} s of oracle time in all",
+        "median_of": 3,
+        "configs": out,
+        "single_thread_one_layer_gbs": round(single, 4),
+        "cpu_model": cpu_model(),
+        "nproc": os.cpu_count(),
+        "cpus_available": len(os.sched_getaffinity(0)),
+    }
 
 
 def traffic_from_profile() -> float | None:
@@ -611,8 +648,8 @@ def main() -> int:
     oracle_fn = None
     if not args.no_cpu_baseline:
         def oracle_fn(case, layer):
-            if layer == 0:
-                sample.append(case)
+            if layer < CPU_LAYERS:
+                sample.append((layer, case))
 
     log("generating, packing and uploading the decode-step set")
     t0 = time.perf_counter()
@@ -676,8 +713,8 @@ def main() -> int:
         },
     }
     if sample:
+        log("CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(sample, nthreads)
-        result["cpu_oracle_single_thread"] = cpu_single_thread(sample)
 
     if args.copy_calibration:
         log("copy calibration: probe reads 1 GiB, flush reads and writes 1 GiB, 3 times each")
