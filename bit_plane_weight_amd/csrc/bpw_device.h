@@ -196,6 +196,53 @@ __device__ __forceinline__ void stage_planes(u32x4 *xl, const int8_t *x, int b0,
     }
 }
 
+// ------------------------------------------------------------------------------------------
+// Byte-lane select ("The .trit format, version 1", section 1: the masks pick the activation bytes that
+// are added and subtracted). Each 4-bit group of a mask is widened to four byte lanes
+// (n * 0x00204081 puts bit i at bit 7i; & 0x01010101 keeps bits 0, 8, 16 and 24) and a signed 4-way
+// int8 dot product (v_dot4_i32_i8) adds the selected bytes of x.
+
+__device__ __forceinline__ int32_t spread4(uint32_t m, int i) {
+    return (int32_t)((((m >> (4 * i)) & 0xFu) * 0x00204081u) & 0x01010101u);
+}
+
+// Blocks [b0, b0 + nb) of x as they are (16 words of four int8 codes per block, word w = columns
+// 4w .. 4w+3), in the LDS slots the bit planes use (xq_slot), one 16-byte piece per lane; the same
+// zero-filled last round as stage_planes.
+__device__ __forceinline__ void stage_bytes(u32x4 *xl, const int8_t *x, int b0, int nb, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(x + (int64_t)b0 * 64, (uint32_t)nb * 64u);
+    const int need = (nb * 4 + 63) / 64;
+    for (int wv = wave; wv < need; wv += kWaves) {
+        const int p = wv * 64 + lane;
+        xl[xq_slot(p >> 2, p & 3)] =
+            __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)p * 16u, 0, 0));
+    }
+}
+
+// Exact partial sum of one row over the K beats a lane holds, activation bytes from LDS: the +1 lanes'
+// dot product minus the -1 lanes'. Same read-ahead and scheduling barrier as row_partial.
+template <int K, int GLOG>
+__device__ __forceinline__ int32_t row_partial_bytelane(const u32x4 *xl, const u32x4 (&B)[K], int g, int G) {
+    int32_t ap = 0, an = 0;
+    uint32_t Xa[16], Xb[16];
+    read_planes<GLOG>(Xa, xl, 0, g, G);
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+        uint32_t(&X)[16] = (k & 1) ? Xb : Xa;
+        uint32_t(&Xn)[16] = (k & 1) ? Xa : Xb;
+        if (k + 1 < K) read_planes<GLOG>(Xn, xl, k + 1, g, G);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            ap = __builtin_amdgcn_sdot4(spread4(B[k].x, i), (int32_t)X[i], ap, false);
+            an = __builtin_amdgcn_sdot4(spread4(B[k].z, i), (int32_t)X[i], an, false);
+            ap = __builtin_amdgcn_sdot4(spread4(B[k].y, i), (int32_t)X[8 + i], ap, false);
+            an = __builtin_amdgcn_sdot4(spread4(B[k].w, i), (int32_t)X[8 + i], an, false);
+        }
+        asm volatile("" : "+v"(ap), "+v"(an)::"memory");
+    }
+    return ap - an;
+}
+
 static inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 }  // namespace bpw

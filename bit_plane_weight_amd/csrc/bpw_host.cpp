@@ -282,40 +282,35 @@ struct Geometry {
     int32_t glog, kblk, nchunk, tile_rows;
 };
 
-// Lanes per row G = 2^glog and beats per lane K.
-// Tiled (byte-lane) kernel: the smallest power-of-two G with ceil(bpr / G) <= kKMax, capped at a
-// full wave; wider rows take passes of G * kKMax blocks.
-// Bit-serial kernels (batch-1 and small batch): the two row widths of the model have compiled-in
+// Lanes per row G = 2^glog and beats per lane K, for the batch-1 kernels (bit-serial and byte-lane
+// selects share the tiles) and the small batch: the two row widths of the model have compiled-in
 // geometry (2560 columns: 8 lanes x 5 beats; 6912 columns: 32 lanes x 4 beats). Other widths take the
-// same rule as above with K <= kKMaxBitSerial for rows of up to kXPassBlocks blocks (one LDS pass);
-// wider rows take passes of kXPassBlocks = 64 lanes x kKMaxBitSerial beats.
-Geometry geometry_for(int64_t bpr, bool bitserial) {
+// smallest power-of-two G with ceil(bpr / G) <= kKMaxBitSerial for rows of up to kXPassBlocks blocks
+// (one LDS pass); wider rows take passes of kXPassBlocks = 64 lanes x kKMaxBitSerial beats.
+Geometry geometry_for(int64_t bpr) {
     Geometry g{0, 0, 0, 0};
     if (bpr == 0) {
         g.tile_rows = bpw::kWaves * bpw::kIters * 64;
         return g;
     }
-    if (bitserial && (bpr == 40 || bpr == 108)) {
+    if (bpr == 40 || bpr == 108) {
         g.glog = bpr == 40 ? 3 : 5;
         g.kblk = bpr == 40 ? 5 : 4;
         g.nchunk = 1;
         g.tile_rows = bpw::kWaves * bpw::kIters * (int32_t)(64 >> g.glog);
         return g;
     }
-    const int kmax = bitserial ? bpw::kKMaxBitSerial : bpw::kKMax;
+    const int kmax = bpw::kKMaxBitSerial;
     int glog = 0;
     while (glog < 6 && ((bpr + (1 << glog) - 1) >> glog) > kmax) ++glog;
     int64_t G = (int64_t)1 << glog;
     int64_t k = (bpr + G - 1) / G;
     int64_t nchunk = 1;
-    if (bitserial && bpr > bpw::kXPassBlocks) {
+    if (bpr > bpw::kXPassBlocks) {
         glog = 6;
         G = 64;
         k = bpw::kXPassBlocks / G;
         nchunk = (bpr + bpw::kXPassBlocks - 1) / bpw::kXPassBlocks;
-    } else if (k > kmax) {
-        k = kmax;
-        nchunk = (bpr + G * k - 1) / (G * k);
     }
     g.glog = glog;
     g.kblk = (int32_t)k;
@@ -347,37 +342,30 @@ inline int64_t tile_units(const Geometry &g) {
 }
 
 int64_t bitserial_tiles(const bpw_gemv_job &j) {
-    const Geometry g = geometry_for(j.m.bpr, true);
+    const Geometry g = geometry_for(j.m.bpr);
     const int64_t tu = tile_units(g);
     return (units_of(j.m.rows, g) + tu - 1) / tu;
-}
-
-int64_t bytelane_tiles(const bpw_gemv_job &j) {
-    const Geometry g = geometry_for(j.m.bpr, false);
-    return (j.m.rows + g.tile_rows - 1) / g.tile_rows;
 }
 
 // An IntMlp pair's tiles: kPairTileUnits row-groups of each matrix (so as many beats as a plain
 // tile of kTileUnits row-groups).
 int64_t pair_tiles(const bpw_intmlp_job &j) {
-    const Geometry g = geometry_for(j.gate.bpr, true);
+    const Geometry g = geometry_for(j.gate.bpr);
     const int64_t tu = tile_units(g) / 2;
     return (units_of(j.gate.rows, g) + tu - 1) / tu;
 }
 
 // n_work counts the tiles before the tail split; total bounds the table after it: the split and the
 // padding of the XCD runs (xcd_runs) give at most (n_work + kMaxXcds) * kTailDiv bit-serial tiles.
-Layout layout_for(const bpw_gemv_job *jobs, int32_t n, bool bitserial, const bpw_intmlp_job *mlp = nullptr,
-                  int32_t n_mlp = 0) {
+Layout layout_for(const bpw_gemv_job *jobs, int32_t n, const bpw_intmlp_job *mlp = nullptr, int32_t n_mlp = 0) {
     Layout L{};
     L.jobs_off = 0;
     L.n_work = 0;
-    for (int32_t i = 0; i < n; ++i) L.n_work += bitserial ? bitserial_tiles(jobs[i]) : bytelane_tiles(jobs[i]);
+    for (int32_t i = 0; i < n; ++i) L.n_work += bitserial_tiles(jobs[i]);
     for (int32_t i = 0; i < n_mlp; ++i) L.n_work += pair_tiles(mlp[i]);
     L.work_off = align_up(L.jobs_off + sizeof(bpw::DevJob) * (size_t)(n + n_mlp));
-    const size_t tile_bytes = bitserial ? sizeof(bpw::Tile) : sizeof(bpw::DevTile);
-    const int64_t tile_bound = bitserial && L.n_work > 0 ? (L.n_work + kMaxXcds) * kTailDiv : L.n_work;
-    L.total = align_up(L.work_off + tile_bytes * (size_t)tile_bound);
+    const int64_t tile_bound = L.n_work > 0 ? (L.n_work + kMaxXcds) * kTailDiv : 0;
+    L.total = align_up(L.work_off + sizeof(bpw::Tile) * (size_t)tile_bound);
     return L;
 }
 
@@ -395,7 +383,7 @@ bpw_status check_job(const bpw_gemv_job &j, int32_t i, const char *kind = "job")
     bpw_status st = check_dev_mat(&j.m, who);
     if (st) return st;
     const uint64_t bytes = (uint64_t)j.m.rows * (uint64_t)j.m.bpr * 16u;
-    const Geometry g = geometry_for(j.m.bpr, false);
+    const Geometry g = geometry_for(j.m.bpr);
     if ((uint64_t)(j.m.rows + g.tile_rows) * (uint64_t)j.m.bpr * 16u >= 0xFFFFFFF0ull)
         return fail(BPW_E_UNSUPPORTED, "%s: %llu plane bytes exceed the 32-bit offsets of one matrix", who,
                     (unsigned long long)bytes);
@@ -498,7 +486,7 @@ struct bpw_gemv_plan {
     int device;
     int32_t kernel;
     const bpw::DevJob *jobs;
-    const void *tiles;             // bpw::Tile (bit-serial) or bpw::DevTile (byte-lane), one per workgroup
+    const bpw::Tile *tiles;        // one per workgroup (either select)
     int64_t n_tiles;
     int32_t has_work;
 };
@@ -645,7 +633,7 @@ bpw_status bpw_upload(const bpw_host_mat *m, void *d_dst, size_t d_len, void *st
 
 size_t bpw_gemv_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs) {
     if (!jobs || n_jobs <= 0) return 0;
-    return std::max(layout_for(jobs, n_jobs, true).total, layout_for(jobs, n_jobs, false).total);
+    return layout_for(jobs, n_jobs).total;
 }
 
 static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp, int32_t n_mlp,
@@ -657,8 +645,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     if ((int64_t)n_jobs + n_mlp > INT32_MAX) return fail(BPW_E_INVAL, "too many jobs");
     if (kernel != BPW_KERNEL_AUTO && kernel != BPW_KERNEL_BITSERIAL && kernel != BPW_KERNEL_BYTELANE)
         return fail(BPW_E_UNSUPPORTED, "unknown kernel %d", (int)kernel);
-    const bool bitserial = (kernel != BPW_KERNEL_BYTELANE);
-    if (!bitserial && n_mlp > 0)
+    if (kernel == BPW_KERNEL_BYTELANE && n_mlp > 0)
         return fail(BPW_E_UNSUPPORTED, "IntMlp pairs run on the bit-serial kernel only (pinned: byte-lane)");
     for (int32_t i = 0; i < n_jobs; ++i) {
         bpw_status st = check_job(jobs[i], i);
@@ -669,7 +656,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         if (st) return st;
     }
     const int32_t n_all = n_jobs + n_mlp;
-    Layout L = layout_for(jobs, n_jobs, bitserial, mlp, n_mlp);
+    Layout L = layout_for(jobs, n_jobs, mlp, n_mlp);
     if (L.n_work > (int64_t)INT32_MAX)
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
     const size_t need = bpw_gemv_intmlp_workspace_bytes(jobs, n_jobs, mlp, n_mlp);
@@ -687,7 +674,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     plan->device = dev;
     plan->kernel = kernel;
     plan->jobs = reinterpret_cast<const bpw::DevJob *>(ws + L.jobs_off);
-    plan->tiles = ws + L.work_off;
+    plan->tiles = reinterpret_cast<const bpw::Tile *>(ws + L.work_off);
     plan->n_tiles = L.n_work;
     plan->has_work = 0;
     if (n_all == 0) {
@@ -698,7 +685,6 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     const size_t table_bytes = L.total;
     std::vector<uint8_t> host(table_bytes, 0);
     auto *hj = reinterpret_cast<bpw::DevJob *>(host.data() + L.jobs_off);
-    auto *ht = reinterpret_cast<bpw::DevTile *>(host.data() + L.work_off);
     auto *hb = reinterpret_cast<bpw::Tile *>(host.data() + L.work_off);
     // Tile-table order: the plain jobs in the order given, with the pairs merged in where their
     // share of the pairs' bytes matches the plain jobs' share so far (for a decode step: each layer's
@@ -726,7 +712,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     for (const int32_t i : order) {
         const bool pair = i >= n_jobs;
         const bpw_dev_mat &m = pair ? mlp[i - n_jobs].gate : jobs[i].m;
-        const Geometry g = geometry_for(m.bpr, bitserial);
+        const Geometry g = geometry_for(m.bpr);
         bpw::DevJob d{};
         d.planes = static_cast<const uint8_t *>(m.d_planes);
         d.rows = (int32_t)m.rows;
@@ -758,14 +744,10 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
             d.w_scale_up = j.up.w_scale;
         }
         hj[i] = d;
-        if (!bitserial) {
-            for (int64_t r0 = 0; r0 < m.rows; r0 += g.tile_rows) ht[t++] = bpw::DevTile{i, (int32_t)r0};
-        } else {
-            // tiles of one job in row order; jobs in the order given, pairs after the plain jobs (the
-            // whole table is then laid out per XCD, below)
-            const int64_t U = units_of(m.rows, g), tu = pair ? tile_units(g) / 2 : tile_units(g);
-            for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
-        }
+        // tiles of one job in row order, jobs in the order above (the whole table is then laid out per
+        // XCD, below)
+        const int64_t U = units_of(m.rows, g), tu = pair ? tile_units(g) / 2 : tile_units(g);
+        for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
         if (m.rows > 0) plan->has_work = 1;  // a job without rows has no tiles (a pair: not even K)
     }
     if (t != L.n_work) {
@@ -773,21 +755,17 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         return fail(BPW_E_UNSUPPORTED, "internal: %lld tiles written, %lld expected", (long long)t, (long long)L.n_work);
     }
     const int xccs = device_xcds();
-    if (bitserial) {
-        if (xccs > kMaxXcds) {
-            delete plan;
-            return fail(BPW_E_UNSUPPORTED, "device has %d XCDs; the tile table is sized for %lld", xccs,
-                        (long long)kMaxXcds);
-        }
-        // a plan too small to give every CU two wide tiles (one layer: 119) takes only narrow ones
-        const double share = t < 2 * (int64_t)device_cus() ? 1.0 : kTailShare;
-        plan->n_tiles = xcd_runs(hb, t, xccs, share);
-        if (plan->n_tiles > (int64_t)INT32_MAX) {
-            delete plan;
-            return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
-        }
-    } else {
-        xcd_contiguous(ht, t, xccs);
+    if (xccs > kMaxXcds) {
+        delete plan;
+        return fail(BPW_E_UNSUPPORTED, "device has %d XCDs; the tile table is sized for %lld", xccs,
+                    (long long)kMaxXcds);
+    }
+    // a plan too small to give every CU two wide tiles (one layer: 119) takes only narrow ones
+    const double share = t < 2 * (int64_t)device_cus() ? 1.0 : kTailShare;
+    plan->n_tiles = xcd_runs(hb, t, xccs, share);
+    if (plan->n_tiles > (int64_t)INT32_MAX) {
+        delete plan;
+        return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
@@ -809,7 +787,7 @@ size_t bpw_gemv_intmlp_workspace_bytes(const bpw_gemv_job *jobs, int32_t n_jobs,
                                        int32_t n_mlp) {
     if (n_mlp <= 0 || !mlp) return bpw_gemv_workspace_bytes(jobs, n_jobs);
     if (n_jobs < 0 || (n_jobs > 0 && !jobs)) return 0;
-    return layout_for(jobs, n_jobs, true, mlp, n_mlp).total;  // pairs need the bit-serial kernel
+    return layout_for(jobs, n_jobs, mlp, n_mlp).total;
 }
 
 bpw_status bpw_gemv_intmlp_plan_create(const bpw_gemv_job *jobs, int32_t n_jobs, const bpw_intmlp_job *mlp,
@@ -831,10 +809,10 @@ bpw_status bpw_gemv_plan_run(const bpw_gemv_plan *plan, void *stream) {
     if (st) return st;
     if (!plan->has_work) return BPW_OK;
     if (plan->kernel == BPW_KERNEL_BYTELANE)
-        return hip_status(bpw::launch_gemv_tiles(plan->jobs, static_cast<const bpw::DevTile *>(plan->tiles),
-                                                 (int32_t)plan->n_tiles, stream),
+        return hip_status(bpw::launch_gemv_bytelane(plan->jobs, plan->tiles,
+                                                    (int32_t)plan->n_tiles, stream),
                           "gemv launch");
-    return hip_status(bpw::launch_gemv_bitserial(plan->jobs, static_cast<const bpw::Tile *>(plan->tiles),
+    return hip_status(bpw::launch_gemv_bitserial(plan->jobs, plan->tiles,
                                                  (int32_t)plan->n_tiles, stream),
                       "gemv launch");
 }
@@ -966,7 +944,7 @@ static bpw_status check_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int
 
 static bpw::SmallBatchArgs small_batch_args(const bpw_dev_mat *m, const int8_t *d_X, int32_t batch, int64_t ldx,
                                             const float *x_scales, int32_t *d_out_i32, float *d_out_f32) {
-    const Geometry g = geometry_for(m->bpr, true);
+    const Geometry g = geometry_for(m->bpr);
     bpw::SmallBatchArgs a{};
     a.planes = static_cast<const uint8_t *>(m->d_planes);
     a.X = d_X;
@@ -996,7 +974,7 @@ bpw_status bpw_gemm_small_batch(const bpw_dev_mat *m, const int8_t *d_X, int32_t
     }
     bpw_status st = check_small_batch(m, d_X, batch, ldx, x_scales, d_out_i32, "small batch");
     if (st) return st;
-    const Geometry g = geometry_for(m->bpr, true);
+    const Geometry g = geometry_for(m->bpr);
     st = check_device();
     if (st) return st;
     if (m->rows == 0) return BPW_OK;
@@ -1089,7 +1067,7 @@ inline int64_t tok_tile_units(const Geometry &g) {
 int64_t tok_base_tiles(const bpw_sb_job *jobs, int32_t n) {
     int64_t t = 0;
     for (int32_t i = 0; i < n; ++i) {
-        const Geometry g = geometry_for(jobs[i].m.bpr, true);
+        const Geometry g = geometry_for(jobs[i].m.bpr);
         const int64_t tu = tok_tile_units(g);
         t += (units_of(jobs[i].m.rows, g) + tu - 1) / tu;
     }
@@ -1206,7 +1184,7 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
             d.w_scale = j.m.w_scale;
             for (int32_t k = 0; k < batch; ++k) d.x_scales[k] = j.x_scales[k];
             hj[i] = d;
-            const Geometry g = geometry_for(j.m.bpr, true);
+            const Geometry g = geometry_for(j.m.bpr);
             const int64_t U = units_of(j.m.rows, g), w = tok_tile_units(g);
             for (int64_t u = 0; u < U; u += w) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + w), 0};
         }

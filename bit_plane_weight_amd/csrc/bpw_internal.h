@@ -12,7 +12,6 @@ namespace bpw {
 // Launch geometry of the ternary GEMV kernels.
 constexpr int kWaves = 4;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;     // wave64
-constexpr int kKMax = 7;                  // 64-column blocks one lane handles per pass (tiled byte-lane kernel)
 constexpr int kKMaxBitSerial = 2;         // beats one lane holds per row-group (bit-serial kernels,
                                           // shapes other than 2560 and 6912 columns)
 constexpr int kSBWaves = 16;              // waves of a small-batch workgroup (one row-group each)
@@ -34,9 +33,9 @@ struct DevJob {
     float w_scale;
     const float *x_scale_ptr;  // if set, the activation scale is read from here (x_scale ignored)
     int32_t glog;           // log2 of lanes per row (G)
-    int32_t kblk;           // blocks per lane per pass (<= kKMax; 0 when cols == 0)
+    int32_t kblk;           // beats per lane per pass (0 when cols == 0)
     int32_t nchunk;         // passes over the row: bpr <= G * kblk * nchunk
-    int32_t tile_rows;      // rows per workgroup tile = kWaves * kIters * (64 / G) (tiled kernels)
+    int32_t tile_rows;      // kWaves * kIters * (64 / G) (host bookkeeping; the kernels do not read it)
     uint32_t plane_bytes;   // rows * bpr * 16 (the buffer range of the weight loads)
     int32_t pair;           // 1: an IntMlp gate/up pair (planes = gate, out_i32 = gate sums or null)
     // IntMlp pairs only:
@@ -57,10 +56,6 @@ struct Tile {
     int32_t pad;
 };
 
-struct DevTile {
-    int32_t job;
-    int32_t row0;
-};
 
 // Small-batch arguments (passed by value; <= kMaxBatch tokens).
 constexpr int kMaxBatch = 64;
@@ -184,7 +179,7 @@ constexpr int kStaticMaxDevices = 64;
 int static_scratch(void **ptr, size_t *len);
 
 // Kernel launchers (bpw_*.hip). Each returns the hipError_t of its launch as int.
-int launch_gemv_tiles(const DevJob *jobs, const DevTile *tiles, int32_t n_tiles, void *stream);  // byte-lane
+int launch_gemv_bytelane(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 // bit-serial: workgroup w runs tiles[w]
 int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);

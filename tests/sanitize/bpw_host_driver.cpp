@@ -49,7 +49,7 @@ hipError_t hipStreamSynchronize(hipStream_t) { unreachable("hipStreamSynchronize
 }
 
 namespace bpw {
-int launch_gemv_tiles(const DevJob *, const DevTile *, int32_t, void *) { unreachable("a launcher"); }
+int launch_gemv_bytelane(const DevJob *, const Tile *, int32_t, void *) { unreachable("a launcher"); }
 int launch_gemv_bitserial(const DevJob *, const Tile *, int32_t, void *) { unreachable("a launcher"); }
 int launch_gemm_small_batch(const SmallBatchArgs &, int32_t, int32_t, void *) { unreachable("a launcher"); }
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &, void *) { unreachable("a launcher"); }

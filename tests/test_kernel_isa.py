@@ -36,11 +36,14 @@ def loop_bodies(asm: str) -> dict:
 
 
 @pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
-def test_streaming_loops_wait_only_for_the_older_loads(tmp_path):
+@pytest.mark.parametrize("src", [SRC, os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_bytelane.hip")],
+                         ids=["bitserial", "bytelane"])
+def test_streaming_loops_wait_only_for_the_older_loads(tmp_path, src):
+    """Both batch-1 kernels (the bit-serial select and the byte-lane select share the tile code)."""
     out = tmp_path / "gemv.s"
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
-                    SRC, "-o", str(out)], check=True, capture_output=True)
+                    src, "-o", str(out)], check=True, capture_output=True)
     loops = {k: b for k, b in loop_bodies(out.read_text()).items()
              if sum("buffer_load_dwordx4" in x for x in b) >= 4}
     # the 2560-column loop (2 x 5 beat loads), the 6912-column loop (2 x 4) and the generic K = 2 one
