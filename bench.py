@@ -33,7 +33,7 @@ BASE_SEED = 0x2B47
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_bitserial_decode_step_traffic.json")
 # sources of the decode-step GEMV kernel; the committed counter summary holds their hash
 KERNEL_SRCS = [os.path.join(ROOT, "bit_plane_weight_amd", "csrc", f)
-               for f in ("bpw_gemv.hip", "bpw_device.h", "bpw_internal.h")]
+               for f in ("bpw_gemv.hip", "bpw_gemv_tile.h", "bpw_device.h", "bpw_internal.h")]
 # the BITCOS GEMV kernel: its VALU instruction count per decode-step launch, from a committed counter
 # run on the same sources
 BITCOS_FILE = os.path.join(ROOT, "profiles", "gemv_bitcos_decode_step_counters.json")

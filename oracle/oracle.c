@@ -452,9 +452,11 @@ int oracle_intmlp(const uint8_t *gate, const uint8_t *up, int64_t len, int64_t r
  * order, gets a sign bit (set when it is -1). Zeros cost their presence bit only, so n weights with
  * nnz nonzeros take n + nnz bits, 2 - z bits per weight at zero density z.
  *
- * Flat form (the page's packer works on a flat list): bit i of the bitmap is bit (i & 7) of byte
- * i >> 3; the k-th nonzero's sign is bit (k & 7) of byte k >> 3 of the sign vector. Sizes:
- * ceil(n / 8) + ceil(nnz / 8) bytes.
+ * Flat form: bit i of the bitmap is bit (i & 7) of byte i >> 3; the k-th nonzero's sign is bit
+ * (k & 7) of byte k >> 3 of the sign vector, set for -1. This is the layout of the packer and
+ * unpacker the page prints in "A bitmap and a sign" (pack_bitcos / unpack_bitcos, tested there by a
+ * round trip on a flat list); the two functions below are written from that definition, not from the
+ * printed code. Sizes: ceil(n / 8) + ceil(nnz / 8) bytes.
  *
  * Row form (the layout the GPU reads; the page leaves the blocking to the kernel): per row,
  * bpr = ceil(cols / 64) presence words (u64, column c at bit c & 63 of word c >> 6, padding clear),
@@ -479,8 +481,8 @@ int oracle_bitcos_pack_flat(const int8_t *w, int64_t n, uint8_t *bitmap, uint8_t
 }
 
 /* The inverse, from the definition of the two arrays: the k-th set presence bit (in weight order)
- * takes sign bit k. The page prints an unpacker of its own; this one is written from the definition
- * and checks its bounds: bitmap_len must cover n bits, and a bitmap with more set bits than the
+ * takes sign bit k (the page's unpack_bitcos in "A bitmap and a sign" decodes the same layout; this
+ * one is written from the definition) and checks its bounds: bitmap_len must cover n bits, and a bitmap with more set bits than the
  * sign_len bytes hold sign bits is refused (OR_E_SIZE) instead of read past the signs. */
 int oracle_bitcos_unpack_flat(const uint8_t *bitmap, int64_t bitmap_len, const uint8_t *signs, int64_t sign_len,
                               int64_t n, int8_t *w) {
