@@ -362,23 +362,27 @@ def configs_measure(bpw, torch, dev, ds, reps: int = 30) -> dict:
     return res
 
 
-def probe_gbs(bpw, torch, dev) -> float:
-    """Streaming-read probe: best of 5 passes over 4 GiB (the pages' measured-roofline method)."""
+def probe_gbs(bpw, torch, dev) -> tuple[float, dict]:
+    """Streaming-read probe (the pages' measured-roofline method): every read shape of the probe, best
+    of 5 passes over 4 GiB each; the probe is the best shape. Returns (GB/s, GB/s per shape)."""
     n = 4 << 30
     buf = torch.zeros(n, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
-    settle(torch, lambda: bpw.bpw_stream_read_probe(buf, sink))
-    best = 0.0
-    for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        bpw.bpw_stream_read_probe(buf, sink)
-        b.record()
-        torch.cuda.synchronize()
-        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    per_shape = {}
+    for shape in range(bpw.PROBE_SHAPES):
+        settle(torch, lambda: bpw.bpw_stream_read_probe(buf, sink, shape=shape))
+        best = 0.0
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            bpw.bpw_stream_read_probe(buf, sink, shape=shape)
+            b.record()
+            torch.cuda.synchronize()
+            best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+        per_shape[shape] = round(best, 1)
     del buf
     torch.cuda.empty_cache()
-    return best
+    return max(per_shape.values()), per_shape
 
 
 def head_measure(bpw, torch, synth, dev, reps: int = 20) -> dict:
@@ -755,8 +759,9 @@ def main() -> int:
     torch.cuda.empty_cache()
     if "probe" in legs:
         log("probe")
-        pg = probe_gbs(bpw, torch, dev)
+        pg, shapes = probe_gbs(bpw, torch, dev)
         result["probe_gbs"] = round(pg, 1)
+        result["probe_gbs_per_shape"] = shapes
         result["pct_probe"] = round(100.0 * achieved / pg, 2)
     if "head" in legs:
         log("dense head")

@@ -22,7 +22,7 @@ __all__ = [
     "gemv_job", "bpw_gemv_workspace_bytes", "bpw_gemv", "bpw_gemv_noalloc", "GemvPlan",
     "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
     "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
-    "bpw_dense_head_gemv", "bpw_stream_read_probe", "bpw_cache_flush",
+    "bpw_dense_head_gemv", "bpw_stream_read_probe", "PROBE_SHAPES", "bpw_cache_flush",
     "TritFile", "TritFormatError", "TritTensor", "bpw_fnv1a64", "TRIT_F32", "TRIT_TERNARY", "TRIT_BF16",
     "BitcosHost", "bpw_bitcos_pack_i8", "bpw_bitcos_from_planes", "DevBitcos", "bpw_bitcos_upload", "bitcos_job",
     "bpw_bitcos_workspace_bytes", "BitcosPlan",
@@ -559,11 +559,14 @@ def bpw_dense_head_gemv(w_bf16, x_bf16, y, stream=None) -> None:
 # ------------------------------------------------------------------------------ measurement
 
 
-def bpw_stream_read_probe(d_buf, d_sink, stream=None) -> None:
+PROBE_SHAPES = 5
+
+
+def bpw_stream_read_probe(d_buf, d_sink, stream=None, shape: int = 0) -> None:
     if d_sink is None or d_sink.element_size() != 4 or d_sink.numel() < 1:
         raise ValueError("d_sink must be a 4-byte-element tensor of at least one element")
-    _lib.check(_lib.lib().bpw_stream_read_probe(_dptr(d_buf), d_buf.numel() * d_buf.element_size(),
-                                                _dptr(d_sink), _stream(stream)))
+    _lib.check(_lib.lib().bpw_stream_read_probe_shape(_dptr(d_buf), d_buf.numel() * d_buf.element_size(),
+                                                      _dptr(d_sink), int(shape), _stream(stream)))
 
 
 def bpw_cache_flush(d_buf, stream=None) -> None:

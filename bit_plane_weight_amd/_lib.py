@@ -138,6 +138,7 @@ def lib():
         "bpw_quant_plan_free": (None, [vp]),
         "bpw_dense_head_gemv": (i32, [vp, i64, i64, vp, vp, vp]),
         "bpw_stream_read_probe": (i32, [vp, sz, vp, vp]),
+        "bpw_stream_read_probe_shape": (i32, [vp, sz, vp, i32, vp]),
         "bpw_trit_open": (i32, [vp, sz, ctypes.POINTER(vp), ctypes.POINTER(BpwTritErr)]),
         "bpw_trit_verify": (i32, [vp, i32, ctypes.POINTER(BpwTritErr)]),
         "bpw_trit_close": (None, [vp]),

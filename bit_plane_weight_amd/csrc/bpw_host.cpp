@@ -1290,12 +1290,20 @@ bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t c
     return hip_status(bpw::launch_dense_head(d_w_bf16, rows, cols, d_x_bf16, d_y, stream), "dense head launch");
 }
 
-bpw_status bpw_stream_read_probe(const void *d_buf, size_t len, uint32_t *d_sink, void *stream) {
+bpw_status bpw_stream_read_probe_shape(const void *d_buf, size_t len, uint32_t *d_sink, int32_t shape,
+                                       void *stream) {
     if (!d_buf || !d_sink || (len % 16) || ((uintptr_t)d_buf & 15u))
         return fail(BPW_E_INVAL, "probe: buffer must be non-NULL, 16-byte aligned, len %% 16 == 0");
+    if (shape < 0 || shape >= bpw::kProbeShapes)
+        return fail(BPW_E_INVAL, "probe: shape %d is not one of 0 .. %d", (int)shape, (int)bpw::kProbeShapes - 1);
+    if (len > ((size_t)1 << 40)) return fail(BPW_E_INVAL, "probe: len above 2^40 bytes");
     bpw_status st = check_device();
     if (st) return st;
-    return hip_status(bpw::launch_probe(d_buf, len, d_sink, stream), "probe launch");
+    return hip_status(bpw::launch_probe(d_buf, len, d_sink, shape, stream), "probe launch");
+}
+
+bpw_status bpw_stream_read_probe(const void *d_buf, size_t len, uint32_t *d_sink, void *stream) {
+    return bpw_stream_read_probe_shape(d_buf, len, d_sink, 0, stream);
 }
 
 bpw_status bpw_cache_flush(void *d_buf, size_t len, void *stream) {

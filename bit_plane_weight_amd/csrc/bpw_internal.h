@@ -190,7 +190,8 @@ int launch_gemv_tokens(const TokJob *jobs, const Tile *tiles, int32_t n_tiles, i
 int launch_gemv_bitcos(const BitcosJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);
 int launch_quantize(const QuantJob *jobs, int32_t n_jobs, void *stream);
-int launch_probe(const void *buf, size_t len, uint32_t *sink, void *stream);
+constexpr int32_t kProbeShapes = 5;
+int launch_probe(const void *buf, size_t len, uint32_t *sink, int32_t shape, void *stream);
 int launch_flush(void *buf, size_t len, void *stream);
 
 }  // namespace bpw

@@ -455,6 +455,13 @@ bpw_status bpw_dense_head_gemv(const uint16_t *d_w_bf16, int64_t rows, int64_t c
  * probe on the same machine): reads len bytes at d_buf (16-byte aligned, len % 16 == 0) once and
  * writes a data-dependent word to d_sink (device uint32 [1]) so the reads cannot be elided. */
 bpw_status bpw_stream_read_probe(const void *d_buf, size_t len, uint32_t *d_sink, void *stream);
+/* The same read in one of five shapes (0 is the one bpw_stream_read_probe uses): 0: 256-thread
+ * workgroups of 10 buffer loads per lane (40 KiB each); 1: the same with global loads; 2: 512 threads
+ * x 8 buffer loads (64 KiB); 3: the same with global loads; 4: 256 threads x 4 buffer loads (16 KiB).
+ * Every shape reads each byte once, non-temporal, in XCD-contiguous runs of workgroups; a measured
+ * roofline takes the best of them. Another shape, or len above 2^40 bytes: BPW_E_INVAL. */
+bpw_status bpw_stream_read_probe_shape(const void *d_buf, size_t len, uint32_t *d_sink, int32_t shape,
+                                       void *stream);
 
 /* Read and rewrite len bytes at d_buf (16-byte aligned, len % 16 == 0) so that caches hold none of
  * the bytes a following timed kernel will read (size it above L2 + the 256 MB last-level cache). */

@@ -63,7 +63,7 @@ int launch_dense_head(const uint16_t *, int64_t, int64_t, const uint16_t *, floa
     unreachable("a launcher");
 }
 int launch_quantize(const QuantJob *, int32_t, void *) { unreachable("a launcher"); }
-int launch_probe(const void *, size_t, uint32_t *, void *) { unreachable("a launcher"); }
+int launch_probe(const void *, size_t, uint32_t *, int32_t, void *) { unreachable("a launcher"); }
 int launch_flush(void *, size_t, void *) { unreachable("a launcher"); }
 int static_scratch(void **, size_t *) { unreachable("static_scratch"); }
 }  // namespace bpw

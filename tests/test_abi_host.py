@@ -177,6 +177,8 @@ def test_empty_and_bad_arguments():
     assert L.bpw_gemv_plan_create(j, 1, 7, None, 0, None, ctypes.byref(h)) == _lib.E_UNSUPPORTED
     assert L.bpw_dense_head_gemv(None, 10, 12, None, None, None) == _lib.E_INVAL
     assert L.bpw_stream_read_probe(None, 16, None, None) == _lib.E_INVAL
+    for shape in (-1, 5, 99):  # checked before any device call
+        assert L.bpw_stream_read_probe_shape(256, 16, 512, shape, None) == _lib.E_INVAL
 
 
 def test_device_check_without_gpu_is_an_error_not_a_fallback():

@@ -349,9 +349,11 @@ def test_argument_errors_on_gpu(dev):
 
 
 def test_probe_and_flush_run(dev):
-    log("case: probe and flush")
-    buf = torch.zeros(64 << 20, dtype=torch.uint8, device=dev)
+    log("case: probe (every shape, a length that ends inside a chunk) and flush")
+    buf = torch.zeros((64 << 20) + 48, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for shape in range(bpw.PROBE_SHAPES):
+        bpw.bpw_stream_read_probe(buf, sink, shape=shape)
     bpw.bpw_stream_read_probe(buf, sink)
     bpw.bpw_cache_flush(buf)
     torch.cuda.synchronize()
