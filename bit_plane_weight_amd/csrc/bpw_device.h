@@ -23,6 +23,13 @@ __device__ __forceinline__ u32x4 load_beat(__amdgpu_buffer_rsrc_t r, uint32_t of
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kAuxNT));
 }
 
+// Next work item for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
+__device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(claim, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(v);
+}
+
 // Bitwise select m ? p : n, written so the compiler emits one v_bitop3_b32.
 __device__ __forceinline__ uint32_t select_bits(uint32_t m, uint32_t p, uint32_t n) { return ((p ^ n) & m) ^ n; }
 

@@ -23,13 +23,6 @@ namespace bpw {
 // matrix use an offset that the buffer range check answers with zeros, which also covers the
 // partial last row-group.
 
-// Next row-group for this wave: lane 0 takes a ticket from the workgroup's LDS counter.
-__device__ __forceinline__ int claim_next(uint32_t *claim, int lane) {
-    uint32_t v = 0;
-    if (lane == 0) v = atomicAdd(claim, 1u);
-    return (int)__builtin_amdgcn_readfirstlane(v);
-}
-
 // IntMlp epilogue of one row of a gate/up pair (Tritium paper, "Numerics", IntMlp): the exact
 // sums a_g, a_u become t = relu(a_g)^2 * a_u in 64-bit integers (|a| <= 128 * cols and the host
 // admits cols <= 16383, so t cannot overflow).

@@ -1028,18 +1028,71 @@ inline int64_t sb_iterations(int64_t bpr) { return (bpr + 3) / 4; }
 
 // The grouped matrix-core launch's workspace: job records, tile table, the table of activation-operand
 // pieces, then each job's activation operands (token groups x iterations x 4 KiB, 256-byte aligned).
+// Tiles of a grouped small-batch job per token group: kSBGroupRows rows each.
+inline int64_t sb_job_tiles(const bpw_sb_job &j) { return (j.m.rows + bpw::kSBGroupRows - 1) / bpw::kSBGroupRows; }
+
+// Table entries the grouped small-batch plan may write for n work tiles: the cost-balanced XCD runs
+// below are padded to the longest run; beyond this bound the plan keeps equal-count runs.
+inline int64_t sb_tile_bound(int64_t n) { return n > 0 ? 2 * n + kMaxXcds : 0; }
+
+// Lay the job-ordered tiles of the grouped small batch out per XCD. The workgroups of one tile differ
+// in cost (a 6912-column tile streams 2.7 times the beats of a 2560-column one) and every tile pays a
+// fixed start (table, operand staging) and end; measured at 4 tokens on the decode-step set, a
+// 256-row tile took about 6.8 us + 1.05 ns per row-beat (17.5 us at 2560 columns, 35.7 at 6912). The
+// job-ordered table is cut into X contiguous runs of equal estimated cost (so each job's operands stay
+// in one XCD's L2), each run is ordered longest tile first (the run then ends in short tiles), and
+// runs are padded with empty tiles (row_tile -1: the workgroup exits at once) and interleaved,
+// workgroup b taking entry b / X of run b mod X. With equal-count runs the XCDs finished 21 us apart.
+// Returns the table length, or n (equal-count runs, xcd_contiguous) if the padded runs would not fit.
+int64_t sb_cost_runs(bpw::SBTile *tiles, int64_t n, int X, const bpw_sb_job *jobs, int64_t cap) {
+    X = std::max(1, X);
+    auto cost = [&](const bpw::SBTile &t) {
+        const bpw_sb_job &j = jobs[t.job];
+        const int64_t r0 = (int64_t)t.row_tile * bpw::kSBGroupRows;
+        const int64_t rows = std::min<int64_t>((int64_t)t.units * bpw::kSBGroupRows, j.m.rows - r0);
+        return 6500.0 + (double)rows * (double)j.m.bpr;
+    };
+    double total = 0.0;
+    for (int64_t i = 0; i < n; ++i) total += cost(tiles[i]);
+    std::vector<std::vector<bpw::SBTile>> runs((size_t)X);
+    double acc = 0.0;
+    size_t longest = 0;
+    for (int64_t i = 0, x = 0; i < n; ++i) {
+        const double c = cost(tiles[i]);
+        // start the next run once this one holds its share (the midpoint of the tile decides)
+        while (x + 1 < X && acc + 0.5 * c > total * (double)(x + 1) / (double)X) ++x;
+        runs[(size_t)x].push_back(tiles[i]);
+        acc += c;
+    }
+    for (auto &r : runs) {
+        std::stable_sort(r.begin(), r.end(),
+                         [&](const bpw::SBTile &a, const bpw::SBTile &b) { return cost(a) > cost(b); });
+        longest = std::max(longest, r.size());
+    }
+    if ((int64_t)(longest * (size_t)X) > cap) {
+        xcd_contiguous(tiles, n, X);
+        return n;
+    }
+    int64_t t = 0;
+    for (size_t k = 0; k < longest; ++k)
+        for (int x = 0; x < X; ++x)
+            tiles[t++] = k < runs[(size_t)x].size() ? runs[(size_t)x][k] : bpw::SBTile{0, -1, 0, 0};  // padding
+    return t;
+}
+
 SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
     SBLayout L{};
     const int64_t groups = (batch + 15) / 16;
     size_t xt_bytes = 0;
     for (int32_t i = 0; i < n; ++i) {
-        L.n_tiles += (jobs[i].m.rows + bpw::kSBGroupRows - 1) / bpw::kSBGroupRows * groups;
+        L.n_tiles += sb_job_tiles(jobs[i]) * groups;
         L.n_xtiles += sb_iterations(jobs[i].m.bpr) * groups;
         xt_bytes += align_up((size_t)(sb_iterations(jobs[i].m.bpr) * groups) * 4096u);
     }
     L.jobs_off = 0;
+    // room for the cost-balanced XCD runs padded to one length (sb_cost_runs)
     L.tiles_off = align_up(sizeof(bpw::SmallBatchArgs) * (size_t)n);
-    L.xtiles_off = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)L.n_tiles);
+    L.xtiles_off = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)sb_tile_bound(L.n_tiles));
     L.xt_off = align_up(L.xtiles_off + sizeof(bpw::XTile) * (size_t)L.n_xtiles);
     L.total = align_up(L.xt_off + xt_bytes);
     return L;
@@ -1238,11 +1291,16 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
         xt += align_up((size_t)(its * groups) * 4096u);
         for (int32_t gq = 0; gq < groups; ++gq)
             for (int64_t it = 0; it < its; ++it) hx[tx++] = bpw::XTile{i, gq, (int32_t)it, 0};
-        const int64_t rt = (j.m.rows + bpw::kSBGroupRows - 1) / bpw::kSBGroupRows;
-        for (int64_t r = 0; r < rt; ++r)
-            for (int32_t gq = 0; gq < groups; ++gq) ht[t++] = bpw::SBTile{i, (int32_t)r, gq, 0};
+        for (int64_t r = 0; r < sb_job_tiles(j); ++r)
+            for (int32_t gq = 0; gq < groups; ++gq) ht[t++] = bpw::SBTile{i, (int32_t)r, gq, 1};
     }
-    xcd_contiguous(ht, t, device_xcds());
+    const int xccs = device_xcds();
+    if (xccs > kMaxXcds) {
+        delete plan;
+        return fail(BPW_E_UNSUPPORTED, "device has %d XCDs; the tile table is sized for %lld", xccs,
+                    (long long)kMaxXcds);
+    }
+    plan->n_tiles = sb_cost_runs(ht, t, xccs, jobs, sb_tile_bound(t));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), L.xt_off, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");

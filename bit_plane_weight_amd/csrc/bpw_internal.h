@@ -100,9 +100,9 @@ constexpr int kSBStages = 2;  // beat register sets per wave (steps in flight + 
 constexpr int kSBGroupRows = kSBGroupWaves * kSBWaveTiles * 16;
 struct SBTile {
     int32_t job;
-    int32_t row_tile;
+    int32_t row_tile;  // rows kSBGroupRows * row_tile ..; -1: an empty tile (padding of the XCD runs)
     int32_t tok_group;
-    int32_t pad;
+    int32_t units;     // 1 (rows kSBGroupRows * row_tile .. + kSBGroupRows - 1); 0 for padding
 };
 
 // One GEMV of 2 to 4 tokens in the grouped small-batch launch (bit-serial; 2560 or 6912 columns).

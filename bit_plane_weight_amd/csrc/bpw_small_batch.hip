@@ -318,10 +318,11 @@ __device__ __forceinline__ v4i mfma_beat_own(const uint32_t *lut, const u32x4 &b
 // one select per word, and one DPP rotate by 8 within each row of 16 lanes.
 __device__ __forceinline__ uint32_t swap8(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false); }
 
-__device__ __forceinline__ void split_step(const u32x4 &r0, const u32x4 &r1, bool lo, u32x4 &p0, u32x4 &p1) {
-    p0 = lo ? r0 : r1;
+__device__ __forceinline__ u32x4 step_first(const u32x4 &r0, const u32x4 &r1, bool lo) { return lo ? r0 : r1; }
+
+__device__ __forceinline__ u32x4 step_second(const u32x4 &r0, const u32x4 &r1, bool lo) {
     const u32x4 t = lo ? r1 : r0;
-    p1 = u32x4{swap8(t.x), swap8(t.y), swap8(t.z), swap8(t.w)};
+    return u32x4{swap8(t.x), swap8(t.y), swap8(t.z), swap8(t.w)};
 }
 
 // The activation operands (see sb_act_operands_kernel) of up to kXtPassSteps steps sit in LDS: the
@@ -333,9 +334,11 @@ constexpr int kXtPassSteps = 6;  // 48 KiB: table + one pass = 80 KiB, two workg
 constexpr int kXtStepBytes = 8192;  // 2 iterations x 4 quarters x 64 lanes x 16 bytes
 constexpr int kXtPassBytes = kXtPassSteps * kXtStepBytes;
 
-// LDS bytes of the grouped launch: the table, then one pass of operands.
-constexpr size_t kSbGroupedLds = (size_t)kLutBytes + (size_t)kXtPassBytes;
-static_assert(2 * kSbGroupedLds <= 160 * 1024, "two workgroups per compute unit");
+// LDS of the grouped launch: the table in a static array (its address is then known when the kernel
+// is compiled and folds into each lookup's instruction offset; from dynamic LDS every lookup paid a
+// v_add of the base, 64 VALU per step), then one pass of operands in dynamic LDS.
+constexpr size_t kSbGroupedLds = (size_t)kXtPassBytes;
+static_assert(2 * ((size_t)kLutBytes + kSbGroupedLds) <= 160 * 1024, "two workgroups per compute unit");
 
 // Copy one pass of operands (kXtPassBytes) from global memory into LDS, all threads of the workgroup,
 // every load issued before the first store, with no branch: bytes past `valid` read zeros through the
@@ -402,20 +405,20 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
                 beat[t][j] = load_beat(wr, in ? (row[t][j] * (uint32_t)bpr + (uint32_t)b) * 16u : kOutOfRange);
             }
     };
+    // A step in two halves (its first iteration for every row tile, then its second), each with its
+    // own four operands: 16 fewer registers live than reading all eight at once.
     auto step = [&](const u32x4 (&beat)[RT][2], int ls) {  // ls: the step's index within the pass
         const uint8_t *xs = xl + (uint32_t)ls * kXtStepBytes + (uint32_t)lane * 16u;
-        u32x4 xa[4], xb[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            xa[q] = *reinterpret_cast<const u32x4 *>(xs + q * 1024);
-            xb[q] = *reinterpret_cast<const u32x4 *>(xs + 4096 + q * 1024);
-        }
+        for (int h = 0; h < 2; ++h) {
+            u32x4 xo[4];
 #pragma unroll
-        for (int t = 0; t < RT; ++t) {
-            u32x4 p0, p1;
-            split_step(beat[t][0], beat[t][1], lo, p0, p1);
-            acc[t] = mfma_beat_own(lut, p0, xa, acc[t], lb);
-            acc[t] = mfma_beat_own(lut, p1, xb, acc[t], lb);
+            for (int q = 0; q < 4; ++q) xo[q] = *reinterpret_cast<const u32x4 *>(xs + h * 4096 + q * 1024);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) {
+                const u32x4 p = h == 0 ? step_first(beat[t][0], beat[t][1], lo) : step_second(beat[t][0], beat[t][1], lo);
+                acc[t] = mfma_beat_own(lut, p, xo, acc[t], lb);
+            }
         }
     };
     for (int s0 = 0; s0 < n_steps || s0 == 0; s0 += kXtPassSteps) {
@@ -459,15 +462,16 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
 
 __global__ __launch_bounds__(64 * kSBGroupWaves) void gemm_small_batch_mfma_grouped_kernel(
     const SmallBatchArgs *__restrict__ jobs, const SBTile *__restrict__ tiles) {
+    __shared__ __attribute__((aligned(16))) uint32_t lut[kLutBytes / 4];
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t *lut = reinterpret_cast<uint32_t *>(smem);
-    fill_lut_copies(lut, 64 * kSBGroupWaves);  // made visible by the first staging barrier
     const SBTile t = tiles[blockIdx.x];
+    if (t.row_tile < 0) return;  // padding of the XCD runs (uniform over the workgroup)
+    fill_lut_copies(lut, 64 * kSBGroupWaves);  // made visible by the first staging barrier
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const SmallBatchArgs &A = jobs[t.job];
     const uint32_t rt0 = (uint32_t)(t.row_tile * kSBGroupWaves * kSBWaveTiles + wave * kSBWaveTiles);
     const bool active = (int64_t)rt0 * kMfmaRows < A.rows;  // wave-uniform; idle waves still stage
-    mfma_wave_tiles<kSBWaveTiles, 64 * kSBGroupWaves, kSBStages>(A, rt0, (uint32_t)t.tok_group, lut, smem + kLutBytes,
+    mfma_wave_tiles<kSBWaveTiles, 64 * kSBGroupWaves, kSBStages>(A, rt0, (uint32_t)t.tok_group, lut, smem,
                                                                  active);
 }
 
