@@ -609,6 +609,92 @@ def traffic_from_profile() -> float | None:
     return rec.get("traffic_bytes_per_launch")
 
 
+def _counter_rows(run_dir: str) -> list[dict]:
+    """Rows of the rocprofv3 counter CSV (--output-format csv) under run_dir."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *counter_collection.csv under {run_dir}")
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows: list[dict], kernel: str, counter: str, grid: int | None = None) -> list[float]:
+    """Per-dispatch totals of one counter for the dispatches of one kernel (and grid size, in threads)."""
+    acc: dict = {}
+    for r in rows:
+        if kernel not in r["Kernel_Name"] or r["Counter_Name"] != counter:
+            continue
+        if grid is not None and int(r["Grid_Size"]) != grid:
+            continue
+        acc[r["Dispatch_Id"]] = acc.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    return list(acc.values())
+
+
+def write_counter_records(fetch_dir: str, write_dir: str, bitcos_dir: str, out_gemv: str = TRAFFIC_FILE,
+                          out_bitcos: str = BITCOS_FILE) -> None:
+    """Write the two committed counter records from three rocprofv3 runs of this file, each with
+    --copy-calibration --legs bitcos: FETCH_SIZE, WRITE_SIZE, and the BITCOS kernel's SQ counters
+    (SQ_INSTS_VALU SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVES). Byte counters are scaled by what they
+    read for the copy calibration (the probe reads 1 GiB, the flush rewrites 1 GiB); each figure is the
+    median over the dispatches. The records carry the hash of the kernel sources as they are now."""
+    fr, wr, br = _counter_rows(fetch_dir), _counter_rows(write_dir), _counter_rows(bitcos_dir)
+    gib_kib = float(1 << 20)
+    probe_fetch = statistics.median(_per_dispatch(fr, "stream_probe_kernel", "FETCH_SIZE"))
+    flush_write = statistics.median(_per_dispatch(wr, "flush_kernel", "WRITE_SIZE"))
+    fetch_scale, write_scale = gib_kib / probe_fetch, gib_kib / flush_write
+    cal = (f"FETCH_SIZE of the streaming probe reading 1 GiB ({gib_kib:.0f} KiB) read {probe_fetch:.1f} KiB; "
+           f"WRITE_SIZE of the cache flush rewriting 1 GiB read {flush_write:.1f} KiB")
+    steps = 11712 * 256  # the decode-step launch's grid, in threads
+    gf = statistics.median(_per_dispatch(fr, "gemv_bitserial_kernel", "FETCH_SIZE", steps))
+    gw = statistics.median(_per_dispatch(wr, "gemv_bitserial_kernel", "WRITE_SIZE", steps))
+    rel = lambda paths: [os.path.relpath(q, ROOT) for q in paths]  # noqa: E731
+    gemv = {
+        "kernel": "gemv_bitserial_kernel",
+        "workload": "decode-step ternary GEMV set, 210 matrices, 521011200 plane bytes, batch 1",
+        "kernel_source_sha256": kernel_source_hash(),
+        "kernel_sources": rel(KERNEL_SRCS),
+        "fetch_size_kib_per_dispatch": round(gf, 1),
+        "write_size_kib_per_dispatch": round(gw, 1),
+        "fetch_scale": round(fetch_scale, 5),
+        "write_scale": round(write_scale, 5),
+        "calibration": cal,
+        "traffic_bytes_per_launch": int(round(gf * 1024 * fetch_scale + gw * 1024 * write_scale)),
+        "algorithmic_bytes_per_launch": {"planes": 521011200, "activations": 668160, "outputs_i32_f32": 5468160},
+    }
+    bf = statistics.median(_per_dispatch(fr, "gemv_bitcos_kernel", "FETCH_SIZE"))
+    bw = statistics.median(_per_dispatch(wr, "gemv_bitcos_kernel", "WRITE_SIZE"))
+    sq = {c: statistics.median(_per_dispatch(br, "gemv_bitcos_kernel", c))
+          for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES")}
+    bitcos = {
+        "kernel": "gemv_bitcos_kernel",
+        "workload": "decode-step ternary GEMV set as BITCOS, 210 matrices, 415166556 bytes (presence 260505600, "
+                    "sign words 151926036, row_start 2734920), batch 1",
+        "kernel_source_sha256": kernel_source_hash(BITCOS_SRCS),
+        "kernel_sources": rel(BITCOS_SRCS),
+        "sq_insts_valu_per_launch": int(sq["SQ_INSTS_VALU"]),
+        "sq_insts_lds_per_launch": int(sq["SQ_INSTS_LDS"]),
+        "sq_lds_bank_conflict_cycles_per_launch": int(sq["SQ_LDS_BANK_CONFLICT"]),
+        "sq_waves_per_launch": int(sq["SQ_WAVES"]),
+        "fetch_size_kib_per_dispatch": round(bf, 1),
+        "write_size_kib_per_dispatch": round(bw, 1),
+        "fetch_scale": round(fetch_scale, 5),
+        "write_scale": round(write_scale, 5),
+        "traffic_bytes_per_launch": int(round(bf * 1024 * fetch_scale + bw * 1024 * write_scale)),
+        "algorithmic_bytes_per_launch": {"presence": 260505600, "sign_words": 151926036, "row_start": 2734920,
+                                         "activations": 668160, "outputs_i32_f32": 5468160},
+    }
+    for path, rec in ((out_gemv, gemv), (out_bitcos, bitcos)):
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        log(f"wrote {os.path.relpath(path, ROOT)}: {rec['traffic_bytes_per_launch']} bytes per launch")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -627,7 +713,13 @@ def main() -> int:
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, read 1 GiB with the streaming probe and rewrite 1 GiB with the cache "
                          "flush (3 times each): kernels of known traffic for scaling hardware byte counters")
+    ap.add_argument("--write-counter-records", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BITCOS_SQ_DIR"),
+                    help="no GPU: write the committed counter records from three rocprofv3 counter runs of this "
+                         "file (see write_counter_records) and exit")
     args = ap.parse_args()
+    if args.write_counter_records:
+        write_counter_records(*args.write_counter_records)
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
