@@ -1103,7 +1103,7 @@ SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
 // beats per row); its tables: one TokJob per job, tiles as the batch-1 plan cuts them (rows per tile
 // capped at kTokTileRows), the same bound for the XCD runs.
 namespace {
-constexpr int32_t kTokAutoMax = 3;  // AUTO: tokens per call the token kernel serves faster than the matrix cores
+constexpr int32_t kTokAutoMax = 2;  // AUTO: tokens per call the token kernel serves faster than the matrix cores
 bool tok_shape(const bpw_dev_mat &m) { return m.bpr == 40 || m.bpr == 108; }
 
 bool tok_ok(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
@@ -1212,9 +1212,10 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
         *out = plan;
         return BPW_OK;
     }
-    // Measured on the decode-step set (three HBM copies in rotation): the token kernel takes 114.7 us
-    // at B = 2 (matrix cores 151.5), 149.3 at B = 3, 188.3 at B = 4 (matrix cores 158.6): each token
-    // adds ~36 us of select work and plane reads. AUTO therefore sends 2 and 3 tokens to it.
+    // Measured on the decode-step set (three HBM copies in rotation): the token kernel takes 109.2 us
+    // at B = 2 (matrix cores 125.7) and 142.8 at B = 3 (matrix cores about 128): each token adds ~35 us
+    // of select work and plane reads, while the matrix cores' time barely grows with B. AUTO therefore
+    // sends only 2 tokens to it.
     const bool tok_auto = kernel == BPW_KERNEL_AUTO && batch <= kTokAutoMax && tok_ok(jobs, n_jobs, batch);
     if (tok_auto || (kernel == BPW_KERNEL_BITSERIAL && batch > 1)) {
         // each beat streamed once and reduced against every token's planes on the VALU

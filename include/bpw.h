@@ -316,7 +316,7 @@ size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jo
  * batch 1 the bit-serial batch-1 grouped GEMV and at batch 2 to 4 the bit-serial token kernel (every
  * beat streamed once and reduced against each token's bit planes), which serves matrices of 2497 to
  * 2560 or 6849 to 6912 columns only (else BPW_E_UNSUPPORTED); BPW_KERNEL_AUTO picks the batch-1 GEMV
- * at batch 1, the token kernel at batch 2 and 3 where every job has such a width, the matrix cores
+ * at batch 1, the token kernel at batch 2 where every job has such a width, the matrix cores
  * otherwise. All give the same integers and floats, bit for bit. Other kernels are
  * BPW_E_UNSUPPORTED. 1 <= batch <= 64.
  * The X buffers are read as they are when a run executes; the scales are the ones given here. The
