@@ -119,6 +119,7 @@ __global__ __launch_bounds__(kSBThreads) void gemm_small_batch_kernel(SmallBatch
 // l, register r holds row 4 * (l / 16) + r, token l % 16.
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRows = 16;    // rows per workgroup
 constexpr int kMfmaTokens = 16;  // tokens per workgroup
@@ -247,34 +248,33 @@ __device__ __forceinline__ u32x4 load_beat_cached(__amdgpu_buffer_rsrc_t r, uint
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// The decode table of the grouped launch in kLutCopies copies: entry e of copy c is the LDS word
-// kLutCopies e + c, and lane l reads copy l % kLutCopies, so the lanes of a wave spread their lookups
-// over the banks whatever entries they ask for (with one shared copy the random entries of a wave's
+// The decode table of the grouped launch in kLutCopies = 32 copies: entry e is a 256-byte LDS row whose
+// first 128 bytes hold its copies (copy c at e * 256 + 4 c) and whose last 128 bytes hold activation
+// operands (see op_base). Lane l reads copy l % 32, so the 32 lanes the LDS serves together hit 32
+// different banks whatever entries they ask for (with one shared copy the random entries of a wave's
 // lookups collided: 3.1 bank conflicts per lookup, measured).
 constexpr int kLutCopies = 32;
-constexpr int kLutBytes = 256 * kLutCopies * 4;
-static_assert(kLutCopies == 32 || kLutCopies == 64, "table copies: 32 or 64");
+constexpr int kLutRowBytes = 256;
+constexpr int kLutBytes = 256 * kLutRowBytes;  // address span of the table; half of it is operands
 
 __device__ __forceinline__ void fill_lut_copies(uint32_t *lut, int nthreads) {
-    u32x4 *l4 = reinterpret_cast<u32x4 *>(lut);
-    for (int i = (int)threadIdx.x; i < kLutBytes / 16; i += nthreads) {
+    uint8_t *base = reinterpret_cast<uint8_t *>(lut);
+    for (int i = (int)threadIdx.x; i < 256 * (kLutCopies / 4); i += nthreads) {
         const uint32_t v = lut_entry((uint32_t)i / (kLutCopies / 4));
-        l4[i] = u32x4{v, v, v, v};
+        *reinterpret_cast<u32x4 *>(base + (i / (kLutCopies / 4)) * kLutRowBytes + (i % (kLutCopies / 4)) * 16) =
+            u32x4{v, v, v, v};
     }
 }
 
 // This lane's constant part of a table address (see lut_addr).
-__device__ __forceinline__ uint32_t lut_lane_bits(int lane) {
-    return kLutCopies == 64 ? (uint32_t)lane << 2 : (uint32_t)(lane & 31) << 3;
-}
+__device__ __forceinline__ uint32_t lut_lane_bits(int lane) { return (uint32_t)(lane % kLutCopies) << 2; }
 
-// LDS byte address of the entry named by byte k of w, in this lane's copy: e * 4 kLutCopies + 4 (lane %
-// kLutCopies). One v_perm_b32 places byte k of w in byte 1 and the lane bits in byte 0 (selectors 4 + k
-// and 0; 0x0C gives zero bytes 2 and 3): e << 8 | lane << 2 for 64 copies; for 32 copies the lane bits
-// are (lane % 32) << 3 and the result is halved, e << 7 | (lane % 32) << 2. Below kLutBytes for any input.
+// LDS byte address of the entry named by byte k of w, in this lane's copy: e * 256 + 4 (lane % 32). One
+// v_perm_b32 places byte k of w in byte 1 and the lane bits in byte 0 (selectors 4 + k and 0; 0x0C gives
+// zero bytes 2 and 3), which is the address itself. Below kLutBytes for any input. (With the copies
+// packed 128 bytes apart, each address needed a shift as well: 64 of a step's 201 VALU.)
 __device__ __forceinline__ uint32_t lut_addr(uint32_t w, int k, uint32_t lane_bits) {
-    const uint32_t a = __builtin_amdgcn_perm(w, lane_bits, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
-    return kLutCopies == 64 ? a : a >> 1;
+    return __builtin_amdgcn_perm(w, lane_bits, 0x0C0C0000u | ((4u + (uint32_t)k) << 8));
 }
 
 __device__ __forceinline__ int lut_at(const uint32_t *lut, uint32_t addr) {
@@ -325,28 +325,44 @@ __device__ __forceinline__ u32x4 step_second(const u32x4 &r0, const u32x4 &r1, b
     return u32x4{swap8(t.x), swap8(t.y), swap8(t.z), swap8(t.w)};
 }
 
-// The activation operands (see sb_act_operands_kernel) of up to kXtPassSteps steps sit in LDS: the
-// matrix-core operand of quarter q of iteration i is the KiB at (4 i + q) KiB, lane l's 16 bytes at 16 l,
-// read with one conflict-free ds_read_b128. Loading them from memory instead, each step's eight operand
-// loads went through the same address path as the weights: the texture address unit stayed 67-76 %
-// busy (counters) while the weights moved at less than half the batch-1 rate.
-constexpr int kXtPassSteps = 6;  // 48 KiB: table + one pass = 80 KiB, two workgroups per compute unit
-constexpr int kXtStepBytes = 8192;  // 2 iterations x 4 quarters x 64 lanes x 16 bytes
+// The activation operands (see sb_act_operands_kernel) of up to kXtPassSteps steps sit in LDS. Loading
+// them from memory instead, each step's eight operand loads went through the same address path as the
+// weights: the texture address unit stayed 67-76 % busy (counters) while the weights moved at less than
+// half the batch-1 rate. Operand j = 4 h + q of a step (quarter q of the step's iteration h) is 1 KiB,
+// 16 bytes per lane, placed as eight 128-byte pieces 256 bytes apart:
+//   op_base(ls) + 2048 j + lane_off(l),   lane_off(l) = 256 (l / 8) + 16 (l % 8)
+// so that steps 0-3 of a pass fill the free halves of the table's rows (op_base = 16 KiB ls + 128 in the
+// table) and steps 4-5 the two halves of a 16 KiB region after it. Eight lanes read one 128-byte piece:
+// each ds_read_b128 stays conflict-free.
+constexpr int kXtPassSteps = 6;       // 48 KiB of operands per pass
+constexpr int kXtStepBytes = 8192;    // 2 iterations x 4 quarters x 64 lanes x 16 bytes
 constexpr int kXtPassBytes = kXtPassSteps * kXtStepBytes;
+constexpr int kXtTableSteps = kLutBytes / 2 / kXtStepBytes;  // steps held in the table's free halves
+constexpr int kXtPieceStride = 2048;  // between the operands of one step
+static_assert(kXtTableSteps == 4 && kXtPassSteps - kXtTableSteps == 2, "two steps in the region after the table");
+
+__device__ __forceinline__ uint32_t lane_off(int lane) { return (uint32_t)(lane >> 3) * 256u + (uint32_t)(lane & 7) * 16u; }
+
+// The first operand's 128-byte piece of step ls (0 <= ls < kXtPassSteps) for lane 0.
+__device__ __forceinline__ uint8_t *op_base(uint32_t *lut, uint8_t *xl2, int ls) {
+    return ls < kXtTableSteps ? reinterpret_cast<uint8_t *>(lut) + 128 + ls * (kXtStepBytes * 2)
+                              : xl2 + (ls - kXtTableSteps) * 128;
+}
 
 // LDS of the grouped launch: the table in a static array (its address is then known when the kernel
 // is compiled and folds into each lookup's instruction offset; from dynamic LDS every lookup paid a
-// v_add of the base, 64 VALU per step), then one pass of operands in dynamic LDS.
-constexpr size_t kSbGroupedLds = (size_t)kXtPassBytes;
+// v_add of the base, 64 VALU per step), then the last two steps of a pass in dynamic LDS.
+constexpr size_t kSbGroupedLds = (size_t)(kXtPassSteps - kXtTableSteps) * kXtStepBytes;
 static_assert(2 * ((size_t)kLutBytes + kSbGroupedLds) <= 160 * 1024, "two workgroups per compute unit");
 
 // Copy one pass of operands (kXtPassBytes) from global memory into LDS, all threads of the workgroup,
 // every load issued before the first store, with no branch: bytes past `valid` read zeros through the
 // buffer range check and are written like the rest. (With per-lane guards on the stores, a skipped
 // store left its load unwaited and the compiler answered with a wait for every load in flight at the
-// top of the streaming loop, seen in the ISA.)
+// top of the streaming loop, seen in the ISA.) Piece p of the pass (16 bytes at 16 p in memory) is lane
+// p % 64 of operand (p / 64) % 8 of step p / 512.
 template <int NT>
-__device__ __forceinline__ void stage_operands(uint8_t *xl, const uint8_t *src, uint32_t valid) {
+__device__ __forceinline__ void stage_operands(uint32_t *lut, uint8_t *xl2, const uint8_t *src, uint32_t valid) {
     static_assert(kXtPassBytes % (NT * 16) == 0, "whole rounds of 16 bytes per thread");
     constexpr int kPer = kXtPassBytes / (NT * 16);
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src, valid);
@@ -355,7 +371,11 @@ __device__ __forceinline__ void stage_operands(uint8_t *xl, const uint8_t *src, 
     for (int k = 0; k < kPer; ++k)
         v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)k * NT + threadIdx.x) * 16u, 0, 0));
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) *reinterpret_cast<u32x4 *>(xl + ((uint32_t)k * NT + threadIdx.x) * 16u) = v[k];
+    for (int k = 0; k < kPer; ++k) {
+        const uint32_t p = (uint32_t)k * NT + threadIdx.x;
+        *reinterpret_cast<u32x4 *>(op_base(lut, xl2, (int)(p >> 9)) + ((p >> 6) & 7u) * kXtPieceStride +
+                                   lane_off((int)(p & 63u))) = v[k];
+    }
 }
 
 // Several calls in one launch. Workgroup b runs tile tiles[b]: kSBGroupRows rows x up to 16 tokens of
@@ -370,9 +390,10 @@ __device__ __forceinline__ void stage_operands(uint8_t *xl, const uint8_t *src, 
 // pass or past the matrix read zeros through the buffer range checks.
 template <int RT, int NT, int ST>
 __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_t rt0, uint32_t tok_group,
-                                                uint32_t *lut, uint8_t *xl, bool active) {
+                                                uint32_t *lut, uint8_t *xl2, bool active) {
     const int lane = threadIdx.x & 63;
     const uint32_t lb = lut_lane_bits(lane);
+    const uint32_t lo_lane = lane_off(lane);
     const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
     const int g = lane >> 4, m = lane & 15;
     const bool lo = m < 8;
@@ -408,12 +429,12 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
     // A step in two halves (its first iteration for every row tile, then its second), each with its
     // own four operands: 16 fewer registers live than reading all eight at once.
     auto step = [&](const u32x4 (&beat)[RT][2], int ls) {  // ls: the step's index within the pass
-        const uint8_t *xs = xl + (uint32_t)ls * kXtStepBytes + (uint32_t)lane * 16u;
+        const uint8_t *xs = op_base(lut, xl2, ls) + lo_lane;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 xo[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xo[q] = *reinterpret_cast<const u32x4 *>(xs + h * 4096 + q * 1024);
+            for (int q = 0; q < 4; ++q) xo[q] = *reinterpret_cast<const u32x4 *>(xs + (4 * h + q) * kXtPieceStride);
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const u32x4 p = h == 0 ? step_first(beat[t][0], beat[t][1], lo) : step_second(beat[t][0], beat[t][1], lo);
@@ -428,7 +449,7 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
         __syncthreads();  // the previous pass's operands are no longer read
         const uint32_t src = (uint32_t)s0 * kXtStepBytes;
         const uint32_t avail = A.xt_group_bytes > src ? A.xt_group_bytes - src : 0u;
-        stage_operands<NT>(xl, xt + src, avail < (uint32_t)kXtPassBytes ? avail : (uint32_t)kXtPassBytes);
+        stage_operands<NT>(lut, xl2, xt + src, avail < (uint32_t)kXtPassBytes ? avail : (uint32_t)kXtPassBytes);
         __syncthreads();  // operands (and on the first pass the table) complete
         for (int st = s0; st < s_end; st += ST) {
 #pragma unroll
@@ -445,6 +466,29 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
     const int otok = (int)tok;
     if (!active || otok >= A.batch) return;
     const float xs = A.x_scales[otok];
+    // Four consecutive rows of one token per lane: one 16-byte store per row tile and output where the
+    // rows and both outputs allow it. Stored one word at a time, the outputs cost 21 us of the decode
+    // step at 4 tokens and 45 us at 16 (measured with the stores removed): each instruction then
+    // scattered 64 single words; with 16-byte stores the step took 8 and 23 us less.
+    const bool vec = (A.rows & 3) == 0 &&
+                     (((uintptr_t)A.out_i32 | (A.out_f32 ? (uintptr_t)A.out_f32 : (uintptr_t)0)) & 15u) == 0;
+    if (vec) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+            const int orow = (int)(rt0 + t) * kMfmaRows + 4 * (lane >> 4);
+            if (orow < A.rows) {  // rows is a multiple of 4: the lane's four rows are all in, or all out
+                const int64_t idx = (int64_t)otok * A.rows + orow;
+                *reinterpret_cast<v4i *>(A.out_i32 + idx) = acc[t];
+                if (A.out_f32) {
+                    f32x4 f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) f[i] = ((float)acc[t][i] * xs) * A.w_scale;  // the scales in turn
+                    *reinterpret_cast<f32x4 *>(A.out_f32 + idx) = f;
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
 #pragma unroll

@@ -703,6 +703,34 @@ def test_small_batch_grouped(dev, batch, kernel):
     plan.free()
 
 
+@pytest.mark.parametrize("batch", (4, 16))
+def test_small_batch_grouped_unaligned_outputs(dev, batch):
+    """Outputs 4 bytes past a 16-byte boundary, rows a multiple of 4: the grouped matrix-core kernel
+    stores word by word there (16-byte stores only with 16-byte aligned outputs). Bit-exact against the
+    oracle, and the guard words on both sides of each output stay untouched."""
+    log(f"case: grouped small batch, unaligned outputs, B={batch}")
+    sets = []
+    for i, (r, c) in enumerate(((640, 2560), (256, 6912), (12, 130))):
+        case, u, Xh, Xd, sc, _, _ = _sb_inputs(dev, 950 + 7 * i + batch, r, c, batch)
+        bi = torch.full((batch * r + 2,), -7, dtype=torch.int32, device=dev)
+        bf = torch.full((batch * r + 2,), -7.0, dtype=torch.float32, device=dev)
+        oi, of = bi[1:1 + batch * r].view(batch, r), bf[1:1 + batch * r].view(batch, r)
+        assert oi.data_ptr() % 16 == 4 and of.data_ptr() % 16 == 4
+        sets.append((case, u, Xh, Xd, sc, oi, of, bi, bf))
+    jobs = [bpw.sb_job(u.m, Xd, sc, oi, of) for (case, u, Xh, Xd, sc, oi, of, bi, bf) in sets]
+    ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws, bpw.KERNEL_MFMA)
+    plan.run()
+    torch.cuda.synchronize()
+    for (case, u, Xh, Xd, sc, oi, of, bi, bf) in sets:
+        acc, y32, y64 = oracle.gemm_small_batch(oracle.pack(case.w), case.rows, case.cols, Xh, sc, case.w_scale,
+                                                nthreads=NT)
+        assert np.array_equal(oi.cpu().numpy(), acc), f"{case.rows}x{case.cols}"
+        assert np.array_equal(of.cpu().numpy().view(np.uint32), y32.view(np.uint32)), f"{case.rows}x{case.cols}"
+        assert bi[0].item() == -7 and bi[-1].item() == -7 and bf[0].item() == -7.0 and bf[-1].item() == -7.0
+    plan.free()
+
+
 TOKEN_SHAPES = ((6912, 2560), (2560, 6912), (640, 2560), (1, 2560), (7, 2500), (65, 6850), (129, 6900),
                 (1025, 2560), (3, 6912))
 
