@@ -298,7 +298,8 @@ def configs_measure(bpw, torch, dev, ds, reps: int = 30) -> dict:
     outside the timed span).
       k_proj: one 640 x 2560 matrix, 409,600 plane bytes (launch-latency dominated);
       layer: one layer's seven projections as one grouped launch (17,367,040 B), and each alone;
-      decode step as 210 single-matrix launches in stream order, for context beside the grouped one."""
+      decode step as 210 single-matrix launches in stream order, for context beside the grouped one;
+      probe_same_bytes: the plain streaming read (every shape) of the k_proj's and the layer's bytes."""
     mats = ds.copies[0][1]
 
     def plan(idx):
@@ -355,6 +356,17 @@ def configs_measure(bpw, torch, dev, ds, reps: int = 30) -> dict:
                                               "gbs": round(ds.plane_bytes / (med * 1e-6) / 1e9, 1)}
     for p, _ in singles:
         p.free()
+
+    def probe_entry(nbytes):
+        # the plain streaming read of the same bytes, every shape, hot like the plans above: the floor
+        # that a launch of this size reaches without any work of the method
+        buf = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        per = {str(sh): round(timed(lambda: bpw.bpw_stream_read_probe(buf, sink, shape=sh), False)[0], 2)
+               for sh in range(bpw.PROBE_SHAPES)}
+        return {"bytes": nbytes, "hot_us_per_shape": per, "best_hot_us": min(per.values())}
+    res["probe_same_bytes"] = {"k_proj_640x2560": probe_entry(res["k_proj_640x2560"]["bytes"]),
+                               "layer_grouped": probe_entry(layer_bytes)}
     pk.free()
     pl.free()
     del flush_buf

@@ -376,7 +376,7 @@ bpw_status bpw_bitcos_plan_create(const bpw_bitcos_job *jobs, int32_t n_jobs, vo
         hj[i] = d;
         const int64_t U = job_units(j.m);
         for (int64_t u = 0; u < U; u += bpw::kBcTileUnits)
-            ht[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + bpw::kBcTileUnits), 0};
+            ht[t++] = bpw::tile_of(i, u, std::min(U, u + bpw::kBcTileUnits));
     }
     bpw::host_xcd_layout(ht, t);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);

@@ -20,7 +20,7 @@ __global__ __launch_bounds__(kThreads) void gemv_bytelane_kernel(const DevJob *_
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Tile t = tiles[blockIdx.x];
-    const DevJob J = jobs[t.job];
+    const DevJob &J = jobs[t.job];  // read where used: the tile record feeds the first loads
     bs_dispatch<true>(J, t, wave, lane, xl, sums, &claim);
 }
 

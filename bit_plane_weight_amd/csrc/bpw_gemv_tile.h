@@ -61,22 +61,26 @@ __device__ __forceinline__ int32_t select_partial(const u32x4 *xl, const u32x4 (
         return row_partial<K, GLOG>(xl, B, g, G);
 }
 
+// The streaming part reads the job's fields from the tile record T (copies the host wrote); the job
+// record J is read for the generic geometry and the output pass only, so its load overlaps the first
+// beats.
 template <bool BL, int K, int GLOG, int NB>
-__device__ __forceinline__ void bs_tile(const DevJob &J, int u0, int u1, int wave, int lane, u32x4 *xl,
+__device__ __forceinline__ void bs_tile(const Tile &T, const DevJob &J, int wave, int lane, u32x4 *xl,
                                            int32_t *sums, uint32_t *claim) {
+    const int u0 = T.u0, u1 = T.u1;
     const int glog = GLOG >= 0 ? GLOG : J.glog;
     const int G = 1 << glog;
     const int g = lane & (G - 1);
     const int q = lane >> glog;
     const int rpi = 64 >> glog;
-    const int bpr = NB > 0 ? NB : J.bpr;
+    const int bpr = NB > 0 ? NB : T.bpr;
     const int pass_blocks = K * G;
     const int nchunk = NB > 0 ? 1 : J.nchunk;
-    const bool pair = J.pair != 0;
+    const bool pair = T.pair != 0;
     const int n = u1 - u0;
     const int V = pair ? 2 * n : n;
-    const __amdgpu_buffer_rsrc_t wr = make_rsrc(J.planes, J.plane_bytes);
-    const __amdgpu_buffer_rsrc_t wu = make_rsrc(pair ? J.planes_up : J.planes, J.plane_bytes);
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(T.planes, T.plane_bytes);
+    const __amdgpu_buffer_rsrc_t wu = make_rsrc(pair ? T.planes_up : T.planes, T.plane_bytes);
     // Row-group v's beats (v is wave-uniform, so the matrix choice is a scalar select).
     auto issue = [&](u32x4 (&B)[K], int v, int bb) {
         const bool up = v >= n;
@@ -93,9 +97,9 @@ __device__ __forceinline__ void bs_tile(const DevJob &J, int u0, int u1, int wav
         __syncthreads();  // every wave is done with the previous planes, sums and counter
         if (threadIdx.x == 0) *claim = (uint32_t)kWaves;
         if constexpr (BL)
-            stage_bytes(xl, J.x, b0, nb, wave, lane);
+            stage_bytes(xl, T.x, b0, nb, wave, lane);
         else
-            stage_planes(xl, J.x, b0, nb, wave, lane);
+            stage_planes(xl, T.x, b0, nb, wave, lane);
         __syncthreads();
         // Two register sets alternate: the loads of the next row-group leave before the current one
         // is reduced. One trip handles two row-groups with no exit in between, so every load is
@@ -151,16 +155,16 @@ __device__ __forceinline__ void bs_tile_empty(const DevJob &J, int u0, int u1, i
 template <bool BL>
 __device__ __forceinline__ void bs_dispatch(const DevJob &J, const Tile &t, int wave, int lane, u32x4 *xl,
                                             int32_t *sums, uint32_t *claim) {
-    if (J.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
-        bs_tile<BL, 5, 3, 40>(J, t.u0, t.u1, wave, lane, xl, sums, claim);
-    else if (J.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
-        bs_tile<BL, 4, 5, 108>(J, t.u0, t.u1, wave, lane, xl, sums, claim);
-    else if (J.kblk == 0)
+    if (t.bpr == 40)  // 2560-column rows: 8 lanes x 5 beats
+        bs_tile<BL, 5, 3, 40>(t, J, wave, lane, xl, sums, claim);
+    else if (t.bpr == 108)  // 6912-column rows: 32 lanes x 4 beats (108 of 128 used)
+        bs_tile<BL, 4, 5, 108>(t, J, wave, lane, xl, sums, claim);
+    else if (t.bpr == 0)
         bs_tile_empty(J, t.u0, t.u1, wave, lane);
     else if (J.kblk == 1)
-        bs_tile<BL, 1, -1, 0>(J, t.u0, t.u1, wave, lane, xl, sums, claim);
+        bs_tile<BL, 1, -1, 0>(t, J, wave, lane, xl, sums, claim);
     else
-        bs_tile<BL, 2, -1, 0>(J, t.u0, t.u1, wave, lane, xl, sums, claim);
+        bs_tile<BL, 2, -1, 0>(t, J, wave, lane, xl, sums, claim);
 }
 
 

@@ -436,12 +436,12 @@ int64_t xcd_runs(bpw::Tile *tiles, int64_t n, int X, double tail_share) {
             }
             const int64_t w = std::max<int64_t>(1, (b.u1 - b.u0 + kTailDiv - 1) / kTailDiv);
             for (int64_t u = b.u0; u < b.u1; u += w)
-                runs[(size_t)x].push_back(bpw::Tile{b.job, (int32_t)u, (int32_t)std::min<int64_t>(b.u1, u + w), 0});
+                runs[(size_t)x].push_back(bpw::tile_of(b.job, u, std::min<int64_t>(b.u1, u + w)));
         }
         s0 += len;
         longest = std::max(longest, runs[(size_t)x].size());
     }
-    const bpw::Tile pad{n > 0 ? src[0].job : 0, 1, 1, 0};
+    const bpw::Tile pad = bpw::tile_of(n > 0 ? src[0].job : 0, 1, 1);
     int64_t t = 0;
     for (size_t k = 0; k < longest; ++k)
         for (int x = 0; x < X; ++x) tiles[t++] = k < runs[(size_t)x].size() ? runs[(size_t)x][k] : pad;
@@ -747,7 +747,7 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
         // tiles of one job in row order, jobs in the order above (the whole table is then laid out per
         // XCD, below)
         const int64_t U = units_of(m.rows, g), tu = pair ? tile_units(g) / 2 : tile_units(g);
-        for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + tu), 0};
+        for (int64_t u = 0; u < U; u += tu) hb[t++] = bpw::tile_of(i, u, std::min(U, u + tu));
         if (m.rows > 0) plan->has_work = 1;  // a job without rows has no tiles (a pair: not even K)
     }
     if (t != L.n_work) {
@@ -766,6 +766,16 @@ static bpw_status create_plan(const bpw_gemv_job *jobs, int32_t n_jobs, const bp
     if (plan->n_tiles > (int64_t)INT32_MAX) {
         delete plan;
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
+    }
+    for (int64_t k = 0; k < plan->n_tiles; ++k) {  // the job fields the tile's first loads need
+        bpw::Tile &b = hb[k];
+        const bpw::DevJob &d = hj[b.job];
+        b.bpr = d.bpr;
+        b.plane_bytes = d.plane_bytes;
+        b.pair = d.pair;
+        b.planes = d.planes;
+        b.planes_up = d.planes_up;
+        b.x = d.x;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     st = hip_status(hipMemcpyAsync(d_ws, host.data(), table_bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
@@ -1240,7 +1250,7 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
             hj[i] = d;
             const Geometry g = geometry_for(j.m.bpr);
             const int64_t U = units_of(j.m.rows, g), w = tok_tile_units(g);
-            for (int64_t u = 0; u < U; u += w) hb[t++] = bpw::Tile{i, (int32_t)u, (int32_t)std::min(U, u + w), 0};
+            for (int64_t u = 0; u < U; u += w) hb[t++] = bpw::tile_of(i, u, std::min(U, u + w));
         }
         const int xccs = device_xcds();
         if (xccs > kMaxXcds) {

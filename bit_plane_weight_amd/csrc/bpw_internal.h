@@ -48,13 +48,30 @@ struct DevJob {
 };
 
 // A tile of the bit-serial GEMV: consecutive row-groups ("units" of 64 / G rows) [u0, u1) of one
-// job, at most kTileRows rows, run by one workgroup.
+// job, at most kTileRows rows, run by one workgroup. In the batch-1 GEMV's tables the tile also
+// carries copies of the job fields its first loads need (the other tables leave them zero), so that
+// the beats and the activation leave after one record load instead of two dependent ones.
 struct Tile {
     int32_t job;
     int32_t u0;
     int32_t u1;
-    int32_t pad;
+    int32_t bpr;
+    uint32_t plane_bytes;
+    int32_t pair;
+    const uint8_t *planes;
+    const uint8_t *planes_up;
+    const int8_t *x;
 };
+static_assert(sizeof(Tile) == 48, "tile records are 48 bytes");
+
+// Host side: the tile of row-groups [u0, u1) of job `job`, job fields zero.
+inline Tile tile_of(int32_t job, int64_t u0, int64_t u1) {
+    Tile t{};
+    t.job = job;
+    t.u0 = (int32_t)u0;
+    t.u1 = (int32_t)u1;
+    return t;
+}
 
 
 // Small-batch arguments (passed by value; <= kMaxBatch tokens).

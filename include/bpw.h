@@ -177,7 +177,7 @@ bpw_status bpw_gemv(const bpw_gemv_job *jobs, int32_t n_jobs, int32_t kernel, vo
  * library's own fixed device array of 1 MiB (one per GPU, held from the first call on that GPU until
  * the process ends); the call allocates no device memory and calls no allocating routine of HIP or
  * torch. The same computation, kernels and results as bpw_gemv, bit for bit. Jobs whose tables need
- * more than 1 MiB (bpw_gemv_workspace_bytes: a decode step's 210 GEMVs need 0.25 MiB) return
+ * more than 1 MiB (bpw_gemv_workspace_bytes: a decode step's 210 GEMVs need 0.70 MiB) return
  * BPW_E_SIZE and launch nothing. Every call on one GPU rewrites that GPU's array: calls may follow
  * one another on one stream (each waits for its table copy, which is ordered after the previous
  * launch), but calls that overlap on one GPU (other streams, other host threads) race on the tables.
