@@ -144,7 +144,8 @@ def prologue_measure(bpw, torch, synth, dev, ds, steps: int = 100) -> dict:
     """The decode step with its activation prep: the Folded quantiser turns each job's float32
     residual h and gain g (seeded: h ~ N(0, 1), g ~ U(0.5, 1.5)) into the job's int8 codes and a
     device-resident scale, then the grouped GEMV reads both. One quantiser launch (210 jobs) plus one
-    GEMV launch per step, timed back to back between HIP events."""
+    GEMV launch per step, timed back to back between HIP events. Beside it, the plain streaming read of
+    the quantiser's input bytes, timed the same way."""
     import numpy as np
     qjobs, scales, keep = [], [], []
     for i, ((layer, proj, name, rows, cols), (x, _)) in enumerate(zip(ds.shapes, ds.xs)):
@@ -182,8 +183,22 @@ def prologue_measure(bpw, torch, synth, dev, ds, steps: int = 100) -> dict:
     for p, _ in plans:
         p.free()
     qplan.free()
+    # the plain streaming read of the quantiser's input bytes (h and g), every shape, timed the same way
+    read_bytes = int(sum(8 * c[4] for c in ds.shapes))
+    buf = torch.zeros(read_bytes, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    probe = {}
+    for sh in range(bpw.PROBE_SHAPES):
+        settle(torch, lambda: bpw.bpw_stream_read_probe(buf, sink, shape=sh))
+        a.record()
+        for i in range(steps):
+            bpw.bpw_stream_read_probe(buf, sink, shape=sh)
+        b.record()
+        torch.cuda.synchronize()
+        probe[str(sh)] = round(a.elapsed_time(b) / steps * 1e3, 2)
     return {"quantise_us": round(q_us, 2), "decode_step_with_quantise_us": round(step_us, 2),
-            "quantised_values": int(sum(c[4] for c in ds.shapes))}
+            "quantised_values": int(sum(c[4] for c in ds.shapes)),
+            "probe_same_read_bytes": {"bytes": read_bytes, "us_per_shape": probe, "best_us": min(probe.values())}}
 
 
 def intmlp_measure(bpw, torch, dev, ds, steps: int = 100) -> dict:
