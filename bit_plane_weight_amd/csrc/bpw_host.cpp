@@ -1016,8 +1016,6 @@ struct bpw_sb_plan {
     const bpw::SmallBatchArgs *jobs;
     const bpw::SBTile *tiles;
     int64_t n_tiles;
-    const bpw::XTile *xtiles;  // the activation-operand pieces the launch writes first
-    int64_t n_xtiles;
     bpw_gemv_plan *gemv;  // batch 1 under AUTO: the batch-1 grouped GEMV over the same jobs
     // 2 to 4 tokens on the bit-serial kernel: its job and tile tables (n_tok_tiles > 0)
     const bpw::TokJob *tok_jobs;
@@ -1028,16 +1026,10 @@ struct bpw_sb_plan {
 
 namespace {
 struct SBLayout {
-    size_t jobs_off, tiles_off, xtiles_off, xt_off, total;
-    int64_t n_tiles, n_xtiles;
+    size_t jobs_off, tiles_off, total;
+    int64_t n_tiles;
 };
 
-// Iterations (4 blocks each) of one small-batch job, and the bytes of its activation operands per token
-// group (4 KiB per iteration).
-inline int64_t sb_iterations(int64_t bpr) { return (bpr + 3) / 4; }
-
-// The grouped matrix-core launch's workspace: job records, tile table, the table of activation-operand
-// pieces, then each job's activation operands (token groups x iterations x 4 KiB, 256-byte aligned).
 // Tiles of a grouped small-batch job per token group: kSBGroupRows rows each.
 inline int64_t sb_job_tiles(const bpw_sb_job &j) { return (j.m.rows + bpw::kSBGroupRows - 1) / bpw::kSBGroupRows; }
 
@@ -1090,21 +1082,15 @@ int64_t sb_cost_runs(bpw::SBTile *tiles, int64_t n, int X, const bpw_sb_job *job
     return t;
 }
 
+// The grouped matrix-core launch's workspace: job records, then the tile table with room for the
+// cost-balanced XCD runs padded to one length (sb_cost_runs).
 SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
     SBLayout L{};
     const int64_t groups = (batch + 15) / 16;
-    size_t xt_bytes = 0;
-    for (int32_t i = 0; i < n; ++i) {
-        L.n_tiles += sb_job_tiles(jobs[i]) * groups;
-        L.n_xtiles += sb_iterations(jobs[i].m.bpr) * groups;
-        xt_bytes += align_up((size_t)(sb_iterations(jobs[i].m.bpr) * groups) * 4096u);
-    }
+    for (int32_t i = 0; i < n; ++i) L.n_tiles += sb_job_tiles(jobs[i]) * groups;
     L.jobs_off = 0;
-    // room for the cost-balanced XCD runs padded to one length (sb_cost_runs)
     L.tiles_off = align_up(sizeof(bpw::SmallBatchArgs) * (size_t)n);
-    L.xtiles_off = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)sb_tile_bound(L.n_tiles));
-    L.xt_off = align_up(L.xtiles_off + sizeof(bpw::XTile) * (size_t)L.n_xtiles);
-    L.total = align_up(L.xt_off + xt_bytes);
+    L.total = align_up(L.tiles_off + sizeof(bpw::SBTile) * (size_t)sb_tile_bound(L.n_tiles));
     return L;
 }
 }  // namespace
@@ -1113,7 +1099,6 @@ SBLayout sb_layout(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
 // beats per row); its tables: one TokJob per job, tiles as the batch-1 plan cuts them (rows per tile
 // capped at kTokTileRows), the same bound for the XCD runs.
 namespace {
-constexpr int32_t kTokAutoMax = 2;  // AUTO: tokens per call the token kernel serves faster than the matrix cores
 bool tok_shape(const bpw_dev_mat &m) { return m.bpr == 40 || m.bpr == 108; }
 
 bool tok_ok(const bpw_sb_job *jobs, int32_t n, int32_t batch) {
@@ -1194,7 +1179,7 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
         if (st) return st;
     }
     const SBLayout L = sb_layout(jobs, n_jobs, batch);
-    if (L.n_tiles > (int64_t)INT32_MAX || L.n_xtiles > (int64_t)INT32_MAX)
+    if (L.n_tiles > (int64_t)INT32_MAX)
         return fail(BPW_E_UNSUPPORTED, "too many tiles for one launch");
     const size_t need = bpw_gemm_small_batch_workspace_bytes(jobs, n_jobs, batch);
     if (n_jobs > 0 && need > ws_len) return fail(BPW_E_SIZE, "workspace %zu bytes < required %zu", ws_len, need);
@@ -1211,8 +1196,6 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
     plan->jobs = reinterpret_cast<const bpw::SmallBatchArgs *>(ws + L.jobs_off);
     plan->tiles = reinterpret_cast<const bpw::SBTile *>(ws + L.tiles_off);
     plan->n_tiles = L.n_tiles;
-    plan->xtiles = reinterpret_cast<const bpw::XTile *>(ws + L.xtiles_off);
-    plan->n_xtiles = L.n_xtiles;
     plan->gemv = nullptr;
     plan->tok_jobs = nullptr;
     plan->tok_tiles = nullptr;
@@ -1222,12 +1205,10 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
         *out = plan;
         return BPW_OK;
     }
-    // Measured on the decode-step set (three HBM copies in rotation): the token kernel takes 109.2 us
-    // at B = 2 (matrix cores 125.7) and 142.8 at B = 3 (matrix cores about 128): each token adds ~35 us
-    // of select work and plane reads, while the matrix cores' time barely grows with B. AUTO therefore
-    // sends only 2 tokens to it.
-    const bool tok_auto = kernel == BPW_KERNEL_AUTO && batch <= kTokAutoMax && tok_ok(jobs, n_jobs, batch);
-    if (tok_auto || (kernel == BPW_KERNEL_BITSERIAL && batch > 1)) {
+    // The token kernel only when pinned: measured on the decode-step set (three HBM copies in
+    // rotation) it takes 107.6 us at B = 2 and 142.8 at B = 3, each token adding ~35 us of select work
+    // and plane reads, against 102.7 and 107.4 on the matrix cores, whose time barely grows with B.
+    if (kernel == BPW_KERNEL_BITSERIAL && batch > 1) {
         // each beat streamed once and reduced against every token's planes on the VALU
         const SBLayout T = tok_layout(jobs, n_jobs);
         std::vector<uint8_t> host(T.total, 0);
@@ -1285,23 +1266,14 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
         *out = plan;
         return BPW_OK;
     }
-    // the tables only: the activation operands behind them are written by every run
-    std::vector<uint8_t> host(L.xt_off, 0);
+    std::vector<uint8_t> host(L.total, 0);
     auto *hj = reinterpret_cast<bpw::SmallBatchArgs *>(host.data() + L.jobs_off);
     auto *ht = reinterpret_cast<bpw::SBTile *>(host.data() + L.tiles_off);
-    auto *hx = reinterpret_cast<bpw::XTile *>(host.data() + L.xtiles_off);
     const int32_t groups = (batch + 15) / 16;
-    int64_t t = 0, tx = 0;
-    size_t xt = L.xt_off;
+    int64_t t = 0;
     for (int32_t i = 0; i < n_jobs; ++i) {
         const bpw_sb_job &j = jobs[i];
         hj[i] = small_batch_args(&j.m, j.d_X, batch, j.ldx, j.x_scales, j.d_out_i32, j.d_out_f32);
-        const int64_t its = sb_iterations(j.m.bpr);
-        hj[i].xt = ws + xt;
-        hj[i].xt_group_bytes = (uint32_t)(its * 4096);
-        xt += align_up((size_t)(its * groups) * 4096u);
-        for (int32_t gq = 0; gq < groups; ++gq)
-            for (int64_t it = 0; it < its; ++it) hx[tx++] = bpw::XTile{i, gq, (int32_t)it, 0};
         for (int64_t r = 0; r < sb_job_tiles(j); ++r)
             for (int32_t gq = 0; gq < groups; ++gq) ht[t++] = bpw::SBTile{i, (int32_t)r, gq, 1};
     }
@@ -1313,7 +1285,7 @@ bpw_status bpw_gemm_small_batch_plan_create(const bpw_sb_job *jobs, int32_t n_jo
     }
     plan->n_tiles = sb_cost_runs(ht, t, xccs, jobs, sb_tile_bound(t));
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    st = hip_status(hipMemcpyAsync(d_ws, host.data(), L.xt_off, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
+    st = hip_status(hipMemcpyAsync(d_ws, host.data(), L.total, hipMemcpyHostToDevice, s), "hipMemcpyAsync");
     if (!st) st = hip_status(hipStreamSynchronize(s), "hipStreamSynchronize");
     if (st) {
         delete plan;
@@ -1335,8 +1307,7 @@ bpw_status bpw_gemm_small_batch_plan_run(const bpw_sb_plan *plan, void *stream) 
         return hip_status(bpw::launch_gemv_tokens(plan->tok_jobs, plan->tok_tiles, (int32_t)plan->n_tok_tiles, plan->nt,
                                                   stream),
                           "grouped small batch (bit-serial tokens) launch");
-    return hip_status(bpw::launch_gemm_small_batch_grouped(plan->jobs, plan->tiles, (int32_t)plan->n_tiles,
-                                                           plan->xtiles, (int32_t)plan->n_xtiles, stream),
+    return hip_status(bpw::launch_gemm_small_batch_grouped(plan->jobs, plan->tiles, (int32_t)plan->n_tiles, stream),
                       "grouped small batch launch");
 }
 

@@ -89,20 +89,6 @@ struct SmallBatchArgs {
     int32_t tg;               // tokens per workgroup (<= kSBMaxTokens)
     float w_scale;
     float x_scales[kMaxBatch];
-    // grouped matrix-core launch only: the activation operands in the order the matrix cores read them,
-    // written by the launch's first kernel: [token group][iteration][quarter][lane] x 16 bytes
-    uint8_t *xt;
-    uint32_t xt_group_bytes;  // bytes of one token group: iterations x 4 KiB
-    int32_t pad;
-};
-
-// One 4 KiB piece of the activation operands of the grouped matrix-core launch: iteration `it` (4
-// blocks) of token group `tg` of call `job`.
-struct XTile {
-    int32_t job;
-    int32_t tg;
-    int32_t it;
-    int32_t pad;
 };
 
 // A tile of the grouped small-batch launch: rows kSBGroupRows * row_tile .. +kSBGroupRows-1 and tokens
@@ -201,8 +187,7 @@ int launch_gemv_bytelane(const DevJob *jobs, const Tile *tiles, int32_t n_tiles,
 int launch_gemv_bitserial(const DevJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_gemm_small_batch(const SmallBatchArgs &a, int32_t row_wgs, int32_t token_groups, void *stream);
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream);
-int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles,
-                                    const XTile *xtiles, int32_t n_xtiles, void *stream);
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream);
 int launch_gemv_tokens(const TokJob *jobs, const Tile *tiles, int32_t n_tiles, int32_t nt, void *stream);
 int launch_gemv_bitcos(const BitcosJob *jobs, const Tile *tiles, int32_t n_tiles, void *stream);
 int launch_dense_head(const uint16_t *w, int64_t rows, int64_t cols, const uint16_t *x, float *y, void *stream);

@@ -325,18 +325,19 @@ __device__ __forceinline__ u32x4 step_second(const u32x4 &r0, const u32x4 &r1, b
     return u32x4{swap8(t.x), swap8(t.y), swap8(t.z), swap8(t.w)};
 }
 
-// The activation operands (see sb_act_operands_kernel) of up to kXtPassSteps steps sit in LDS. Loading
-// them from memory instead, each step's eight operand loads went through the same address path as the
-// weights: the texture address unit stayed 67-76 % busy (counters) while the weights moved at less than
-// half the batch-1 rate. Operand j = 4 h + q of a step (quarter q of the step's iteration h) is 1 KiB,
-// 16 bytes per lane, placed as eight 128-byte pieces 256 bytes apart:
+// The activation operands of up to kXtPassSteps steps sit in LDS: the matrix-core operand of quarter q
+// of iteration h of a step is, in lane l = 16 g + n, codes 16 q .. 16 q + 15 of block 4 h + g of the
+// step (8 blocks) of token n of the workgroup's token group. Loading them from memory in that order
+// instead, each step's eight operand loads went through the same address path as the weights: the
+// texture address unit stayed 67-76 % busy (counters) while the weights moved at less than half the
+// batch-1 rate. Operand j = 4 h + q of a step is 1 KiB, 16 bytes per lane, placed as eight 128-byte
+// pieces 256 bytes apart:
 //   op_base(ls) + 2048 j + lane_off(l),   lane_off(l) = 256 (l / 8) + 16 (l % 8)
 // so that steps 0-3 of a pass fill the free halves of the table's rows (op_base = 16 KiB ls + 128 in the
 // table) and steps 4-5 the two halves of a 16 KiB region after it. Eight lanes read one 128-byte piece:
 // each ds_read_b128 stays conflict-free.
-constexpr int kXtPassSteps = 6;       // 48 KiB of operands per pass
+constexpr int kXtPassSteps = 6;       // 48 KiB of operands per pass (16 token slots)
 constexpr int kXtStepBytes = 8192;    // 2 iterations x 4 quarters x 64 lanes x 16 bytes
-constexpr int kXtPassBytes = kXtPassSteps * kXtStepBytes;
 constexpr int kXtTableSteps = kLutBytes / 2 / kXtStepBytes;  // steps held in the table's free halves
 constexpr int kXtPieceStride = 2048;  // between the operands of one step
 static_assert(kXtTableSteps == 4 && kXtPassSteps - kXtTableSteps == 2, "two steps in the region after the table");
@@ -355,26 +356,44 @@ __device__ __forceinline__ uint8_t *op_base(uint32_t *lut, uint8_t *xl2, int ls)
 constexpr size_t kSbGroupedLds = (size_t)(kXtPassSteps - kXtTableSteps) * kXtStepBytes;
 static_assert(2 * ((size_t)kLutBytes + kSbGroupedLds) <= 160 * 1024, "two workgroups per compute unit");
 
-// Copy one pass of operands (kXtPassBytes) from global memory into LDS, all threads of the workgroup,
-// every load issued before the first store, with no branch: bytes past `valid` read zeros through the
-// buffer range check and are written like the rest. (With per-lane guards on the stores, a skipped
-// store left its load unwaited and the compiler answered with a wait for every load in flight at the
-// top of the streaming loop, seen in the ISA.) Piece p of the pass (16 bytes at 16 p in memory) is lane
-// p % 64 of operand (p / 64) % 8 of step p / 512.
+// One pass of the call's activation operands (the steps s0 .. s0 + kXtPassSteps - 1), read from X
+// itself by all threads of the workgroup. Piece c of the pass is token n = c / kPassPieces of the
+// workgroup's token group and 16-byte piece k = c % kPassPieces of that token's columns in the pass
+// (block 8 s0 + k / 4 of the row, codes 16 (k % 4) .. +15), so consecutive threads read consecutive
+// 16 bytes of one token's row; the piece goes to operand j = 4 ((k / 16) % 2) + k % 4 of local step
+// k / 32, lane 16 ((k / 4) % 4) + n. Rounds that hold only tokens past the batch are skipped: those
+// lanes' operands keep whatever LDS held, and only their own output columns, never stored, depend on
+// them. Pieces past the row's blocks or past the batch read zeros through the buffer range check.
+// Every load of a round is issued before the first LDS write. (A separate launch that wrote the
+// operands out in the matrix cores' order first cost 5.9-6.4 us per run on the decode-step set, and
+// 10.7 MB of writes.)
+constexpr int kPassPieces = kXtPassSteps * 8 * 4;  // 16-byte pieces of one token's columns in a pass
+
 template <int NT>
-__device__ __forceinline__ void stage_operands(uint32_t *lut, uint8_t *xl2, const uint8_t *src, uint32_t valid) {
-    static_assert(kXtPassBytes % (NT * 16) == 0, "whole rounds of 16 bytes per thread");
-    constexpr int kPer = kXtPassBytes / (NT * 16);
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src, valid);
-    u32x4 v[kPer];
+__device__ __forceinline__ void stage_x(uint32_t *lut, uint8_t *xl2, const SmallBatchArgs &A, int tok0, int s0) {
+    static_assert((kMfmaTokens * kPassPieces) % NT == 0, "whole rounds");
+    constexpr int kRounds = kMfmaTokens * kPassPieces / NT;
+    const int real = min(kMfmaTokens, A.batch - tok0) * kPassPieces;  // pieces of tokens inside the batch
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(A.X, A.x_bytes);
+    u32x4 v[kRounds];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k)
-        v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((uint32_t)k * NT + threadIdx.x) * 16u, 0, 0));
+    for (int r = 0; r < kRounds; ++r) {
+        if (r * NT >= real) break;  // uniform over the workgroup
+        const int c = r * NT + (int)threadIdx.x;
+        const int n = c / kPassPieces, k = c - n * kPassPieces;
+        const int b = 8 * s0 + (k >> 2);
+        const bool in = c < real && b < A.bpr;
+        const uint32_t off = (uint32_t)((int64_t)(tok0 + n) * A.ldx + 64 * b + 16 * (k & 3));
+        v[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, in ? off : kOutOfRange, 0, 0));
+    }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-        const uint32_t p = (uint32_t)k * NT + threadIdx.x;
-        *reinterpret_cast<u32x4 *>(op_base(lut, xl2, (int)(p >> 9)) + ((p >> 6) & 7u) * kXtPieceStride +
-                                   lane_off((int)(p & 63u))) = v[k];
+    for (int r = 0; r < kRounds; ++r) {
+        if (r * NT >= real) break;
+        const int c = r * NT + (int)threadIdx.x;
+        const int n = c / kPassPieces, k = c - n * kPassPieces;
+        const int bl = k >> 2;  // block within the pass
+        *reinterpret_cast<u32x4 *>(op_base(lut, xl2, bl >> 3) + (4 * ((bl >> 2) & 1) + (k & 3)) * kXtPieceStride +
+                                   lane_off(16 * (bl & 3) + n)) = v[r];
     }
 }
 
@@ -399,7 +418,6 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
     const bool lo = m < 8;
     const int bpr = A.bpr;
     const int n_steps = (bpr + 7) / 8;
-    const uint8_t *xt = A.xt + (size_t)tok_group * A.xt_group_bytes;
     const __amdgpu_buffer_rsrc_t wr = make_rsrc(A.planes, A.plane_bytes);
     uint32_t row[RT][2];
     bool live[RT][2];
@@ -447,9 +465,7 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
 #pragma unroll
         for (int k = 0; k + 1 < ST; ++k) issue(bb[k], s0 + k);
         __syncthreads();  // the previous pass's operands are no longer read
-        const uint32_t src = (uint32_t)s0 * kXtStepBytes;
-        const uint32_t avail = A.xt_group_bytes > src ? A.xt_group_bytes - src : 0u;
-        stage_operands<NT>(lut, xl2, xt + src, avail < (uint32_t)kXtPassBytes ? avail : (uint32_t)kXtPassBytes);
+        stage_x<NT>(lut, xl2, A, (int)(tok_group * kMfmaTokens), s0);
         __syncthreads();  // operands (and on the first pass the table) complete
         for (int st = s0; st < s_end; st += ST) {
 #pragma unroll
@@ -519,24 +535,6 @@ __global__ __launch_bounds__(64 * kSBGroupWaves) void gemm_small_batch_mfma_grou
                                                                  active);
 }
 
-// The activation operands of the grouped launch, in the order its matrix cores read them: piece (i, q, l)
-// of token group tg is the 16 bytes lane l = 16 g + n feeds as quarter q of iteration i: codes 16 q ..
-// 16 q + 15 of block 4 i + g of token 16 tg + n (zero past the batch or past the row). Each workgroup
-// writes one iteration (4 KiB); the main kernel copies them into LDS contiguously. Gathered from X by
-// the main kernel's own loads (64 scattered 16-byte pieces per instruction), the operand loads alone took
-// 137 us at 2 tokens and 261 us at 16 on the decode-step set (measured with the weight work removed),
-// against 78 us for the weight stream.
-__global__ __launch_bounds__(256) void sb_act_operands_kernel(const SmallBatchArgs *__restrict__ jobs,
-                                                              const XTile *__restrict__ xtiles) {
-    const XTile x = xtiles[blockIdx.x];
-    const SmallBatchArgs &A = jobs[x.job];
-    const int t = threadIdx.x, q = t >> 6, l = t & 63, n = l & 15, g = l >> 4;
-    const int tok = 16 * x.tg + n, b = 4 * x.it + g;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (tok < A.batch && b < A.bpr) v = *reinterpret_cast<const u32x4 *>(A.X + (int64_t)tok * A.ldx + 64 * b + 16 * q);
-    *reinterpret_cast<u32x4 *>(A.xt + (size_t)x.tg * A.xt_group_bytes + ((size_t)(4 * x.it + q) * 64 + l) * 16) = v;
-}
-
 // ------------------------------------------------------------------------------------------
 // Launcher.
 
@@ -551,18 +549,12 @@ int launch_gemm_small_batch_mfma(const SmallBatchArgs &a, void *stream) {
     return hipGetLastError();
 }
 
-int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles,
-                                    const XTile *xtiles, int32_t n_xtiles, void *stream) {
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *jobs, const SBTile *tiles, int32_t n_tiles, void *stream) {
     if (n_tiles <= 0) return hipSuccess;
     const size_t lds = kSbGroupedLds;
     const hipError_t ea = hipFuncSetAttribute(reinterpret_cast<const void *>(gemm_small_batch_mfma_grouped_kernel),
                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (ea != hipSuccess) return ea;
-    if (n_xtiles > 0) {
-        hipLaunchKernelGGL(sb_act_operands_kernel, dim3((unsigned)n_xtiles), dim3(256), 0, as_stream(stream), jobs, xtiles);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL(gemm_small_batch_mfma_grouped_kernel, dim3((unsigned)n_tiles), dim3(64 * kSBGroupWaves), lds,
                        as_stream(stream), jobs, tiles);
     return hipGetLastError();

@@ -308,17 +308,14 @@ typedef struct bpw_sb_plan bpw_sb_plan;
 size_t bpw_gemm_small_batch_workspace_bytes(const bpw_sb_job *jobs, int32_t n_jobs, int32_t batch);
 
 /* Check the jobs, write the job and tile tables into d_ws (256-byte aligned; the call waits for the
- * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues the work for all of them: one
- * launch, or on the matrix cores two (the first writes every job's activations into the workspace in
- * the order the matrix cores read them, 4 KiB per 4 blocks and 16 tokens, so the workspace also holds
- * those operands: bpw_gemm_small_batch_workspace_bytes counts them; runs of one plan must not overlap).
+ * copy) and return a plan; bpw_gemm_small_batch_plan_run then queues the work for all of them as one
+ * launch. The workspace holds the tables only and is not written by a run.
  * Kernels: BPW_KERNEL_MFMA, the int8 matrix cores (any batch, any shape); BPW_KERNEL_BITSERIAL, at
  * batch 1 the bit-serial batch-1 grouped GEMV and at batch 2 to 4 the bit-serial token kernel (every
  * beat streamed once and reduced against each token's bit planes), which serves matrices of 2497 to
  * 2560 or 6849 to 6912 columns only (else BPW_E_UNSUPPORTED); BPW_KERNEL_AUTO picks the batch-1 GEMV
- * at batch 1, the token kernel at batch 2 where every job has such a width, the matrix cores
- * otherwise. All give the same integers and floats, bit for bit. Other kernels are
- * BPW_E_UNSUPPORTED. 1 <= batch <= 64.
+ * at batch 1 and the matrix cores otherwise. All give the same integers and floats, bit for bit. Other
+ * kernels are BPW_E_UNSUPPORTED. 1 <= batch <= 64.
  * The X buffers are read as they are when a run executes; the scales are the ones given here. The
  * workspace, matrices, X and outputs must outlive the plan; outputs of different jobs must not
  * overlap. */

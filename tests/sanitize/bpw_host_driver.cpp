@@ -53,8 +53,7 @@ int launch_gemv_bytelane(const DevJob *, const Tile *, int32_t, void *) { unreac
 int launch_gemv_bitserial(const DevJob *, const Tile *, int32_t, void *) { unreachable("a launcher"); }
 int launch_gemm_small_batch(const SmallBatchArgs &, int32_t, int32_t, void *) { unreachable("a launcher"); }
 int launch_gemm_small_batch_mfma(const SmallBatchArgs &, void *) { unreachable("a launcher"); }
-int launch_gemm_small_batch_grouped(const SmallBatchArgs *, const SBTile *, int32_t, const XTile *, int32_t,
-                                    void *) {
+int launch_gemm_small_batch_grouped(const SmallBatchArgs *, const SBTile *, int32_t, void *) {
     unreachable("a launcher");
 }
 int launch_gemv_tokens(const TokJob *, const Tile *, int32_t, int32_t, void *) { unreachable("a launcher"); }

@@ -739,8 +739,8 @@ TOKEN_SHAPES = ((6912, 2560), (2560, 6912), (640, 2560), (1, 2560), (7, 2500), (
 @pytest.mark.parametrize("batch", (2, 3, 4))
 def test_small_batch_grouped_tokens(dev, batch, kernel):
     """2 to 4 tokens over the two model row widths (with ragged rows, ragged columns and junk past
-    cols in X): the bit-serial token kernel, under AUTO and pinned, equals the oracle and the matrix-core
-    kernel bit for bit, on two runs of one plan."""
+    cols in X): the bit-serial token kernel (pinned) and AUTO (the matrix cores) equal the oracle and
+    the single-call matrix-core kernel bit for bit, on two runs of one plan."""
     log(f"case: grouped small batch, bit-serial tokens, B={batch} kernel={kernel}")
     sets = [_sb_inputs(dev, 1200 + 13 * i + batch, r, c, batch) for i, (r, c) in enumerate(TOKEN_SHAPES)]
     jobs = [bpw.sb_job(u.m, Xd, sc, oi, of) for (case, u, Xh, Xd, sc, oi, of) in sets]
@@ -764,11 +764,11 @@ def test_small_batch_grouped_tokens(dev, batch, kernel):
     plan.free()
 
 
-def test_small_batch_grouped_tokens_decode_step(dev):
-    """The 210 matrices of a decode step at B = 2 in one launch of the token kernel (the benchmark's
-    launch), every output against the oracle."""
-    log("case: grouped small batch, decode step, B=2 (bit-serial tokens)")
-    batch = 2
+@pytest.mark.parametrize("batch,kernel", ((2, bpw.KERNEL_BITSERIAL), (4, bpw.KERNEL_AUTO), (16, bpw.KERNEL_AUTO)))
+def test_small_batch_grouped_decode_step(dev, batch, kernel):
+    """The 210 matrices of a decode step in one launch: at B = 2 on the bit-serial token kernel, at B = 4
+    and 16 on the matrix cores (AUTO; the benchmark's launches). Every output against the oracle."""
+    log(f"case: grouped small batch, decode step, B={batch} kernel={kernel}")
     sets, jobs = [], []
     for layer in range(synth.N_LAYERS):
         for c in synth.layer_cases(707, layer):
@@ -780,10 +780,10 @@ def test_small_batch_grouped_tokens_decode_step(dev):
             sets.append((c, u, X, Xd, sc, oi, of))
             jobs.append(bpw.sb_job(u.m, Xd, sc, oi, of))
     ws = torch.empty(bpw.bpw_gemm_small_batch_workspace_bytes(jobs, batch), dtype=torch.uint8, device=dev)
-    plan = bpw.SmallBatchPlan(jobs, batch, ws)
+    plan = bpw.SmallBatchPlan(jobs, batch, ws, kernel)
     plan.run()
     torch.cuda.synchronize()
-    log("  GPU done; oracle over 210 matrices x 2 tokens")
+    log(f"  GPU done; oracle over 210 matrices x {batch} tokens")
     for (c, u, X, Xd, sc, oi, of) in sets:
         acc, y32, _ = oracle.gemm_small_batch(oracle.pack(c.w), c.rows, c.cols, X, sc, c.w_scale, nthreads=NT)
         assert np.array_equal(oi.cpu().numpy(), acc), c.name
