@@ -332,17 +332,23 @@ __device__ __forceinline__ u32x4 step_second(const u32x4 &r0, const u32x4 &r1, b
 // texture address unit stayed 67-76 % busy (counters) while the weights moved at less than half the
 // batch-1 rate. Operand j = 4 h + q of a step is 1 KiB, 16 bytes per lane, placed as eight 128-byte
 // pieces 256 bytes apart:
-//   op_base(ls) + 2048 j + lane_off(l),   lane_off(l) = 256 (l / 8) + 16 (l % 8)
+//   op_base(ls) + 2048 j + lane_off(l, q),   lane_off(l, q) = 256 (l / 8) + 16 ((l ^ s) % 8),
+//   s = q + 4 ((l / 16) % 2)
 // so that steps 0-3 of a pass fill the free halves of the table's rows (op_base = 16 KiB ls + 128 in the
-// table) and steps 4-5 the two halves of a 16 KiB region after it. Eight lanes read one 128-byte piece:
-// each ds_read_b128 stays conflict-free.
+// table) and steps 4-5 the two halves of a 16 KiB region after it. Eight lanes read one 128-byte piece,
+// in some order: each ds_read_b128 stays conflict-free. The swizzle s serves the staging writes, where
+// consecutive threads hold the quarters q and block groups g = l / 16 of one token: without it the 16
+// lanes that the LDS serves at once all wrote the same 16-byte bank slot (13 M conflict cycles per
+// launch at 16 tokens).
 constexpr int kXtPassSteps = 6;       // 48 KiB of operands per pass (16 token slots)
 constexpr int kXtStepBytes = 8192;    // 2 iterations x 4 quarters x 64 lanes x 16 bytes
 constexpr int kXtTableSteps = kLutBytes / 2 / kXtStepBytes;  // steps held in the table's free halves
 constexpr int kXtPieceStride = 2048;  // between the operands of one step
 static_assert(kXtTableSteps == 4 && kXtPassSteps - kXtTableSteps == 2, "two steps in the region after the table");
 
-__device__ __forceinline__ uint32_t lane_off(int lane) { return (uint32_t)(lane >> 3) * 256u + (uint32_t)(lane & 7) * 16u; }
+__device__ __forceinline__ uint32_t lane_off(int lane, int q) {
+    return (uint32_t)(lane >> 3) * 256u + (uint32_t)((lane ^ (q | ((lane >> 2) & 4))) & 7) * 16u;
+}
 
 // The first operand's 128-byte piece of step ls (0 <= ls < kXtPassSteps) for lane 0.
 __device__ __forceinline__ uint8_t *op_base(uint32_t *lut, uint8_t *xl2, int ls) {
@@ -393,7 +399,7 @@ __device__ __forceinline__ void stage_x(uint32_t *lut, uint8_t *xl2, const Small
         const int n = c / kPassPieces, k = c - n * kPassPieces;
         const int bl = k >> 2;  // block within the pass
         *reinterpret_cast<u32x4 *>(op_base(lut, xl2, bl >> 3) + (4 * ((bl >> 2) & 1) + (k & 3)) * kXtPieceStride +
-                                   lane_off(16 * (bl & 3) + n)) = v[r];
+                                   lane_off(16 * (bl & 3) + n, k & 3)) = v[r];
     }
 }
 
@@ -412,7 +418,9 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
                                                 uint32_t *lut, uint8_t *xl2, bool active) {
     const int lane = threadIdx.x & 63;
     const uint32_t lb = lut_lane_bits(lane);
-    const uint32_t lo_lane = lane_off(lane);
+    uint32_t lo_lane[4];  // this lane's offset within each quarter's operand
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo_lane[q] = lane_off(lane, q);
     const uint32_t tok = tok_group * kMfmaTokens + (lane & 15);
     // The epilogue's inputs, loaded first: the output pointers, the weight scale, the shape and the
     // token's scale (the empty asm keeps the compiler from sinking their loads to the stores). Loaded at
@@ -458,12 +466,13 @@ __device__ __forceinline__ void mfma_wave_tiles(const SmallBatchArgs &A, uint32_
     // A step in two halves (its first iteration for every row tile, then its second), each with its
     // own four operands: 16 fewer registers live than reading all eight at once.
     auto step = [&](const u32x4 (&beat)[RT][2], int ls) {  // ls: the step's index within the pass
-        const uint8_t *xs = op_base(lut, xl2, ls) + lo_lane;
+        const uint8_t *xs = op_base(lut, xl2, ls);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 xo[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) xo[q] = *reinterpret_cast<const u32x4 *>(xs + (4 * h + q) * kXtPieceStride);
+            for (int q = 0; q < 4; ++q)
+                xo[q] = *reinterpret_cast<const u32x4 *>(xs + lo_lane[q] + (4 * h + q) * kXtPieceStride);
 #pragma unroll
             for (int t = 0; t < RT; ++t) {
                 const u32x4 p = h == 0 ? step_first(beat[t][0], beat[t][1], lo) : step_second(beat[t][0], beat[t][1], lo);
