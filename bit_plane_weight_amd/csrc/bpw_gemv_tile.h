@@ -87,6 +87,14 @@ __device__ __forceinline__ void bs_tile(const Tile &T, const DevJob &J, int wave
         const int u = u0 + (up ? v - n : v);
         issue_row<K, NB>(B, up ? wu : wr, (uint32_t)(u * rpi + q), v < V, bb, G, bpr);
     };
+    // The output pass's job fields, read once the first beats are out (the empty asm keeps the compiler
+    // from waiting for them before those beats, and from reloading them after the last barrier, where
+    // each load stood before the tile's stores).
+    int32_t rows = 0;
+    int32_t *out_i32 = nullptr;
+    float *out_f32 = nullptr;
+    const float *xs_ptr = nullptr;
+    float xs = 0.f, w_scale = 0.f;
     for (int ch = 0; ch < nchunk; ++ch) {
         const int b0 = ch * pass_blocks;
         const int nb = min(pass_blocks, bpr - b0);
@@ -94,6 +102,16 @@ __device__ __forceinline__ void bs_tile(const Tile &T, const DevJob &J, int wave
         u32x4 B0[K], B1[K];
         int v = wave;  // every wave's first row-group is fixed; the rest are claimed
         issue(B0, v, bb);
+        if (ch == 0) {
+            rows = J.rows;
+            out_i32 = J.out_i32;
+            out_f32 = J.out_f32;
+            w_scale = J.w_scale;
+            xs = J.x_scale;
+            xs_ptr = J.x_scale_ptr;  // dereferenced at the output pass: a vector load waited for here
+                                     // would wait for the beats in flight too
+            asm volatile("" : "+s"(rows), "+s"(out_i32), "+s"(out_f32), "+s"(w_scale), "+s"(xs), "+s"(xs_ptr));
+        }
         __syncthreads();  // every wave is done with the previous planes, sums and counter
         if (threadIdx.x == 0) *claim = (uint32_t)kWaves;
         if constexpr (BL)
@@ -132,9 +150,15 @@ __device__ __forceinline__ void bs_tile(const Tile &T, const DevJob &J, int wave
             if (row0 + i < J.rows) write_pair_row(J, row0 + i, sums[i], sums[nr + i]);
         if (u0 == 0 && threadIdx.x == 0) write_pair_k(J);
     } else {
-        const float xs = job_x_scale(J);
-        for (int i = threadIdx.x; i < nr; i += kThreads)
-            if (row0 + i < J.rows) write_row(J, xs, row0 + i, sums[i]);
+        if (xs_ptr) xs = *xs_ptr;  // the job's activation scale from device memory
+        for (int i = threadIdx.x; i < nr; i += kThreads) {
+            const int row = row0 + i;
+            if (row < rows) {
+                const int32_t sum = sums[i];
+                out_i32[row] = sum;
+                if (out_f32) out_f32[row] = ((float)sum * xs) * w_scale;  // each product rounded on its own
+            }
+        }
     }
 }
 
