@@ -23,7 +23,7 @@ __all__ = [
     "intmlp_job", "bpw_gemv_intmlp_workspace_bytes",
     "bpw_gemm_small_batch", "sb_job", "bpw_gemm_small_batch_workspace_bytes", "SmallBatchPlan", "quant_job", "bpw_quantize_workspace_bytes", "bpw_quantize", "QuantPlan",
     "bpw_dense_head_gemv", "bpw_stream_read_probe", "PROBE_SHAPES", "bpw_cache_flush",
-    "TritFile", "TritFormatError", "TritTensor", "bpw_fnv1a64", "TRIT_F32", "TRIT_TERNARY", "TRIT_BF16",
+    "TritFile", "TritFormatError", "TritTensor", "bpw_fnv1a64", "trit_write", "TRIT_F32", "TRIT_TERNARY", "TRIT_BF16",
     "BitcosHost", "bpw_bitcos_pack_i8", "bpw_bitcos_from_planes", "DevBitcos", "bpw_bitcos_upload", "bitcos_job",
     "bpw_bitcos_workspace_bytes", "BitcosPlan",
 ]
@@ -474,6 +474,42 @@ class TritTensor:
 def bpw_fnv1a64(data) -> int:
     buf = np.frombuffer(memoryview(data), dtype=np.uint8)
     return _lib.lib().bpw_fnv1a64(buf.ctypes.data if buf.size else None, buf.size)
+
+
+def trit_write(tensors, config: bytes = b"", with_hash: bool = True) -> bytes:
+    """bpw_trit_write: a .trit v1 container from [(name, dtype, dims, scale, data)] (name str, dtype one of
+    TRIT_F32 / TRIT_TERNARY / TRIT_BF16, dims a sequence of 1..4 ints, data a bytes-like payload: .trit
+    planes for a ternary tensor, little-endian elements otherwise). Records come out sorted by name;
+    the same tensors in any order give the same bytes. Raises TritFormatError naming the check a reader
+    would fail."""
+    arr = (_lib.BpwTritTensorIn * max(1, len(tensors)))()
+    keep = []
+    for k, (name, dtype, dims, scale, data) in enumerate(tensors):
+        nb = name.encode("utf-8") if isinstance(name, str) else bytes(name)
+        buf = np.frombuffer(memoryview(data), dtype=np.uint8)
+        keep += [nb, buf]
+        e = arr[k]
+        e.name, e.name_len, e.dtype, e.ndim = nb, len(nb), int(dtype), len(dims)
+        if len(dims) > 4:
+            raise ValueError(f"tensor {k}: {len(dims)} dims (at most 4)")
+        for j, d in enumerate(dims):
+            e.dims[j] = int(d)
+        e.scale = float(scale)
+        e.data = buf.ctypes.data if buf.size else None
+        e.byte_len = buf.size
+    cfg = bytes(config)
+    err = _lib.BpwTritErr()
+    need = ctypes.c_uint64()
+    st = _lib.lib().bpw_trit_write_size(arr, len(tensors), len(cfg), ctypes.byref(need), ctypes.byref(err))
+    if st != _lib.OK:
+        raise TritFormatError(st, _lib.lib().bpw_last_error().decode(), err)
+    out = np.empty(max(1, need.value), dtype=np.uint8)
+    written = ctypes.c_uint64()
+    st = _lib.lib().bpw_trit_write(arr, len(tensors), cfg, len(cfg), int(bool(with_hash)), out.ctypes.data,
+                                   need.value, ctypes.byref(written), ctypes.byref(err))
+    if st != _lib.OK:
+        raise TritFormatError(st, _lib.lib().bpw_last_error().decode(), err)
+    return out[: written.value].tobytes()
 
 
 class TritFile:

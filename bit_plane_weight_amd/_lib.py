@@ -32,6 +32,12 @@ class BpwTritTensor(ctypes.Structure):
                 ("data", ctypes.c_void_p)]
 
 
+class BpwTritTensorIn(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("name_len", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("ndim", ctypes.c_int32), ("dims", ctypes.c_uint32 * 4), ("scale", ctypes.c_float),
+                ("reserved", ctypes.c_uint32), ("data", ctypes.c_void_p), ("byte_len", ctypes.c_uint64)]
+
+
 class BpwDevMat(ctypes.Structure):
     _fields_ = [("d_planes", ctypes.c_void_p), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("bpr", ctypes.c_int64), ("w_scale", ctypes.c_float), ("reserved", ctypes.c_uint32),
@@ -149,6 +155,10 @@ def lib():
         "bpw_trit_stored_hash": (ctypes.c_uint64, [vp]),
         "bpw_fnv1a64": (ctypes.c_uint64, [vp, sz]),
         "bpw_trit_load": (i32, [vp, i64, ctypes.POINTER(vp), ctypes.POINTER(BpwErr)]),
+        "bpw_trit_write_size": (i32, [ctypes.POINTER(BpwTritTensorIn), i64, sz, ctypes.POINTER(ctypes.c_uint64),
+                                      ctypes.POINTER(BpwTritErr)]),
+        "bpw_trit_write": (i32, [ctypes.POINTER(BpwTritTensorIn), i64, ctypes.c_char_p, sz, i32, vp, sz,
+                                 ctypes.POINTER(ctypes.c_uint64), ctypes.POINTER(BpwTritErr)]),
         "bpw_cache_flush": (i32, [vp, sz, vp]),
         "bpw_bitcos_pack_i8": (i32, [vp, i64, i64, f32, ctypes.POINTER(vp), E]),
         "bpw_bitcos_from_planes": (i32, [vp, ctypes.POINTER(vp)]),

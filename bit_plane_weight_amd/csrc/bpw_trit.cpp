@@ -1,6 +1,6 @@
-// bpw_trit.cpp - .trit v1 container reader ("The .trit format, version 1": section 2 "File layout",
-// 2.1 "Header fields", 2.2 "Tensor record", 2.3 "Ternary payload", 2.4 "Dense payload", section 4
-// "Validation", section 6 "What a reader is allowed to assume"). Host only.
+// bpw_trit.cpp - .trit v1 container reader and writer ("The .trit format, version 1": section 2 "File
+// layout", 2.1 "Header fields", 2.2 "Tensor record", 2.3 "Ternary payload", 2.4 "Dense payload",
+// section 4 "Validation", section 6 "What a reader is allowed to assume"). Host only.
 //
 // The file is untrusted: every read is bounds-checked against the file length before it happens,
 // every size sum is overflow-checked, and every failure is a status with the check's number. Fields
@@ -411,6 +411,224 @@ bpw_status bpw_trit_load(const bpw_trit_file *f, int64_t index, bpw_host_mat **o
         return tfail(nullptr, BPW_E_INVAL, 0, -1, index, "tensor %lld is not ternary", (long long)index);
     return bpw_load(f->bytes + f->payload_start + r.offset, (size_t)r.byte_len, (int64_t)r.dims[0],
                     (int64_t)r.dims[1], r.scale, out, err);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------------------------
+// Writer. Deterministic: records sorted by name bytewise (section 2.2 asks for sorted names so that
+// conversions are byte-identical), payloads packed in that order at multiples of 64, the file ending
+// with the last tensor's bytes. Every input is checked first, each failure numbered by the reader
+// check it would trip, so that what this writes always opens and verifies.
+
+namespace {
+
+constexpr uint64_t align64(uint64_t v) { return (v + 63) / 64 * 64; }
+
+struct WriteLayout {
+    std::vector<uint32_t> order;    // caller indices in record order
+    std::vector<uint64_t> offsets;  // payload offset of each tensor, by caller index
+    uint64_t payload_start = 0;
+    uint64_t payload_len = 0;       // offset of the last record plus its byte_len
+};
+
+bool name_less(const bpw_trit_tensor_in &a, const bpw_trit_tensor_in &b) {
+    return std::lexicographical_compare(reinterpret_cast<const uint8_t *>(a.name),
+                                        reinterpret_cast<const uint8_t *>(a.name) + a.name_len,
+                                        reinterpret_cast<const uint8_t *>(b.name),
+                                        reinterpret_cast<const uint8_t *>(b.name) + b.name_len);
+}
+
+// The field checks of one tensor, in record order.
+bpw_status check_tensor_in(const bpw_trit_tensor_in &t, int64_t i, bpw_trit_err *err) {
+    if (!t.name || t.name_len < 1 || t.name_len > (int64_t)kMaxName)
+        return tfail(err, BPW_E_FORMAT, 7, -1, i, "tensor %lld: name_len %lld outside 1..1024 (or name NULL)",
+                     (long long)i, (long long)t.name_len);
+    if (!utf8_ok(reinterpret_cast<const uint8_t *>(t.name), (size_t)t.name_len))
+        return tfail(err, BPW_E_FORMAT, 7, -1, i, "tensor %lld: name is not valid UTF-8", (long long)i);
+    if (t.dtype < 0 || t.dtype > 2)
+        return tfail(err, BPW_E_FORMAT, 8, -1, i, "tensor %lld: unknown dtype %d", (long long)i, (int)t.dtype);
+    if (t.ndim < 1 || t.ndim > 4)
+        return tfail(err, BPW_E_FORMAT, 8, -1, i, "tensor %lld: ndim %d outside 1..4", (long long)i, (int)t.ndim);
+    if (t.reserved != 0)
+        return tfail(err, BPW_E_FORMAT, 8, -1, i, "tensor %lld: reserved is %u", (long long)i, t.reserved);
+    uint64_t prod = 1;
+    bool overflow = false;
+    for (int k = 0; k < t.ndim; ++k) overflow |= !mul_ok(prod, t.dims[k], prod);
+    if (overflow) return tfail(err, BPW_E_FORMAT, 9, -1, i, "tensor %lld: shape product overflows", (long long)i);
+    if (!std::isfinite(t.scale) || !(t.scale > 0.0f))
+        return tfail(err, BPW_E_FORMAT, 10, -1, i, "tensor %lld: scale %g is not finite and > 0", (long long)i,
+                     (double)t.scale);
+    uint64_t expect = 0;
+    if (t.dtype == BPW_TRIT_TERNARY) {
+        if (t.ndim != 2)
+            return tfail(err, BPW_E_FORMAT, 14, -1, i, "tensor %lld: ternary with ndim %d", (long long)i, (int)t.ndim);
+        const uint64_t bpr = ((uint64_t)t.dims[1] + 63) / 64;
+        if (!mul_ok((uint64_t)t.dims[0], bpr, expect) || !mul_ok(expect, 16, expect))
+            return tfail(err, BPW_E_FORMAT, 9, -1, i, "tensor %lld: byte count overflows", (long long)i);
+        if (t.byte_len != expect)
+            return tfail(err, BPW_E_FORMAT, 15, -1, i, "tensor %lld: byte_len %llu != rows * beats_per_row * 16 = %llu",
+                         (long long)i, (unsigned long long)t.byte_len, (unsigned long long)expect);
+    } else {
+        if (!mul_ok(prod, t.dtype == BPW_TRIT_F32 ? 4 : 2, expect))
+            return tfail(err, BPW_E_FORMAT, 9, -1, i, "tensor %lld: byte count overflows", (long long)i);
+        if (t.byte_len != expect)
+            return tfail(err, BPW_E_FORMAT, 16, -1, i, "tensor %lld: byte_len %llu != elements * element size = %llu",
+                         (long long)i, (unsigned long long)t.byte_len, (unsigned long long)expect);
+    }
+    if (t.byte_len > 0 && !t.data)
+        return tfail(err, BPW_E_INVAL, 0, -1, i, "tensor %lld: data is NULL", (long long)i);
+    return BPW_OK;
+}
+
+// Checks every tensor and the counts, sorts, and places the payloads. The config's bytes are checked
+// by the caller (bpw_trit_write_size sees only their length).
+bpw_status write_layout(const bpw_trit_tensor_in *t, int64_t n, size_t config_len, WriteLayout &L, bpw_trit_err *err) {
+    if (n < 0 || (n > 0 && !t)) return tfail(err, BPW_E_INVAL, 0, -1, -1, "bad tensor list");
+    if (config_len > kMaxConfig)
+        return tfail(err, BPW_E_FORMAT, 6, -1, -1, "config_len %zu exceeds 16 MiB", config_len);
+    if (n > (int64_t)kMaxTensors)
+        return tfail(err, BPW_E_FORMAT, 7, -1, -1, "%lld tensors exceed 1048576", (long long)n);
+    uint64_t head = 4 + 4 + 4 + 8 + 4 + (uint64_t)config_len + 4;
+    for (int64_t i = 0; i < n; ++i) {
+        const bpw_status st = check_tensor_in(t[i], i, err);
+        if (st) return st;
+        head += 2 + (uint64_t)t[i].name_len + 4 + 4 * (uint64_t)t[i].ndim + 4 + 4 + 8 + 8;
+    }
+    L.order.resize((size_t)n);
+    for (int64_t i = 0; i < n; ++i) L.order[(size_t)i] = (uint32_t)i;
+    std::stable_sort(L.order.begin(), L.order.end(), [&](uint32_t a, uint32_t b) { return name_less(t[a], t[b]); });
+    for (size_t k = 1; k < L.order.size(); ++k) {
+        const bpw_trit_tensor_in &a = t[L.order[k - 1]], &b = t[L.order[k]];
+        if (a.name_len == b.name_len && std::memcmp(a.name, b.name, (size_t)a.name_len) == 0)
+            return tfail(err, BPW_E_FORMAT, 7, -1, (int64_t)L.order[k], "tensor %u: duplicate name", L.order[k]);
+    }
+    L.offsets.assign((size_t)n, 0);
+    uint64_t off = 0, end = 0;
+    for (const uint32_t i : L.order) {
+        L.offsets[i] = off;
+        if (t[i].byte_len > UINT64_MAX - off - 63)
+            return tfail(err, BPW_E_FORMAT, 9, -1, (int64_t)i, "tensor %u: payload size overflows", i);
+        end = off + t[i].byte_len;
+        off = align64(end);
+    }
+    L.payload_start = align64(head);
+    L.payload_len = end;
+    if (L.payload_len > UINT64_MAX - L.payload_start)
+        return tfail(err, BPW_E_FORMAT, 9, -1, -1, "container size overflows");
+    return BPW_OK;
+}
+
+// P1 and P2 of one ternary payload (checks 17 and 18, first offending beat in row-major order).
+bpw_status check_planes(const bpw_trit_tensor_in &t, int64_t i, bpw_trit_err *err) {
+    const uint64_t rows = t.dims[0], cols = t.dims[1], bpr = (cols + 63) / 64;
+    const uint64_t tail = (cols % 64 == 0) ? ~0ull : ((1ull << (cols % 64)) - 1ull);
+    for (uint64_t row = 0; row < rows; ++row)
+        for (uint64_t b = 0; b < bpr; ++b) {
+            uint64_t pos, neg;
+            std::memcpy(&pos, t.data + (row * bpr + b) * 16, 8);
+            std::memcpy(&neg, t.data + (row * bpr + b) * 16 + 8, 8);
+            const uint64_t both = pos & neg;
+            const uint64_t pad = b + 1 == bpr ? (pos | neg) & ~tail : 0;
+            if (both || pad) {
+                const bool p1 = both != 0;
+                const int64_t col = (int64_t)(64 * b) + __builtin_ctzll(p1 ? both : pad);
+                tfail(err, p1 ? BPW_E_P1_BOTH_BITS : BPW_E_P2_PADDING, p1 ? 17 : 18, -1, i,
+                      "tensor %lld: row %llu beat %llu column %lld %s", (long long)i, (unsigned long long)row,
+                      (unsigned long long)b, (long long)col, p1 ? "has both bits set" : "has a padding bit set");
+                if (err) {
+                    err->row = (int64_t)row;
+                    err->beat = (int64_t)b;
+                    err->col = col;
+                }
+                return p1 ? BPW_E_P1_BOTH_BITS : BPW_E_P2_PADDING;
+            }
+        }
+    return BPW_OK;
+}
+
+template <class T>
+uint8_t *put(uint8_t *p, T v) {
+    std::memcpy(p, &v, sizeof v);  // little-endian hosts, as the format is
+    return p + sizeof v;
+}
+
+}  // namespace
+
+extern "C" {
+
+bpw_status bpw_trit_write_size(const bpw_trit_tensor_in *tensors, int64_t n, size_t config_len, uint64_t *bytes,
+                               bpw_trit_err *err) {
+    clear_err(err);
+    if (!bytes) return tfail(err, BPW_E_INVAL, 0, -1, -1, "bytes is NULL");
+    *bytes = 0;
+    try {
+        WriteLayout L;
+        const bpw_status st = write_layout(tensors, n, config_len, L, err);
+        if (st) return st;
+        *bytes = L.payload_start + L.payload_len;
+    } catch (const std::bad_alloc &) {
+        return tfail(err, BPW_E_INVAL, 0, -1, -1, "out of host memory");
+    }
+    return BPW_OK;
+}
+
+bpw_status bpw_trit_write(const bpw_trit_tensor_in *tensors, int64_t n, const char *config, size_t config_len,
+                          int32_t with_hash, uint8_t *out, size_t out_len, uint64_t *written, bpw_trit_err *err) {
+    clear_err(err);
+    if (!written) return tfail(err, BPW_E_INVAL, 0, -1, -1, "written is NULL");
+    *written = 0;
+    if (config_len > 0 && !config) return tfail(err, BPW_E_INVAL, 0, -1, -1, "config is NULL");
+    if (config_len <= kMaxConfig && !utf8_ok(reinterpret_cast<const uint8_t *>(config), config_len))
+        return tfail(err, BPW_E_FORMAT, 6, -1, -1, "config is not valid UTF-8");
+    try {
+        WriteLayout L;
+        bpw_status st = write_layout(tensors, n, config_len, L, err);
+        if (st) return st;
+        for (int64_t i = 0; i < n; ++i)
+            if (tensors[i].dtype == BPW_TRIT_TERNARY && (st = check_planes(tensors[i], i, err)) != BPW_OK) return st;
+        const uint64_t total = L.payload_start + L.payload_len;
+        if (!out || out_len < total) {
+            *written = total;
+            return tfail(err, BPW_E_SIZE, 0, -1, -1, "out holds %zu bytes, the container needs %llu", out_len,
+                         (unsigned long long)total);
+        }
+        uint8_t *p = out;
+        std::memcpy(p, "TRIT", 4);
+        p = put<uint32_t>(p + 4, 1u);           // version
+        p = put<uint32_t>(p, 0u);               // header flags
+        uint8_t *hash_at = p;
+        p = put<uint64_t>(p, 0ull);             // payload hash, below
+        p = put<uint32_t>(p, (uint32_t)config_len);
+        if (config_len) std::memcpy(p, config, config_len);
+        p += config_len;
+        p = put<uint32_t>(p, (uint32_t)n);
+        for (const uint32_t i : L.order) {
+            const bpw_trit_tensor_in &t = tensors[i];
+            p = put<uint16_t>(p, (uint16_t)t.name_len);
+            std::memcpy(p, t.name, (size_t)t.name_len);
+            p += t.name_len;
+            p = put<uint8_t>(p, (uint8_t)t.dtype);
+            p = put<uint8_t>(p, (uint8_t)t.ndim);
+            p = put<uint8_t>(p, 0);
+            p = put<uint8_t>(p, 0);
+            for (int k = 0; k < t.ndim; ++k) p = put<uint32_t>(p, t.dims[k]);
+            p = put<float>(p, t.scale);
+            p = put<uint32_t>(p, 0u);           // tensor flags
+            p = put<uint64_t>(p, L.offsets[i]);
+            p = put<uint64_t>(p, t.byte_len);
+        }
+        std::memset(p, 0, (size_t)(out + L.payload_start - p));  // up to the payload start
+        uint8_t *payload = out + L.payload_start;
+        std::memset(payload, 0, (size_t)L.payload_len);
+        for (int64_t i = 0; i < n; ++i)
+            if (tensors[i].byte_len) std::memcpy(payload + L.offsets[(size_t)i], tensors[i].data, (size_t)tensors[i].byte_len);
+        if (with_hash) put<uint64_t>(hash_at, bpw_fnv1a64(payload, (size_t)L.payload_len));
+        *written = total;
+    } catch (const std::bad_alloc &) {
+        return tfail(err, BPW_E_INVAL, 0, -1, -1, "out of host memory");
+    }
+    return BPW_OK;
 }
 
 }  // extern "C"

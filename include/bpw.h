@@ -380,6 +380,39 @@ uint64_t bpw_fnv1a64(const uint8_t *data, size_t len);
  * copied and validated exactly as bpw_load does (P1, P2), with the record's scale as w_scale. */
 bpw_status bpw_trit_load(const bpw_trit_file *f, int64_t index, bpw_host_mat **out, bpw_err *err);
 
+/* One tensor for bpw_trit_write. The caller keeps name and data alive during the call. */
+typedef struct bpw_trit_tensor_in {
+    const char *name;      /* UTF-8, name_len bytes (1..1024), unique within the file */
+    int64_t name_len;
+    int32_t dtype;         /* bpw_trit_dtype */
+    int32_t ndim;          /* 1..4; a ternary tensor has 2: rows = dims[0], cols = dims[1] */
+    uint32_t dims[4];      /* outermost first; entries past ndim are ignored */
+    float scale;           /* finite, > 0 (w_scale of a ternary tensor) */
+    uint32_t reserved;     /* 0 */
+    const uint8_t *data;   /* byte_len bytes: .trit v1 planes (rows * beats_per_row * 16) for a ternary
+                              tensor, little-endian elements (product of dims x 4 or 2) for F32 / BF16 */
+    uint64_t byte_len;
+} bpw_trit_tensor_in;
+
+/* Bytes of the container bpw_trit_write makes from these tensors and a config of config_len bytes.
+ * The same field checks as bpw_trit_write except the payload scan; on failure *bytes is 0. */
+bpw_status bpw_trit_write_size(const bpw_trit_tensor_in *tensors, int64_t n, size_t config_len, uint64_t *bytes,
+                               bpw_trit_err *err);
+/* Write a .trit v1 container ("The .trit format, version 1", sections 2-2.4) into out: the header
+ * (version 1, no flags), the config, one record per tensor sorted by name (bytewise, so a conversion
+ * gives the same bytes whatever the order of the input), each payload at the next multiple of 64
+ * after the previous one, the payload starting at the first multiple of 64 after the table and the
+ * file ending with the last tensor's bytes; gaps are zero. with_hash != 0 stores the FNV-1a-64 of the
+ * payload (every byte from its start to the end of the file), 0 stores no hash. Every field is checked
+ * before anything is written, and a tensor a reader would refuse is refused here with the number of
+ * the check it would fail (err->check: 6 config, 7 count / names, 8 dtype / ndim / reserved, 9 shape
+ * overflow, 10 scale, 14-16 byte_len, 17 / 18 P1 / P2 of a ternary payload with its row, beat and
+ * column; err->tensor is the index in `tensors`). out_len below the container's size: BPW_E_SIZE
+ * with *written set to the size needed and nothing written. On success *written is the size. Any file
+ * it writes opens and verifies with bpw_trit_open and bpw_trit_verify. */
+bpw_status bpw_trit_write(const bpw_trit_tensor_in *tensors, int64_t n, const char *config, size_t config_len,
+                          int32_t with_hash, uint8_t *out, size_t out_len, uint64_t *written, bpw_trit_err *err);
+
 /* ------------------------------------------------------------------------ BITCOS */
 
 /* BITCOS ("BITCOS: Intel's Ternary LLM Weight Format Goes Below 1.58 Bits", "A bitmap and a sign"): a

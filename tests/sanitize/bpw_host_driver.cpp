@@ -189,6 +189,55 @@ std::string trits_case(const Buf &b, int64_t rows, int64_t cols) {
     return out;
 }
 
+// Open a container and write its tensors and config again with bpw_trit_write (flags bit 0: store the
+// payload hash). The output is the write's check and location, or its size and FNV-1a-64; a file the
+// writer accepted must reopen and verify.
+std::string rewrite_case(const Buf &b, uint32_t flags) {
+    bpw_trit_file *f = nullptr;
+    bpw_trit_err e;
+    std::memset(&e, 0, sizeof e);
+    if (bpw_trit_open(b.p, b.n, &f, &e) != BPW_OK)
+        return fmt("open %d %lld", e.check, (long long)e.tensor);
+    const char *json = nullptr;
+    size_t json_len = 0;
+    if (bpw_trit_config(f, &json, &json_len) != BPW_OK) unreachable("bpw_trit_config failed on an open file");
+    const int64_t n = bpw_trit_tensor_count(f);
+    std::vector<bpw_trit_tensor_in> in((size_t)n);
+    for (int64_t i = 0; i < n; ++i) {
+        bpw_trit_tensor t;
+        if (bpw_trit_tensor_info(f, i, &t) != BPW_OK) unreachable("bpw_trit_tensor_info failed in range");
+        bpw_trit_tensor_in &w = in[(size_t)i];
+        w.name = t.name;
+        w.name_len = t.name_len;
+        w.dtype = t.dtype;
+        w.ndim = t.ndim;
+        for (int k = 0; k < 4; ++k) w.dims[k] = t.dims[k];
+        w.scale = t.scale;
+        w.reserved = 0;
+        w.data = t.data;
+        w.byte_len = t.byte_len;
+    }
+    uint64_t need = 0;
+    if (bpw_trit_write_size(in.data(), n, json_len, &need, &e) != BPW_OK) unreachable("an opened file's tensors refused");
+    Buf out((size_t)need);
+    uint64_t written = 0;
+    const bpw_status st = bpw_trit_write(in.data(), n, json, json_len, (int32_t)(flags & 1), out.p, out.n, &written, &e);
+    std::string line;
+    if (st != BPW_OK) {
+        line = fmt("%d %lld %lld %lld %lld", e.check, (long long)e.tensor, (long long)e.row, (long long)e.beat,
+                   (long long)e.col);
+    } else {
+        if (written != need) unreachable("written size differs from the computed one");
+        bpw_trit_file *g = nullptr;
+        if (bpw_trit_open(out.p, out.n, &g, &e) != BPW_OK || bpw_trit_verify(g, 1, &e) != BPW_OK)
+            unreachable("a written container does not open and verify");
+        bpw_trit_close(g);
+        line = fmt("0 | %llu %llu", (unsigned long long)written, (unsigned long long)fnv_of(out.p, out.n));
+    }
+    bpw_trit_close(f);
+    return line;
+}
+
 }  // namespace
 
 int main(int argc, char **argv) {
@@ -218,6 +267,7 @@ int main(int argc, char **argv) {
             case 1: line = container_case(b, hd.flags); break;
             case 2: line = planes_case(b, hd.rows, hd.cols); break;
             case 3: line = trits_case(b, hd.rows, hd.cols); break;
+            case 4: line = rewrite_case(b, hd.flags); break;
             default: unreachable("an unknown case op");
         }
         std::fputs(line.c_str(), stdout);

@@ -1,12 +1,13 @@
 """libbpw's untrusted-input host code under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU).
 
-The container reader, the plane packer / validator / loader and the BITCOS packers are compiled from
-the library's own host sources with clang's -fsanitize=address,undefined (tests/sanitize holds the
-driver; the GPU launchers and HIP calls are stubs that abort if reached) and run over the same suites
-as the ctypes tests: every truncation of the format page's complete file and of a multi-tensor file,
-the 3,000 random header mutations, payload bit flips, the validator's corruption suites with hostile
-lengths and shapes, and the packers over ragged shapes, bad values and the zero-density range. Every
-result line is compared with the oracle, and any sanitizer report fails the run."""
+The container reader and writer, the plane packer / validator / loader and the BITCOS packers are
+compiled from the library's own host sources with clang's -fsanitize=address,undefined
+(tests/sanitize holds the driver; the GPU launchers and HIP calls are stubs that abort if reached)
+and run over the same suites as the ctypes tests: every truncation of the format page's complete
+file and of a multi-tensor file, the 3,000 random header mutations, payload bit flips, the
+validator's corruption suites with hostile lengths and shapes, the packers over ragged shapes, bad
+values and the zero-density range, and the container writer rewriting every file of the container
+suites. Every result line is compared with the oracle, and any sanitizer report fails the run."""
 import os
 import shutil
 import struct
@@ -102,6 +103,23 @@ def container_expected(data: bytes, flags: int) -> str:
         except oracle.OracleError as e:
             parts.append(f"{t.dtype}:{i}:{e.code}:{e.row}:{e.beat}:{e.col}")
     return " ".join(parts)
+
+
+def rewrite_expected(data: bytes, flags: int) -> str:
+    """The library writer, given an opened file's tensors in record order and its config, refuses what the
+    oracle's verify refuses (P1 / P2: check, tensor, row, beat, column) and otherwise writes exactly the
+    oracle writer's bytes for the same tensors."""
+    try:
+        g = tc.TritFile(data)
+    except tc.TritError as e:
+        return f"open {e.check} {e.tensor}"
+    try:
+        g.verify(False)
+    except tc.TritError as e:
+        return f"{e.check} {e.tensor} {e.row} {e.beat} {e.col}"
+    ts = [(t.name.decode("utf-8"), t.dtype, t.dims, t.scale, g.payload(i)) for i, t in enumerate(g.tensors)]
+    out = tc.write(g.config, ts, with_hash=bool(flags & 1))
+    return f"0 | {len(out)} {tc.fnv1a64(out)}"
 
 
 def lib_shape_ok(rows: int, cols: int) -> bool:
@@ -228,6 +246,19 @@ def test_container_suites_under_sanitizers(driver, tmp_path):
     lines = run_cases(driver, tmp_path, recs)
     for k, ((_, flags, _, _, data), line) in enumerate(zip(recs, lines)):
         assert line == container_expected(data, flags), (k, len(data), line)
+
+
+def test_writer_rewrites_under_sanitizers(driver, tmp_path):
+    """bpw_trit_write over every container of the suites above (written back from the opened tensors,
+    with and without the payload hash): byte for byte the oracle writer's output, or the same P1 / P2
+    refusal as the oracle's verify; every written file reopens and verifies."""
+    recs = [(4, flags & 1, 0, 0, data) for _, flags, _, _, data in container_records()]
+    lines = run_cases(driver, tmp_path, recs)
+    kinds = set()
+    for k, ((_, flags, _, _, data), line) in enumerate(zip(recs, lines)):
+        assert line == rewrite_expected(data, flags), (k, len(data), line)
+        kinds.add(line.split()[0])
+    assert {"0", "open", "17", "18"} <= kinds, kinds
 
 
 def test_validator_suites_under_sanitizers(driver, tmp_path):
