@@ -543,14 +543,21 @@ CPU_HEAD_ROWS = 8192  # rows of the dense head in its CPU sample
 
 
 def cpu_model() -> str:
+    """The host CPU as /proc/cpuinfo names it: the model name, then vendor, family, model and stepping
+    numbers (a virtualised host may report only a generic model name such as "AMD EPYC")."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                key, _, val = line.partition(":")
+                fields.setdefault(key.strip(), val.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    ident = ", ".join(f"{k} {fields[k]}" for k in ("vendor_id", "cpu family", "model", "stepping") if k in fields)
+    name = fields.get("model name", "unknown")
+    return f"{name} ({ident})" if ident else name
 
 
 def _median_rate(run, nbytes: int, min_seconds: float, runs: int = 3) -> tuple[float, list[float], float]:
