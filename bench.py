@@ -481,19 +481,20 @@ def small_batch_measure(bpw, torch, synth, dev, reps: int = 64, kernel: int = 0)
     return out
 
 
-SB_RUNS = "1,2,2m,3,4,4m,8,16"  # batch sizes of the grouped small-batch leg; "m" pins the matrix cores
+SB_RUNS = "1,2,2b,3,4,8,16"  # batch sizes of the grouped small-batch leg; "m" pins the matrix cores, "b" the
+                             # bit-serial kernels (the token kernel from B = 2)
 
 
 def grouped_small_batch_measure(bpw, torch, synth, dev, ds, steps: int = 50, runs_spec: str = SB_RUNS) -> list[dict]:
     """The decode-step set (210 matrices, 521 MB of planes) at batch B: every matrix times its own B
     int8 activation vectors, all in one grouped launch, the HBM copies in rotation. Under AUTO, B = 1
-    runs the batch-1 GEMV, B = 2 .. 4 the bit-serial token kernel (each beat streamed once, reduced
-    against every token on the VALU) and larger B the int8 matrix cores; B = 2 and 4 are also timed on
-    the matrix cores. Shows where the weight stream stops being the limit as B grows."""
+    runs the batch-1 GEMV and larger B the int8 matrix cores; B = 2 is also timed on the bit-serial
+    token kernel (each beat streamed once, reduced against every token on the VALU). Shows where the
+    weight stream stops being the limit as B grows."""
     out = []
-    runs = [(int(r.rstrip("m")), bpw.KERNEL_MFMA if r.endswith("m") else bpw.KERNEL_AUTO)
-            for r in runs_spec.split(",")]
-    names = {bpw.KERNEL_AUTO: "auto", bpw.KERNEL_MFMA: "mfma"}
+    pin = {"m": bpw.KERNEL_MFMA, "b": bpw.KERNEL_BITSERIAL}
+    runs = [(int(r.rstrip("mb")), pin.get(r[-1], bpw.KERNEL_AUTO)) for r in runs_spec.split(",")]
+    names = {bpw.KERNEL_AUTO: "auto", bpw.KERNEL_MFMA: "mfma", bpw.KERNEL_BITSERIAL: "bitserial"}
     for batch, kernel in runs:
         xs = []
         for i, (layer, proj, name, rows, cols) in enumerate(ds.shapes):
@@ -743,7 +744,7 @@ def main() -> int:
                     help="comma-separated companion measurements to run (default all): " + ",".join(LEGS))
     ap.add_argument("--sb-batches", default=SB_RUNS,
                     help="batch sizes of the small_batch_decode_step leg, comma-separated; a trailing m pins the "
-                         "matrix cores (default %(default)s)")
+                         "matrix cores, a trailing b the bit-serial kernels (default %(default)s)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the steps, read 1 GiB with the streaming probe and rewrite 1 GiB with the cache "
                          "flush (3 times each): kernels of known traffic for scaling hardware byte counters")
