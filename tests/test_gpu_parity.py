@@ -839,15 +839,21 @@ def test_small_batch_grouped_new_inputs_and_errors(dev):
 # ----------------------------------------------------------------------------- .trit container -> GPU
 
 
-def test_container_to_grouped_gemv(dev):
-    """One layer's seven projections written into a .trit v1 container (by the oracle's writer), opened
-    and verified by the library, loaded, uploaded and run as one grouped GEMV: equal to the oracle on
-    the same trits, bit for bit."""
+@pytest.mark.parametrize("writer", ("oracle", "library"))
+def test_container_to_grouped_gemv(dev, writer):
+    """One layer's seven projections written into a .trit v1 container, opened and verified by the
+    library, loaded, uploaded and run as one grouped GEMV: equal to the oracle on the same trits, bit
+    for bit. Written by the oracle's writer from the oracle's packing, or by the library's packer and
+    writer (the whole product path from int8 trits to outputs)."""
     from oracle import trit_container as tc
-    log("case: .trit container -> load -> upload -> grouped GEMV")
+    log(f"case: .trit container ({writer} writer) -> load -> upload -> grouped GEMV")
     cases = synth.layer_cases(31337, 0)
-    data = tc.write(b'{"hidden_size": 2560}', [(c.name, tc.TRIT, [c.rows, c.cols], c.w_scale, oracle.pack(c.w).tobytes())
-                                               for c in cases], with_hash=False)
+    if writer == "oracle":
+        data = tc.write(b'{"hidden_size": 2560}', [(c.name, tc.TRIT, [c.rows, c.cols], c.w_scale,
+                                                    oracle.pack(c.w).tobytes()) for c in cases], with_hash=False)
+    else:
+        data = bpw.trit_write([(c.name, bpw.TRIT_TERNARY, [c.rows, c.cols], c.w_scale, bpw.bpw_pack_i8(c.w))
+                               for c in cases], b'{"hidden_size": 2560}')
     f = bpw.TritFile(data)
     f.verify()
     ups = []
