@@ -85,27 +85,70 @@ def basic_blocks(asm: str) -> dict:
     return blocks
 
 
+def successors(blocks: dict) -> dict:
+    """Control-flow successors of each basic block: its branch targets, and the next block unless it ends
+    in an unconditional branch or the end of the program."""
+    names, succ = list(blocks), {}
+    for i, n in enumerate(names):
+        body, out = blocks[n], []
+        for x in body:
+            m = re.match(r"s_c?branch\w*\s+(\.LBB\d+_\d+)", x)
+            if m:
+                out.append(m.group(1))
+        last = body[-1] if body else ""
+        if i + 1 < len(names) and not last.startswith("s_branch ") and not last.startswith("s_endpgm"):
+            out.append(names[i + 1])
+        succ[n] = out
+    return succ
+
+
 @pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
 def test_grouped_small_batch_stream_waits_only_for_the_older_loads(tmp_path):
-    """The grouped matrix-core small batch: in every basic block that holds matrix-core instructions (the
-    streaming loop), no wait issued after the block's own beat loads drains the vector-memory counter:
-    the beats a step issues for the next step stay in flight while it decodes and multiplies. A
-    vmcnt(0) before the block's first load waits only for loads issued in an earlier block (the step's
-    own beats, which it needs next). A per-lane guard on the operand staging once left a load unwaited,
-    and the compiler put waits for every load in flight into this loop."""
+    """The grouped matrix-core small batch: after every weight-beat load (the
+    non-temporal 16-byte loads), each control-flow path reaches a matrix-core instruction before any wait
+    that drains the vector-memory counter, so the beats a step issues for the next step stay in flight
+    while the current step is decoded and multiplied. A path may end at a barrier instead: the beats a
+    pass issues before staging its operands are waited for with the operands. A per-lane guard on the
+    operand staging once left a load unwaited, and the compiler put waits for every load in flight into
+    this loop. The paths are followed through the control flow because the compiler may put a step's
+    loads and its matrix-core instructions in different basic blocks."""
     out = tmp_path / "sb.s"
     src = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", "bpw_small_batch.hip")
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-ffp-contract=off",
                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-S", "--cuda-device-only",
                     src, "-o", str(out)], check=True, capture_output=True)
-    kernel = re.split(r"\n(?=_ZN3bpw36gemm_small_batch_mfma_grouped_kernel)", out.read_text())[1]
-    kernel = kernel.split("s_endpgm")[0]
-    blocks = {n: b for n, b in basic_blocks(kernel).items() if any("v_mfma" in x for x in b)}
-    assert sum(sum("buffer_load_dwordx4" in x for x in b) for b in blocks.values()) >= 4, "no streaming loop found"
-    for name, body in blocks.items():
-        issued = False
-        for x in body:
-            issued = issued or "buffer_load_dwordx4" in x
-            m = re.search(r"vmcnt\((\d+)\)", x)
-            if m and issued:
-                assert int(m.group(1)) > 0, f"block {name}: a wait drains the loads this block issued"
+    kernels = re.split(r"\n(?=_ZN3bpw36gemm_small_batch_mfma_grouped_kernel)", out.read_text())[1:]
+    assert len(kernels) == 1
+    for kernel in kernels:
+        kernel = kernel.split(".Lfunc_end")[0]
+        blocks = basic_blocks(kernel)
+        succ = successors(blocks)
+        beat = lambda x: x.startswith("buffer_load_dwordx4") and x.endswith(" nt")
+        assert sum(sum(beat(x) for x in b) for b in blocks.values()) >= 8, "no streaming loop found"
+        assert sum(sum("v_mfma" in x for x in b) for b in blocks.values()) >= 16, "no matrix-core step found"
+
+        def first_event(name, start):
+            """'mfma', 'barrier' or 'end' on every path from instruction `start` of block `name`, or the
+            block where a drain comes first."""
+            seen, todo = set(), [(name, start)]
+            while todo:
+                n, i = todo.pop()
+                stop = False
+                for x in blocks[n][i:]:
+                    if "v_mfma" in x or x.startswith("s_barrier") or x.startswith("s_endpgm"):
+                        stop = True
+                        break
+                    if re.search(r"vmcnt\(0\)", x):
+                        return n
+                if not stop:
+                    for m in succ[n]:
+                        if m not in seen:
+                            seen.add(m)
+                            todo.append((m, 0))
+            return None
+
+        for name, body in blocks.items():
+            loads = [i for i, x in enumerate(body) if beat(x)]
+            if loads:
+                bad = first_event(name, loads[-1] + 1)
+                assert bad is None, f"beats loaded in {name}: a wait in {bad} drains them before the next step"
