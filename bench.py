@@ -50,10 +50,15 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash(paths=None) -> str:
+    """SHA-256 of the kernel's sources and of the compiler flags its translation unit (the first path)
+    is built with, so a record taken from another build of the same sources does not match."""
+    from bit_plane_weight_amd import build as bpw_build
+    paths = paths or KERNEL_SRCS
     h = hashlib.sha256()
-    for path in paths or KERNEL_SRCS:
+    for path in paths:
         with open(path, "rb") as f:
             h.update(f.read())
+    h.update(" ".join(bpw_build.flags_for(paths[0])).encode())
     return h.hexdigest()
 
 
