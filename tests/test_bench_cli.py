@@ -60,3 +60,16 @@ def test_counter_records_from_rocprof_csv(tmp_path):
     assert g["traffic_bytes_per_launch"] == (255000 * 2 + 5000) * 1024
     assert g["kernel_source_sha256"] == bench.kernel_source_hash()
     assert b["sq_insts_valu_per_launch"] == 50000000 and b["traffic_bytes_per_launch"] == (200000 * 2 + 5000) * 1024
+
+
+def test_kernel_hash_covers_the_build_flags(monkeypatch):
+    """A counter record names the kernel by its sources and its compiler flags: the same sources built
+    with other flags are another kernel, and its traffic is not reported from the record."""
+    import bench
+    from bit_plane_weight_amd import build as bpw_build
+    h = bench.kernel_source_hash()
+    base = bpw_build.flags_for
+    monkeypatch.setattr(bpw_build, "flags_for", lambda src: [f for f in base(src) if "preload" not in f])
+    assert bench.kernel_source_hash() != h
+    monkeypatch.setattr(bpw_build, "flags_for", base)
+    assert bench.kernel_source_hash() == h

@@ -152,3 +152,26 @@ def test_grouped_small_batch_stream_waits_only_for_the_older_loads(tmp_path):
             if loads:
                 bad = first_event(name, loads[-1] + 1)
                 assert bad is None, f"beats loaded in {name}: a wait in {bad} drains them before the next step"
+
+
+@pytest.mark.skipif(not (os.path.exists(HIPCC) or shutil.which("hipcc")), reason="hipcc not installed")
+def test_kernel_arguments_preloaded_except_the_quantiser(tmp_path):
+    """The build preloads kernel arguments into SGPRs for the kernel files: the descriptor of a kernel
+    whose arguments are pointers (the grouped GEMV, the grouped small batch) has a preload length, and
+    its code starts with the compiler's fallback that loads them itself where the firmware does not.
+    (Arguments passed as a structure by value are not preloaded.) The quantiser is built without it,
+    as it measured slower with it."""
+    from bit_plane_weight_amd import build as bpw_build
+    for name, kernel, preloaded in (("bpw_gemv.hip", "gemv_bitserial_kernel", True),
+                                    ("bpw_small_batch.hip", "gemm_small_batch_mfma_grouped_kernel", True),
+                                    ("bpw_quantize.hip", "quantize_kernel", False)):
+        src = os.path.join(ROOT, "bit_plane_weight_amd", "csrc", name)
+        out = tmp_path / (name + ".s")
+        flags = [f for f in bpw_build.flags_for(src) if f != "-fPIC"]
+        subprocess.run([HIPCC, *flags, "-S", "--cuda-device-only", src, "-o", str(out)], check=True,
+                       capture_output=True)
+        blocks = re.findall(r"\.amdhsa_kernel (\S+)\n(.*?)\.end_amdhsa_kernel", out.read_text(), re.S)
+        lengths = [int(re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length\s+(\d+)", b).group(1))
+                   for k, b in blocks if kernel in k]
+        assert len(lengths) == 1, (name, [k for k, _ in blocks])
+        assert (lengths[0] > 0) == preloaded, (name, lengths)
